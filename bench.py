@@ -1,0 +1,376 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP8 Linear hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the hot path over one batch of synthetic, seeded
+input that is already resident in HBM: the MXFP8 quantize kernels that
+produce the GEMM operands from bf16, then the MXFP8 GEMM(s) with their
+epilogues.  The default workload is the large square forward GEMM:
+rowwise and columnwise MXFP8 quantize of both 8192 x 8192 bf16 inputs, then
+the 8192^3 E4M3 GEMM (bf16 out).  Other workloads (--workload decoder_fwd,
+hybrid_bwd, moe_grouped, tiny) print the same kind of line for their step.
+
+One JSON line is printed.  `value` is the whole-step throughput: the GEMM
+flops of a step divided by the measured wall time of a step (quantize time
+included).  Per-kernel averages come from HIP events recorded between the
+launches on the launch stream inside the timed region; `roofline` reports
+the dominant kernel against MI355X's published peak, `kernels` every
+kernel, `cpu_baseline` the CPU oracle timed on a bounded sample.
+
+Bandwidth measurements rotate over several copies of every bf16 input and
+quantize output (more than the 256 MB last-level cache), so a kernel's
+reads come from HBM rather than from a cache warmed by the previous step.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # dense FP8 / MXFP8 MFMA, MI355X
+PEAK_HBM_GBS = 8000.0         # HBM3E, MI355X
+METRIC = "MXFP8 GEMM TFLOP/s + % of MI355X FP8 MFMA peak; quantize GB/s % of HBM"
+ROTATE = 4                     # copies of each bandwidth-bound input / output
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="square_8192",
+                   choices=["square_8192", "decoder_fwd", "hybrid_bwd", "moe_grouped", "tiny"])
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the timed region, copy a 512 MiB buffer 3 times (counter calibration)")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------- the step
+
+class Step:
+    """A list of kernel launches over resident buffers, with per-op accounting."""
+
+    def __init__(self, name):
+        self.name = name
+        self.ops = []      # (label, kind, fn(rot), flops, bytes)
+
+    def add(self, label, kind, fn, flops=0.0, nbytes=0.0):
+        self.ops.append((label, kind, fn, flops, nbytes))
+
+    @property
+    def flops(self):
+        return sum(o[3] for o in self.ops)
+
+
+def q_bytes(rows, cols):
+    return rows * cols * (2 + 1 + 1 / 32)
+
+
+def gemm_bytes(M, N, K, epi, grouped_experts=0):
+    b = M * K * (1 + 1 / 32) + N * K * (1 + 1 / 32) * max(1, grouped_experts) + M * N * 2
+    if epi == "bias_gelu_aux":
+        b += M * N * 2
+    if epi != "none":
+        b += N * 2 * max(1, grouped_experts)
+    return b
+
+
+def build_step(workload, torch, te, workloads):
+    """Allocate resident inputs and outputs; return a Step whose ops take the rotation index."""
+    dev = torch.device("cuda:0")
+
+    def upload(bits):
+        return torch.from_numpy(bits.view("int16")).to(dev)
+
+    def rotated(bits):
+        t = upload(bits)
+        return [t] + [t.clone() for _ in range(ROTATE - 1)]
+
+    def qbufs(rows, cols, direction):
+        out = []
+        for _ in range(ROTATE):
+            if direction == "row":
+                out.append((torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+                            torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)))
+            else:
+                out.append((torch.empty((cols, rows), dtype=torch.uint8, device=dev),
+                            torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)))
+        return out
+
+    step = Step(workload)
+    w = workloads.ALL[workload]()
+    quantized = {}  # (tensor spec, dir) -> rotating (q, s)
+
+    def add_quantize(spec, fmt, direction, label):
+        key = (spec, direction, fmt)
+        if key in quantized:
+            return quantized[key]
+        src = rotated(spec.make())
+        rows, cols = spec.shape
+        bufs = qbufs(rows, cols, direction)
+
+        def fn(r, src=src, bufs=bufs, fmt=fmt, direction=direction):
+            q, s = bufs[r]
+            if direction == "row":
+                te.te_mxfp8_quantize(src[r], fmt, "row", q, s, None, None)
+            else:
+                te.te_mxfp8_quantize(src[r], fmt, "col", None, None, q, s)
+        step.add(label, "quantize", fn, 0.0, q_bytes(rows, cols))
+        quantized[key] = bufs
+        return bufs
+
+    for spec, fmt, direction in w.quantize:
+        add_quantize(spec, fmt, direction, f"quantize_{direction}_{spec.shape[0]}x{spec.shape[1]}_t{spec.tensor_id}")
+
+    for g in w.gemms:
+        qa = add_quantize(g.a_src, g.fmt_a, g.a_dir, f"quantize_{g.a_dir}_{g.name}_A")
+        qb = add_quantize(g.b_src, g.fmt_b, g.b_dir, f"quantize_{g.b_dir}_{g.name}_B")
+        bias = upload(g.bias.make()) if g.bias is not None else None
+        d = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev)
+        aux = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev) if g.epilogue == "bias_gelu_aux" else None
+
+        def fn(r, g=g, qa=qa, qb=qb, bias=bias, d=d, aux=aux):
+            te.te_mxfp8_gemm(qa[r][0], qa[r][1], g.fmt_a, qb[r][0], qb[r][1], g.fmt_b, d, g.epilogue, bias, aux)
+        step.add(f"gemm_{g.name}_{g.M}x{g.N}x{g.K}", "gemm", fn, g.flops, gemm_bytes(g.M, g.N, g.K, g.epilogue))
+
+    for g in w.grouped:
+        qa = add_quantize(g.a_src, g.fmt_a, "row", f"quantize_row_{g.name}_A")
+        qb = add_quantize(g.b_src, g.fmt_b, "row", f"quantize_row_{g.name}_B")
+        bias = upload(g.bias.make()) if g.bias is not None else None
+        counts = workloads.moe_counts(g.total_m, g.experts)
+        splits = torch.tensor(counts, dtype=torch.int32, device=dev)
+        d = torch.empty((g.total_m, g.N), dtype=torch.bfloat16, device=dev)
+        aux = torch.empty((g.total_m, g.N), dtype=torch.bfloat16, device=dev) if g.epilogue == "bias_gelu_aux" else None
+
+        def fn(r, g=g, qa=qa, qb=qb, bias=bias, d=d, aux=aux, splits=splits):
+            te.te_mxfp8_grouped_gemm(splits, qa[r][0], qa[r][1], g.fmt_a, qb[r][0], qb[r][1], g.fmt_b, g.N, d,
+                                     g.epilogue, bias, aux)
+        flops = 2.0 * g.total_m * g.N * g.K
+        step.add(f"grouped_gemm_{g.name}_{g.experts}x{g.N}x{g.K}", "gemm", fn, flops,
+                 gemm_bytes(g.total_m, g.N, g.K, g.epilogue, g.experts))
+
+    for spec, fmt in w.current_scaling:
+        src = rotated(spec.make())
+        n = spec.shape[0] * spec.shape[1]
+        ws = torch.empty(te.te_amax_workspace_size(n), dtype=torch.uint8, device=dev)
+        outs = [(torch.empty(spec.shape, dtype=torch.uint8, device=dev),
+                 *(torch.empty(1, dtype=torch.float32, device=dev) for _ in range(3))) for _ in range(ROTATE)]
+
+        def fn(r, src=src, outs=outs, ws=ws, fmt=fmt):
+            q, a, s, si = outs[r]
+            te.te_fp8_cast_current_scaling(src[r], fmt, q, a, s, si, ws)
+        step.add(f"current_scaling_cast_{spec.shape[0]}x{spec.shape[1]}", "cast", fn, 0.0, n * (2 + 3))
+    return step
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(workload, workloads):
+    """Time the oracle on a bounded sample of the step and scale it to the full step.
+
+    Sample: the oracle's step restricted to the first S rows of every operand
+    (S = 1024 for 8192-sized operands): the quantizes of those rows and the
+    GEMM block D[:S, :S].  The full-step time is estimated as
+    quantize_time * (full quantize elements / sampled ones) +
+    gemm_time * (full GEMM flops / sampled ones).
+    """
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl absent
+        threads = 1
+    w = workloads.ALL[workload]()
+    q_time = q_elems_s = q_elems_full = 0.0
+    g_time = g_flops_s = g_flops_full = 0.0
+    S = 1024
+    gemms = list(w.gemms)
+    for g in gemms:
+        a, b = g.a_src.make(), g.b_src.make()
+        sm, sn = min(S, g.M), min(S, g.N)
+        fa, fb = oracle.format_by_name(g.fmt_a), oracle.format_by_name(g.fmt_b)
+        t0 = time.perf_counter()
+        qa, sa = (oracle.quantize_rowwise(a[:sm], fa) if g.a_dir == "row"
+                  else oracle.quantize_colwise(np.ascontiguousarray(a[:, :sm]), fa))
+        qb, sb = (oracle.quantize_rowwise(b[:sn], fb) if g.b_dir == "row"
+                  else oracle.quantize_colwise(np.ascontiguousarray(b[:, :sn]), fb))
+        t1 = time.perf_counter()
+        bias = g.bias.make()[:sn] if g.bias is not None else None
+        oracle.mx_gemm(qa, sa, fa, qb, sb, fb, bias, g.epilogue)
+        t2 = time.perf_counter()
+        q_time += t1 - t0
+        q_elems_s += (sm + sn) * g.K
+        q_elems_full += (g.M + g.N) * g.K
+        g_time += t2 - t1
+        g_flops_s += 2.0 * sm * sn * g.K
+        g_flops_full += 2.0 * g.M * g.N * g.K
+    for spec, fmt, direction in w.quantize:
+        if any(spec in (g.a_src, g.b_src) for g in gemms):
+            q_elems_full += spec.shape[0] * spec.shape[1]  # the other direction of an operand already timed
+    for g in w.grouped:
+        counts = workloads.moe_counts(g.total_m, g.experts)
+        a = g.a_src.make()
+        b = g.b_src.make()
+        sm = min(256, int(counts[0]))
+        fa = oracle.format_by_name(g.fmt_a)
+        t0 = time.perf_counter()
+        qa, sa = oracle.quantize_rowwise(a[:sm], fa)
+        qb, sb = oracle.quantize_rowwise(b[:g.N], fa)
+        t1 = time.perf_counter()
+        bias = g.bias.make()[0] if g.bias is not None else None
+        oracle.mx_gemm(qa, sa, fa, qb, sb, fa, bias, g.epilogue)
+        t2 = time.perf_counter()
+        q_time += t1 - t0
+        q_elems_s += (sm + g.N) * g.K
+        q_elems_full += (g.total_m + g.experts * g.N) * g.K
+        g_time += t2 - t1
+        g_flops_s += 2.0 * sm * g.N * g.K
+        g_flops_full += 2.0 * g.total_m * g.N * g.K
+    est = q_time * (q_elems_full / max(q_elems_s, 1)) + g_time * (g_flops_full / max(g_flops_s, 1))
+    return {"value": g_flops_full / est / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"oracle (numpy fp64) on the first {S} rows of each operand: quantize "
+                       f"{q_elems_s:.3g} elements in {q_time:.2f} s (1 thread), GEMM {g_flops_s:.3g} flop in "
+                       f"{g_time:.2f} s ({threads} BLAS threads); full step estimated at {est:.1f} s by scaling "
+                       f"each part to the full step's elements / flops"),
+            "host_cpus": os.cpu_count()}
+
+
+# ------------------------------------------------------------------ traffic
+
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mxfp8_mixed_precision_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(label):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    entry = data.get("kernels", {}).get(label)
+    if not entry or data.get("sources_hash") != kernel_sources_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the MXFP8 Linear path is built and measured on a single MI355X "
+              "(multi-GPU sharding is described, not run). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mxfp8_mixed_precision_amd as te
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    step = build_step(args.workload, torch, te, workloads)
+    stream = torch.cuda.current_stream()
+    nops = len(step.ops)
+
+    def run(i, events=None):
+        r = i % ROTATE
+        for k, (_, _, fn, _, _) in enumerate(step.ops):
+            if events is not None:
+                events[k].record(stream)
+            fn(r)
+        if events is not None:
+            events[nops].record(stream)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        run(i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    kernels = []
+    for k, (label, kind, _, flops, nbytes) in enumerate(step.ops):
+        ms = sum(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps)) / args.steps
+        ent = {"name": label, "kind": kind, "avg_ms": round(ms, 5)}
+        if flops:
+            ent["tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+            ent["frac_fp8_peak"] = round(ent["tflops"] / PEAK_FP8_TFLOPS, 4)
+        if nbytes:
+            ent["gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            ent["frac_hbm_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
+        kernels.append(ent)
+
+    dom = max(range(nops), key=lambda k: kernels[k]["avg_ms"])
+    dlabel, dkind, _, dflops, dbytes = step.ops[dom]
+    dms = kernels[dom]["avg_ms"]
+    if dkind == "gemm":
+        roof = {"bound": "mfma", "achieved": round(dflops / (dms * 1e-3) / 1e12, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(dbytes / (dms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = measured_traffic(dlabel)
+    roof["kernel"] = dlabel
+
+    value = step.flops / (ms_per_step * 1e-3) / 1e12
+    qk = [k for k in kernels if k["kind"] == "quantize"]
+    w = workloads.ALL[args.workload]()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3/e5m2 x e8m0 -> fp32 acc, bf16 out",
+        "data": "synthetic (seeded N(0, sigma) bf16, outlier columns per config)",
+        "config": {"workload": w.name, "gemm_flops_per_step": step.flops, "parallelism": "single GPU",
+                   "rotating_buffers": ROTATE},
+        "roofline": roof,
+        "quantize_gbs_min": min((k["gbs"] for k in qk), default=None),
+        "quantize_frac_hbm_min": min((k["frac_hbm_peak"] for k in qk), default=None),
+        "kernels": kernels,
+    }
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, workloads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

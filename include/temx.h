@@ -1,0 +1,193 @@
+/*
+ * temx.h -- C ABI of the MXFP8 Linear hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the FP8 Linear path that sits behind Transformer
+ * Engine's Linear / LayerNormMLP modules on ROCm:
+ *   - per-tensor amax (two-stage, no atomics) and the current-scaling cast;
+ *   - MXFP8 1-D block quantization of bf16 tensors, rowwise and transposed
+ *     columnwise (32-element blocks, one E8M0 power-of-two scale per block);
+ *   - the MXFP8 x MXFP8 -> fp32-accumulate GEMM with bias, GELU(tanh) and
+ *     GELU-aux (pre-activation) epilogues;
+ *   - a single-launch grouped (MoE) variant over ragged expert row counts.
+ *
+ * Sources, cited by page title and section:
+ *   [ROCm-TE]  "Transformer Engine On ROCm and AMDGPU" (ROCm/TransformerEngine
+ *              README): "MXFP8 support on ROCm (gfx95x only)", "Blockwise FP8
+ *              GEMM support on ROCm" (E8M0 power-of-two scales), "Two-stage
+ *              amax Kernel", "Experimental Triton Kernels on ROCm"
+ *              (cast_transpose), "Grouped GEMM using CK_Tile".
+ *   [TE-JAX]   "Getting Started" (Transformer Engine JAX quickstart): GELU
+ *              with the tanh approximation; "Enabling Quantization" (HYBRID).
+ *   [FP8-WF]   "Workflow: NVIDIA TransformerEngine FP8 Training Quickstart",
+ *              Step 4: E4M3 forward / E5M2 backward (HYBRID); current scaling.
+ *   [HK-PR]    "HipKittens MXFP8 GEMM Support" (ROCm/TransformerEngine PR
+ *              #566): description (BIAS, GELU AUX epilogues) and review
+ *              threads (1-D MXFP8 scaling mode; K % 128, M % 16, N % 16;
+ *              "TN" layout).
+ *
+ * Encoding conventions (the pages do not define them; OCP FP8 / OCP MX):
+ *   E4M3 is the OCP "FN" variant (max 448, no Inf), E5M2 is IEEE-like (max
+ *   57344).  Block scale code = max(biased_exp(block amax) - emax, 0) with
+ *   emax 8 (E4M3) / 15 (E5M2), i.e. floor(log2(amax)) - emax biased by 127.
+ *   Element codes are the saturating round-to-nearest-even encoding of
+ *   x / 2^(code - 127); the sign is kept (negative underflow gives 0x80).
+ *   Inputs holding NaN or Inf give unspecified codes.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers unless stated; the caller owns every
+ *     buffer.  The library never allocates, frees or caches device memory
+ *     and keeps no state between calls other than a per-device cache of the
+ *     compute-unit count.
+ *   - All work is enqueued on `stream` (0 = the null stream); no entry point
+ *     synchronizes the host.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     failure a non-TE_OK status is returned and nothing runs.  A failed
+ *     launch returns TE_ERR_HIP.  Nothing throws across the ABI.
+ *   - Data pointers must be 16-byte aligned (TE_ERR_ALIGN otherwise); scale
+ *     pointers and scalar outputs have no alignment requirement beyond
+ *     their type.
+ *   - Tensors are row-major.  bf16 values are passed as their uint16 bit
+ *     patterns.  MXFP8 data is uint8 [rows, K] with E8M0 scales uint8
+ *     [rows, K/32] (unpadded, row-major).
+ */
+#ifndef TEMX_H
+#define TEMX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TE_OK = 0,
+  TE_ERR_NULL = 1,       /* a required pointer is NULL, or an unused one is not */
+  TE_ERR_SHAPE = 2,      /* a size violates the entry point's shape rules */
+  TE_ERR_ALIGN = 3,      /* a data pointer is not 16-byte aligned */
+  TE_ERR_DTYPE = 4,      /* unsupported format / dtype / format combination */
+  TE_ERR_WORKSPACE = 5,  /* workspace smaller than the size query returns */
+  TE_ERR_HIP = 6,        /* a HIP call or kernel launch failed */
+  TE_ERR_VALUE = 7       /* an enum argument is out of range */
+} te_status;
+
+typedef enum { TE_BF16 = 0, TE_FP32 = 1, TE_E4M3 = 2, TE_E5M2 = 3, TE_E8M0 = 4 } te_dtype;
+
+typedef enum { TE_EPI_NONE = 0, TE_EPI_BIAS = 1, TE_EPI_BIAS_GELU_AUX = 2 } te_epilogue;
+
+typedef enum { TE_ROWWISE = 1, TE_COLWISE = 2, TE_BOTH = 3 } te_qdir;
+
+/* Human-readable name of a status code (static storage). */
+const char* te_status_str(te_status status);
+
+/*
+ * Per-tensor amax, two-stage ([ROCm-TE] "Two-stage amax Kernel"): stage one
+ * writes one partial maximum per workgroup into `workspace`, stage two
+ * reduces them; no atomics.
+ *   x          bf16 [n]; n >= 0 (n == 0 gives amax 0)
+ *   amax_out   float [1], device: max |x_i| (exact; -0 counts as 0)
+ *   workspace  device scratch of at least te_amax_workspace_size(n) bytes
+ */
+size_t te_amax_workspace_size(int64_t n);
+te_status te_amax_reduce(const uint16_t* x, int64_t n, float* amax_out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Current-scaling FP8 cast ([FP8-WF] Step 4, Float8CurrentScaling; margin 0
+ * as in the [TE-JAX] recipes): amax as above, then on the device
+ *   scale     = fl32(fmt_max / amax)  (fmt_max 448 for E4M3, 57344 for E5M2;
+ *               amax == 0 gives 1; a quotient beyond the float range gives
+ *               the largest finite float)
+ *   scale_inv = fl32(1 / scale)
+ *   q_i       = saturating RNE encode of fl32(x_i * scale).
+ *   x          bf16 [n]
+ *   fmt        TE_E4M3 or TE_E5M2
+ *   q_out      uint8 [n]
+ *   amax_out, scale_out, scale_inv_out   float [1] each, device
+ *   workspace  at least te_amax_workspace_size(n) bytes
+ */
+te_status te_fp8_cast_current_scaling(const uint16_t* x, int64_t n, te_dtype fmt, uint8_t* q_out,
+                                      float* amax_out, float* scale_out, float* scale_inv_out,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * MXFP8 1-D block quantization ([ROCm-TE] "MXFP8 support on ROCm"; scales
+ * E8M0 per [ROCm-TE] "Blockwise FP8 GEMM support"; HYBRID formats per
+ * [FP8-WF] Step 4; the transposed copy is what cast_transpose provides in
+ * [ROCm-TE] "Experimental Triton Kernels on ROCm").
+ *   x       bf16 [rows, cols]
+ *   fmt     TE_E4M3 or TE_E5M2
+ *   dir     TE_ROWWISE, TE_COLWISE or TE_BOTH
+ *   rowwise (dir & TE_ROWWISE): blocks of 32 along cols; needs cols % 32 == 0.
+ *           q_row uint8 [rows, cols], s_row uint8 [rows, cols/32]
+ *   colwise (dir & TE_COLWISE): blocks of 32 down each column, stored
+ *           transposed; needs rows % 32 == 0 and cols % 8 == 0.
+ *           q_col uint8 [cols, rows], s_col uint8 [cols, rows/32]
+ *   Output pointers of a direction not requested must be NULL.
+ *   rows, cols >= 0; an empty tensor enqueues nothing.
+ */
+te_status te_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, te_dtype fmt, te_qdir dir,
+                            uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                            hipStream_t stream);
+
+/*
+ * MXFP8 GEMM, "TN" ([HK-PR] description and review threads):
+ *   D[m, n] = epi( sum_k A[m, k] * B[n, k] )   with fp32 accumulation, where
+ *   A[m, k] = val(a[m, k]) * 2^(a_scale[m, k/32] - 127) (likewise B).
+ *   a        uint8 [M, K], a_scale uint8 [M, K/32], a_fmt E4M3 or E5M2
+ *   b        uint8 [N, K], b_scale uint8 [N, K/32], b_fmt E4M3 or E5M2
+ *            (E5M2 x E5M2 is rejected with TE_ERR_DTYPE)
+ *   d        [M, N], d_dtype TE_BF16 (round to nearest even) or TE_FP32
+ *   epi      TE_EPI_NONE:          D = acc
+ *            TE_EPI_BIAS:          D = acc + bias[n]
+ *            TE_EPI_BIAS_GELU_AUX: pre = acc + bias[n]; aux = bf16(pre);
+ *                                  D = gelu_tanh(pre)  ([TE-JAX] tanh GELU)
+ *   bias     bf16 [N]; required iff epi != TE_EPI_NONE, NULL otherwise
+ *   aux      bf16 [M, N]; required iff epi == TE_EPI_BIAS_GELU_AUX, NULL otherwise
+ *   Shapes: M, N, K >= 0; K % 128 == 0, M % 16 == 0, N % 16 == 0 (the
+ *   [HK-PR] checks; M and N need not be multiples of the tile size).
+ *   M == 0 or N == 0 enqueues nothing; K == 0 gives D = epi(0).
+ *   workspace: none is needed (te_mxfp8_gemm_workspace_size returns 0);
+ *   pass NULL / 0.
+ */
+size_t te_mxfp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt,
+                        const uint8_t* b, const uint8_t* b_scale, te_dtype b_fmt,
+                        int64_t M, int64_t N, int64_t K,
+                        void* d, te_dtype d_dtype, te_epilogue epi,
+                        const uint16_t* bias, uint16_t* aux,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Grouped MXFP8 GEMM in one launch ([ROCm-TE] single-launch grouped GEMM /
+ * "Grouped GEMM using CK_Tile"; epilogues as te_mxfp8_gemm).  Expert g owns
+ * rows [off_g, off_g + m_splits[g]) of A, D and aux, where off_g is the sum
+ * of the earlier splits:
+ *   D_g = epi(A_g . B_g^T + bias_g).
+ *   num_groups  G >= 1
+ *   m_splits    int32 [G], DEVICE memory, read by the kernel (no host sync).
+ *               Precondition: every split >= 0 and their sum == total_m.
+ *               The kernel clamps rows to [0, total_m), so bad splits cannot
+ *               write outside D / aux, but their results are unspecified.
+ *   a           uint8 [total_m, K], a_scale [total_m, K/32]
+ *   b           uint8 [G * N, K] (experts stacked), b_scale [G * N, K/32]
+ *   d           [total_m, N] (d_dtype as te_mxfp8_gemm)
+ *   bias        bf16 [G, N] iff epi != NONE; aux bf16 [total_m, N] iff GELU-aux
+ *   Shapes: total_m >= 0, N % 16 == 0, K % 128 == 0, K > 0, N > 0.
+ *   workspace: none (NULL / 0).
+ */
+te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_splits, int64_t total_m,
+                                const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt,
+                                const uint8_t* b, const uint8_t* b_scale, te_dtype b_fmt,
+                                int64_t N, int64_t K,
+                                void* d, te_dtype d_dtype, te_epilogue epi,
+                                const uint16_t* bias, uint16_t* aux,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TEMX_H */

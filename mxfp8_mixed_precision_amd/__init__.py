@@ -1,0 +1,189 @@
+"""Python binding of libtemx.so, the MXFP8 Linear hot path for MI355X (gfx950).
+
+Every function named ``te_*`` marshals torch tensors (device memory) and the
+current HIP stream into the C entry point of the same name declared in
+``include/temx.h``; all computation happens in the library's HIP kernels.
+The helpers without the prefix only allocate outputs with torch and call the
+``te_*`` functions.  There is no fallback: importing this package fails if
+the library has not been built (``python -m mxfp8_mixed_precision_amd.build``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtemx.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m mxfp8_mixed_precision_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+# enum values of include/temx.h
+TE_OK, TE_ERR_NULL, TE_ERR_SHAPE, TE_ERR_ALIGN, TE_ERR_DTYPE, TE_ERR_WORKSPACE, TE_ERR_HIP, TE_ERR_VALUE = range(8)
+TE_BF16, TE_FP32, TE_E4M3, TE_E5M2, TE_E8M0 = range(5)
+TE_EPI_NONE, TE_EPI_BIAS, TE_EPI_BIAS_GELU_AUX = range(3)
+TE_ROWWISE, TE_COLWISE, TE_BOTH = 1, 2, 3
+
+FORMATS = {"e4m3": TE_E4M3, "e5m2": TE_E5M2}
+EPILOGUES = {"none": TE_EPI_NONE, "bias": TE_EPI_BIAS, "bias_gelu_aux": TE_EPI_BIAS_GELU_AUX}
+DIRECTIONS = {"row": TE_ROWWISE, "col": TE_COLWISE, "both": TE_BOTH}
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_SIGS = {
+    "te_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "te_amax_workspace_size": (_sz, [_i64]),
+    "te_amax_reduce": (ctypes.c_int, [_vp, _i64, _vp, _vp, _sz, _vp]),
+    "te_fp8_cast_current_scaling": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "te_mxfp8_quantize": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]),
+    "te_mxfp8_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "te_mxfp8_gemm": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _i64, _i64, _i64,
+                                     _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
+    "te_mxfp8_grouped_gemm": (ctypes.c_int, [_i32, _vp, _i64, _vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int,
+                                             _i64, _i64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class TemxError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {te_status_str(status)}")
+        self.status = status
+
+
+def te_status_str(status: int) -> str:
+    return _lib.te_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != TE_OK:
+        raise TemxError(fn, status)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _fmt(f) -> int:
+    return FORMATS[f] if isinstance(f, str) else int(f)
+
+
+# ---------------------------------------------------------------- entry points
+
+def te_amax_workspace_size(n: int) -> int:
+    return int(_lib.te_amax_workspace_size(int(n)))
+
+
+def te_amax_reduce(x, amax_out, workspace, stream=None) -> None:
+    _check("te_amax_reduce", _lib.te_amax_reduce(_ptr(x), x.numel(), _ptr(amax_out), _ptr(workspace),
+                                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def te_fp8_cast_current_scaling(x, fmt, q_out, amax_out, scale_out, scale_inv_out, workspace, stream=None) -> None:
+    _check("te_fp8_cast_current_scaling", _lib.te_fp8_cast_current_scaling(
+        _ptr(x), x.numel(), _fmt(fmt), _ptr(q_out), _ptr(amax_out), _ptr(scale_out), _ptr(scale_inv_out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def te_mxfp8_quantize(x, fmt, direction, q_row=None, s_row=None, q_col=None, s_col=None, stream=None) -> None:
+    d = DIRECTIONS[direction] if isinstance(direction, str) else int(direction)
+    rows, cols = x.shape
+    _check("te_mxfp8_quantize", _lib.te_mxfp8_quantize(
+        _ptr(x), rows, cols, _fmt(fmt), d, _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(stream)))
+
+
+def te_mxfp8_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    return int(_lib.te_mxfp8_gemm_workspace_size(M, N, K))
+
+
+def te_mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, d, epilogue="none", bias=None, aux=None,
+                  workspace=None, stream=None) -> None:
+    M, K = a.shape
+    N = b.shape[0]
+    d_dtype = TE_BF16 if d.dtype == torch.bfloat16 else TE_FP32
+    epi = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("te_mxfp8_gemm", _lib.te_mxfp8_gemm(
+        _ptr(a), _ptr(a_scale), _fmt(a_fmt), _ptr(b), _ptr(b_scale), _fmt(b_fmt), M, N, K,
+        _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def te_mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n: int, d, epilogue="none",
+                          bias=None, aux=None, workspace=None, stream=None) -> None:
+    total_m, K = a.shape
+    d_dtype = TE_BF16 if d.dtype == torch.bfloat16 else TE_FP32
+    epi = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("te_mxfp8_grouped_gemm", _lib.te_mxfp8_grouped_gemm(
+        m_splits.numel(), _ptr(m_splits), total_m, _ptr(a), _ptr(a_scale), _fmt(a_fmt), _ptr(b), _ptr(b_scale),
+        _fmt(b_fmt), n, K, _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+# ------------------------------------------------------- allocating helpers
+
+def mxfp8_quantize(x, fmt="e4m3", direction="row", stream=None):
+    """bf16 [rows, cols] (torch.bfloat16 or int16/uint16 bits) -> (q_row, s_row, q_col, s_col), None where
+    a direction is not requested."""
+    rows, cols = x.shape
+    d = DIRECTIONS[direction]
+    dev = x.device
+    q_row = s_row = q_col = s_col = None
+    if d & TE_ROWWISE:
+        q_row = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        s_row = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    if d & TE_COLWISE:
+        q_col = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+        s_col = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
+    te_mxfp8_quantize(x, fmt, d, q_row, s_row, q_col, s_col, stream)
+    return q_row, s_row, q_col, s_col
+
+
+def amax(x, stream=None):
+    ws = torch.empty(max(te_amax_workspace_size(x.numel()), 4), dtype=torch.uint8, device=x.device)
+    out = torch.empty(1, dtype=torch.float32, device=x.device)
+    te_amax_reduce(x, out, ws, stream)
+    return out
+
+
+def fp8_cast_current_scaling(x, fmt="e4m3", stream=None):
+    """-> (q, amax, scale, scale_inv) with q shaped like x."""
+    dev = x.device
+    ws = torch.empty(max(te_amax_workspace_size(x.numel()), 4), dtype=torch.uint8, device=dev)
+    q = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    a, s, si = (torch.empty(1, dtype=torch.float32, device=dev) for _ in range(3))
+    te_fp8_cast_current_scaling(x, fmt, q, a, s, si, ws, stream)
+    return q, a, s, si
+
+
+def mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, epilogue="none", bias=None, out_dtype=torch.bfloat16,
+               stream=None):
+    """-> (D, aux) for D = epilogue(A . B^T); aux is None unless epilogue == "bias_gelu_aux"."""
+    M, N = a.shape[0], b.shape[0]
+    d = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    aux = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if epilogue == "bias_gelu_aux" else None
+    te_mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, d, epilogue, bias, aux, None, stream)
+    return d, aux
+
+
+def mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n, epilogue="none", bias=None,
+                       out_dtype=torch.bfloat16, stream=None):
+    total_m = a.shape[0]
+    d = torch.empty((total_m, n), dtype=out_dtype, device=a.device)
+    aux = torch.empty((total_m, n), dtype=torch.bfloat16, device=a.device) if epilogue == "bias_gelu_aux" else None
+    te_mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n, d, epilogue, bias, aux, None, stream)
+    return d, aux

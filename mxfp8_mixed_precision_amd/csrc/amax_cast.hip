@@ -1,0 +1,205 @@
+// Per-tensor amax (two-stage) and the current-scaling FP8 cast for gfx950.
+//
+// Method: "Transformer Engine On ROCm and AMDGPU", "Two-stage amax Kernel":
+// per-workgroup maxima, then one small reduction over them, no atomics.
+// "Workflow: NVIDIA TransformerEngine FP8 Training Quickstart", Step 4:
+// Float8CurrentScaling takes the scale from the current tensor; margin 0 as
+// in the "Getting Started" (TE JAX) recipes.  Readings where the pages are
+// silent: scale = fl32(fmt_max / amax) (1 when amax is 0, the largest finite
+// float when the quotient overflows), scale_inv = fl32(1 / scale), and each
+// element is the saturating round-to-nearest-even encode of fl32(x * scale).
+//
+// The maximum is taken over the |x| bit patterns as integers (exact for
+// non-NaN bf16), so it does not depend on the reduction order.
+#include <float.h>
+
+#include "temx_device.h"
+
+namespace temx {
+namespace {
+
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxUnroll = 4;
+constexpr int64_t kAmaxMaxBlocks = 1024;
+
+int64_t amax_blocks(int64_t n) {
+  const int64_t chunks = n / 8;
+  int64_t b = (chunks + kAmaxThreads * kAmaxUnroll - 1) / (kAmaxThreads * kAmaxUnroll);
+  if (b < 1) b = 1;
+  return b > kAmaxMaxBlocks ? kAmaxMaxBlocks : b;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t block_max(uint32_t v) {
+  __shared__ uint32_t red[kAmaxThreads / 64];
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t m = red[0];
+#pragma unroll
+  for (int i = 1; i < kAmaxThreads / 64; ++i) m = max(m, red[i]);
+  return m;
+}
+
+// Stage one: grid-stride over 16-byte chunks; the n % 8 tail is read by
+// block 0.  partial[blockIdx.x] = max |x| bits over the block's share.
+__global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                    uint32_t* __restrict__ partial) {
+  const int64_t nchunks = n / 8;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads * kAmaxUnroll;
+  for (int64_t c0 = (int64_t)blockIdx.x * kAmaxThreads * kAmaxUnroll + threadIdx.x; c0 < nchunks; c0 += stride) {
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int64_t c = c0 + (int64_t)u * kAmaxThreads;
+      v[u] = c < nchunks ? load_nt16(xv + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) m = max(m, absmax_bits8(v[u]));
+  }
+  if (blockIdx.x == 0) {
+    const int64_t i = nchunks * 8 + threadIdx.x;
+    if (i < n) m = max(m, (uint32_t)(x[i] & 0x7FFFu));
+  }
+  m = block_max(m);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+// Stage two: one workgroup reduces the partial maxima; with a format it
+// also writes scale and scale_inv.
+template <int FMT>  // 0 = amax only
+__global__ __launch_bounds__(kAmaxThreads) void amax_final_kernel(const uint32_t* __restrict__ partial, int nparts,
+                                                                  float* __restrict__ amax_out,
+                                                                  float* __restrict__ scale_out,
+                                                                  float* __restrict__ scale_inv_out) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += kAmaxThreads) m = max(m, partial[i]);
+  m = block_max(m);
+  if (threadIdx.x != 0) return;
+  const float amax = bf16_bits_to_float(m);
+  *amax_out = amax;
+  if constexpr (FMT != 0) {
+    // A float32 quotient rounded once to float64 and then to float32 equals the
+    // correctly rounded float32 quotient (53 >= 2*24 + 2; Figueroa, "When is
+    // double rounding innocuous?", 1995), so these are IEEE float32 divisions.
+    float scale = 1.0f;
+    if (amax != 0.0f) {
+      scale = (float)((double)FmtTraits<FMT>::max_value / (double)amax);
+      if (!(scale <= FLT_MAX)) scale = FLT_MAX;
+    }
+    *scale_out = scale;
+    *scale_inv_out = (float)(1.0 / (double)scale);
+  }
+}
+
+// Cast: y = fl32(x * scale), clamped to the finite range, then the plain
+// round-to-nearest-even converts v_cvt_pk_{fp8,bf8}_f32.
+template <int FMT>
+__device__ __forceinline__ uint32_t cast4(uint32_t p0, uint32_t p1, float scale) {
+  constexpr float mx = FmtTraits<FMT>::max_value;
+  float a = __uint_as_float(p0 << 16) * scale, b = __uint_as_float(p0 & 0xFFFF0000u) * scale;
+  float c = __uint_as_float(p1 << 16) * scale, d = __uint_as_float(p1 & 0xFFFF0000u) * scale;
+  a = __builtin_amdgcn_fmed3f(a, -mx, mx);
+  b = __builtin_amdgcn_fmed3f(b, -mx, mx);
+  c = __builtin_amdgcn_fmed3f(c, -mx, mx);
+  d = __builtin_amdgcn_fmed3f(d, -mx, mx);
+  int r;
+  if constexpr (FMT == TE_E4M3) {
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  } else {
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, r, true);
+  }
+  return (uint32_t)r;
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                   const float* __restrict__ scale_ptr, uint8_t* __restrict__ q) {
+  const float scale = *scale_ptr;
+  const int64_t nchunks = n / 8;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c < nchunks) {
+    const uint4 v = load_nt16(reinterpret_cast<const uint4*>(x) + c);
+    uint2 r;
+    r.x = cast4<FMT>(v.x, v.y, scale);
+    r.y = cast4<FMT>(v.z, v.w, scale);
+    reinterpret_cast<uint2*>(q)[c] = r;
+  } else if (c == nchunks) {
+    // tail of n % 8 elements
+    for (int64_t i = nchunks * 8; i < n; ++i) {
+      const uint32_t h = x[i];
+      q[i] = (uint8_t)(cast4<FMT>(h, 0, scale) & 0xFFu);
+    }
+  }
+}
+
+te_status launch_amax(const uint16_t* x, int64_t n, uint32_t* partial, int64_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL(amax_partial_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream, x, n, partial);
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace temx
+
+using namespace temx;
+
+extern "C" size_t te_amax_workspace_size(int64_t n) {
+  if (n < 0) return 0;
+  return (size_t)amax_blocks(n) * sizeof(uint32_t);
+}
+
+extern "C" te_status te_amax_reduce(const uint16_t* x, int64_t n, float* amax_out, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  TE_REQUIRE(n >= 0, TE_ERR_SHAPE);
+  TE_REQUIRE(amax_out != nullptr && workspace != nullptr, TE_ERR_NULL);
+  TE_REQUIRE(n == 0 || x != nullptr, TE_ERR_NULL);
+  TE_REQUIRE(n == 0 || aligned16(x), TE_ERR_ALIGN);
+  TE_REQUIRE(((uintptr_t)workspace & 3u) == 0, TE_ERR_ALIGN);
+  const int64_t blocks = amax_blocks(n);
+  TE_REQUIRE(workspace_bytes >= (size_t)blocks * sizeof(uint32_t), TE_ERR_WORKSPACE);
+  uint32_t* partial = static_cast<uint32_t*>(workspace);
+  if (launch_amax(x, n, partial, blocks, stream) != TE_OK) return TE_ERR_HIP;
+  hipLaunchKernelGGL(amax_final_kernel<0>, dim3(1), dim3(kAmaxThreads), 0, stream, partial, (int)blocks, amax_out,
+                     nullptr, nullptr);
+  return launch_status();
+}
+
+extern "C" te_status te_fp8_cast_current_scaling(const uint16_t* x, int64_t n, te_dtype fmt, uint8_t* q_out,
+                                                 float* amax_out, float* scale_out, float* scale_inv_out,
+                                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  TE_REQUIRE(is_fp8(fmt), TE_ERR_DTYPE);
+  TE_REQUIRE(n >= 0, TE_ERR_SHAPE);
+  TE_REQUIRE(amax_out != nullptr && scale_out != nullptr && scale_inv_out != nullptr && workspace != nullptr,
+             TE_ERR_NULL);
+  TE_REQUIRE(n == 0 || (x != nullptr && q_out != nullptr), TE_ERR_NULL);
+  TE_REQUIRE(n == 0 || (aligned16(x) && aligned16(q_out)), TE_ERR_ALIGN);
+  TE_REQUIRE(((uintptr_t)workspace & 3u) == 0, TE_ERR_ALIGN);
+  const int64_t blocks = amax_blocks(n);
+  TE_REQUIRE(workspace_bytes >= (size_t)blocks * sizeof(uint32_t), TE_ERR_WORKSPACE);
+  TE_REQUIRE(n / 8 / 256 < (int64_t)1 << 31, TE_ERR_SHAPE);
+  uint32_t* partial = static_cast<uint32_t*>(workspace);
+  if (launch_amax(x, n, partial, blocks, stream) != TE_OK) return TE_ERR_HIP;
+  if (fmt == TE_E4M3)
+    hipLaunchKernelGGL(amax_final_kernel<TE_E4M3>, dim3(1), dim3(kAmaxThreads), 0, stream, partial, (int)blocks,
+                       amax_out, scale_out, scale_inv_out);
+  else
+    hipLaunchKernelGGL(amax_final_kernel<TE_E5M2>, dim3(1), dim3(kAmaxThreads), 0, stream, partial, (int)blocks,
+                       amax_out, scale_out, scale_inv_out);
+  if (launch_status() != TE_OK) return TE_ERR_HIP;
+  if (n == 0) return TE_OK;
+  const int64_t grid = (n / 8 + 1 + 255) / 256;  // + 1 covers the tail thread
+  if (fmt == TE_E4M3)
+    hipLaunchKernelGGL(cast_kernel<TE_E4M3>, dim3((unsigned)grid), dim3(256), 0, stream, x, n, scale_out, q_out);
+  else
+    hipLaunchKernelGGL(cast_kernel<TE_E5M2>, dim3((unsigned)grid), dim3(256), 0, stream, x, n, scale_out, q_out);
+  return launch_status();
+}

@@ -1,0 +1,398 @@
+// MXFP8 GEMM ("TN": A [M, K], B [N, K], D = A . B^T) with bias / GELU(tanh) /
+// GELU-aux epilogues, dense and grouped, for gfx950.
+//
+// Method: "HipKittens MXFP8 GEMM Support" (ROCm/TransformerEngine PR #566):
+// an MXFP8 GEMM with BIAS and GELU AUX epilogues; review threads: 1-D MXFP8
+// scaling, K % 128 == 0, M % 16 == 0, N % 16 == 0, "TN" operands.  GELU is
+// the tanh approximation ("Getting Started", TE JAX quickstart).  The grouped
+// form is the single-launch grouped GEMM of "Transformer Engine On ROCm and
+// AMDGPU" ("Grouped GEMM using CK_Tile").
+//
+// Design for CDNA4:
+// * v_mfma_scale_f32_16x16x128_f8f6f4 consumes the fp8 codes and the E8M0
+//   block scales directly.  Its operand layout (lane l = 16 g + r holds row r,
+//   bytes 0-15 = K 16g..16g+15 and bytes 16-31 = K 64+16g..; the scale byte
+//   of K-block kb comes from lane r + 16 kb) means a lane loads two 16-byte
+//   chunks of one row and supplies the scale of block g of that row.
+// * The MFMA's A operand is a B-tile row (n) and its B operand an A-tile row
+//   (m), so each lane ends with 4 consecutive output columns of one row: the
+//   epilogue stores 8 bytes (bf16) per lane straight from registers.
+// * 256 x 256 workgroup tile, 4 waves in 2 x 2, 128 x 128 per wave (8 x 8
+//   MFMA tiles = 256 fp32 accumulators per lane), K step 128.
+// * A, B and their scale tiles are copied global -> LDS with the gfx950
+//   direct-to-LDS loads (global_load_lds_dwordx4 / _dword), double-buffered
+//   (2 x 66 KB).  16-byte chunks of a 128-byte LDS row are XOR-swizzled so
+//   the ds_read_b128 of 16 consecutive rows hit distinct banks.
+// * Workgroup -> tile mapping is XCD-aware: workgroups are dealt round-robin
+//   to the 8 XCDs, so each XCD is given a contiguous run of tiles (grouped in
+//   bands of 4 row-tiles) and its L2 sees the reuse.
+// * Ragged M / N tails: loads clamp the row index (valid memory, unused
+//   results), stores are masked.  The workspace is 0 bytes.
+#include "temx_device.h"
+
+namespace temx {
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int kThreads = 256;
+constexpr int WT = 128;        // wave tile edge
+constexpr int FR = WT / 16;    // MFMA tiles per wave edge
+constexpr int kAData = BM * BK;
+constexpr int kBData = BN * BK;
+constexpr int kAScale = BM * 4;
+constexpr int kBScale = BN * 4;
+constexpr int kStage = kAData + kBData + kAScale + kBScale;
+constexpr int kLds = 2 * kStage;
+constexpr int kGroupM = 4;      // row-tile band of the raster order
+constexpr int kMaxGroups = 1024;
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int F> struct MfmaFmt;  // cbsz / blgp operand format codes
+template <> struct MfmaFmt<TE_E4M3> { static constexpr int v = 0; };
+template <> struct MfmaFmt<TE_E5M2> { static constexpr int v = 1; };
+
+struct Operand {
+  const uint8_t* data;   // [rows, K]
+  const uint8_t* scale;  // [rows, K/32]
+  int64_t row0;          // first row of the tile
+  int64_t last;          // last valid row (loads clamp to it)
+};
+
+// Issue the direct-to-LDS copies of one 256 x 128 data tile and its 256 x 4
+// scale tile.  Wave w copies 8 of the 32 one-kilobyte slices (8 rows each)
+// and one of the four 256-byte scale slices.
+__device__ __forceinline__ void load_operand(uint8_t* lds_data, uint8_t* lds_scale, const Operand& op,
+                                             int64_t K, int kt, int wave, int lane) {
+  const int64_t kq = K / 32;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = wave + 4 * i;
+    const int row = 8 * q + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    int64_t gr = op.row0 + row;
+    gr = gr < op.last ? gr : op.last;
+    const uint8_t* src = op.data + gr * K + (int64_t)kt * BK + chunk * 16;
+    __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)(lds_data + q * 1024), 16, 0, 0);
+  }
+  int64_t gr = op.row0 + 64 * wave + lane;
+  gr = gr < op.last ? gr : op.last;
+  const uint8_t* ssrc = op.scale + gr * kq + (int64_t)kt * 4;
+  __builtin_amdgcn_global_load_lds((global_void_t*)ssrc, (lds_void_t*)(lds_scale + wave * 256), 4, 0, 0);
+}
+
+struct Frag {
+  v8i v;
+  int s;
+};
+
+// Two 16-byte chunks (K 16g.. and 64+16g..) of LDS row `row`, and the E8M0
+// byte of block g of that row in the low byte of s.
+__device__ __forceinline__ Frag read_frag(const uint8_t* data, const uint8_t* scale, int row, int g, int sw) {
+  const uint8_t* p = data + row * BK;
+  const uint4 lo = *reinterpret_cast<const uint4*>(p + ((g ^ sw) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + (((g + 4) ^ sw) << 4));
+  Frag f;
+  f.v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  f.s = (int)(*reinterpret_cast<const uint32_t*>(scale + row * 4) >> (8 * g));
+  return f;
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ void compute_stage(const uint8_t* stage, v4f (&acc)[FR][FR], int wm, int wn, int lane) {
+  const uint8_t* a_data = stage;
+  const uint8_t* b_data = stage + kAData;
+  const uint8_t* a_scale = stage + kAData + kBData;
+  const uint8_t* b_scale = a_scale + kAScale;
+  const int g = lane >> 4, r = lane & 15, sw = swz(r);
+  Frag bop[FR];
+#pragma unroll
+  for (int j = 0; j < FR; ++j) bop[j] = read_frag(a_data, a_scale, wm * WT + 16 * j + r, g, sw);
+#pragma unroll
+  for (int i = 0; i < FR; ++i) {
+    const Frag aop = read_frag(b_data, b_scale, wn * WT + 16 * i + r, g, sw);
+#pragma unroll
+    for (int j = 0; j < FR; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop.v, bop[j].v, acc[i][j], MfmaFmt<FB>::v,
+                                                                   MfmaFmt<FA>::v, 0, aop.s, 0, bop[j].s);
+  }
+}
+
+template <int FA, int FB>
+__device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[FR][FR], const Operand& A, const Operand& B,
+                                         int64_t K, int wave, int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+  for (int i = 0; i < FR; ++i)
+#pragma unroll
+    for (int j = 0; j < FR; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int kt_n = (int)(K / BK);
+  if (kt_n == 0) return;
+  load_operand(lds, lds + kAData + kBData, A, K, 0, wave, lane);
+  load_operand(lds + kAData, lds + kAData + kBData + kAScale, B, K, 0, wave, lane);
+  for (int kt = 0; kt < kt_n; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kt + 1 < kt_n) {
+      uint8_t* nx = lds + ((kt + 1) & 1) * kStage;
+      load_operand(nx, nx + kAData + kBData, A, K, kt + 1, wave, lane);
+      load_operand(nx + kAData, nx + kAData + kBData + kAScale, B, K, kt + 1, wave, lane);
+    }
+    compute_stage<FA, FB>(lds + (kt & 1) * kStage, acc, wm, wn, lane);
+  }
+}
+
+// Epilogue from registers.  acc[i][j][e] is D[m][n] with
+// m = m0 + 128 wm + 16 j + (lane & 15), n = n0 + 128 wn + 16 i + 4 (lane >> 4) + e.
+template <int EPI, int OUT>
+__device__ __forceinline__ void epilogue(const v4f (&acc)[FR][FR], void* d, uint16_t* aux, const uint16_t* bias,
+                                         int64_t m0, int64_t m_end, int64_t n0, int64_t N, int wave, int lane) {
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int i = 0; i < FR; ++i) {
+    const int64_t n = n0 + wn * WT + 16 * i + 4 * g;
+    if (n >= N) continue;
+    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+    if constexpr (EPI != TE_EPI_NONE) {
+      const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+      b0 = bf16_bits_to_float(bb.x & 0xFFFFu);
+      b1 = bf16_bits_to_float(bb.x >> 16);
+      b2 = bf16_bits_to_float(bb.y & 0xFFFFu);
+      b3 = bf16_bits_to_float(bb.y >> 16);
+    }
+#pragma unroll
+    for (int j = 0; j < FR; ++j) {
+      const int64_t m = m0 + wm * WT + 16 * j + r;
+      if (m >= m_end) continue;
+      float v0 = acc[i][j][0] + b0, v1 = acc[i][j][1] + b1, v2 = acc[i][j][2] + b2, v3 = acc[i][j][3] + b3;
+      if constexpr (EPI == TE_EPI_BIAS_GELU_AUX) {
+        *reinterpret_cast<uint2*>(aux + m * N + n) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        v0 = gelu_tanh(v0);
+        v1 = gelu_tanh(v1);
+        v2 = gelu_tanh(v2);
+        v3 = gelu_tanh(v3);
+      }
+      if constexpr (OUT == TE_BF16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(d) + m * N + n) =
+            make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(d) + m * N + n) = make_float4(v0, v1, v2, v3);
+      }
+    }
+  }
+}
+
+struct GemmParams {
+  const uint8_t* a;
+  const uint8_t* a_scale;
+  const uint8_t* b;
+  const uint8_t* b_scale;
+  void* d;
+  const uint16_t* bias;
+  uint16_t* aux;
+  int64_t M, N, K;
+  const int32_t* m_splits;  // grouped only
+  int32_t groups;           // grouped only
+};
+
+// Dense: one workgroup per 256 x 256 tile.
+template <int FA, int FB, int EPI, int OUT>
+__global__ __launch_bounds__(kThreads) void mx_gemm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntm = (int)((p.M + BM - 1) / BM), ntn = (int)((p.N + BN - 1) / BN);
+  const int ntiles = ntm * ntn;
+  // XCD-aware remap: workgroup b runs on XCD b % 8; give each XCD a
+  // contiguous run of tiles.
+  const int bid = blockIdx.x;
+  const int per = ntiles / 8;
+  const int t = bid < 8 * per ? (bid % 8) * per + bid / 8 : bid;
+  // raster in bands of kGroupM row-tiles
+  const int band = t / (kGroupM * ntn);
+  const int first_tm = band * kGroupM;
+  const int band_rows = min(ntm - first_tm, kGroupM);
+  const int in_band = t % (kGroupM * ntn);
+  const int tm = first_tm + in_band % band_rows;
+  const int tn = in_band / band_rows;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  Operand A{p.a, p.a_scale, m0, p.M - 1};
+  Operand B{p.b, p.b_scale, n0, p.N - 1};
+  v4f acc[FR][FR];
+  mainloop<FA, FB>(lds, acc, A, B, p.K, wave, lane);
+  epilogue<EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
+}
+
+// Grouped: a persistent grid walks the flat list of (expert row-tile,
+// n-tile) pairs, built in LDS from the device-resident splits.
+template <int FA, int FB, int EPI, int OUT>
+__global__ __launch_bounds__(kThreads) void mx_grouped_gemm_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+  __shared__ int tile_prefix[kMaxGroups + 1];
+  __shared__ int64_t row_off[kMaxGroups + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = p.groups;
+  const int64_t total_m = p.M;
+  if (threadIdx.x == 0) {
+    int tiles = 0;
+    int64_t off = 0;
+    tile_prefix[0] = 0;
+    row_off[0] = 0;
+    for (int e = 0; e < G; ++e) {
+      int64_t me = p.m_splits[e];
+      me = me < 0 ? 0 : me;
+      int64_t end = off + me;
+      end = end > total_m ? total_m : end;
+      tiles += (int)((end - off + BM - 1) / BM);
+      off = end;
+      tile_prefix[e + 1] = tiles;
+      row_off[e + 1] = off;
+    }
+  }
+  __syncthreads();
+  const int ntn = (int)((p.N + BN - 1) / BN);
+  const int total = tile_prefix[G] * ntn;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, nslots = gridDim.x / 8;
+  const int chunk = (total + 7) / 8;
+  const int t_end = min((xcd + 1) * chunk, total);
+  for (int t = xcd * chunk + slot; t < t_end; t += nslots) {
+    const int rt = t / ntn, tn = t % ntn;
+    int lo = 0, hi = G;  // find e with tile_prefix[e] <= rt < tile_prefix[e + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_prefix[mid] <= rt) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int64_t m0 = row_off[e] + (int64_t)(rt - tile_prefix[e]) * BM;
+    const int64_t m_end = row_off[e + 1];
+    const int64_t n0 = (int64_t)tn * BN;
+    Operand A{p.a, p.a_scale, m0, m_end - 1};
+    Operand B{p.b + (int64_t)e * p.N * p.K, p.b_scale + (int64_t)e * p.N * (p.K / 32), n0, p.N - 1};
+    v4f acc[FR][FR];
+    __syncthreads();  // the previous tile's last reads of stage 0/1 are done
+    mainloop<FA, FB>(lds, acc, A, B, p.K, wave, lane);
+    epilogue<EPI, OUT>(acc, p.d, p.aux, EPI == TE_EPI_NONE ? nullptr : p.bias + (int64_t)e * p.N, m0, m_end, n0,
+                       p.N, wave, lane);
+  }
+}
+
+template <bool GROUPED, int FA, int FB, int EPI, int OUT>
+te_status launch4(const GemmParams& p, dim3 grid, hipStream_t stream) {
+  if constexpr (GROUPED)
+    hipLaunchKernelGGL((mx_grouped_gemm_kernel<FA, FB, EPI, OUT>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<FA, FB, EPI, OUT>), grid, dim3(kThreads), 0, stream, p);
+  return launch_status();
+}
+
+template <bool GROUPED, int FA, int FB, int EPI>
+te_status launch3(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stream) {
+  return out == TE_BF16 ? launch4<GROUPED, FA, FB, EPI, TE_BF16>(p, grid, stream)
+                        : launch4<GROUPED, FA, FB, EPI, TE_FP32>(p, grid, stream);
+}
+
+template <bool GROUPED, int FA, int FB>
+te_status launch2(const GemmParams& p, te_epilogue epi, te_dtype out, dim3 grid, hipStream_t stream) {
+  switch (epi) {
+    case TE_EPI_NONE: return launch3<GROUPED, FA, FB, TE_EPI_NONE>(p, out, grid, stream);
+    case TE_EPI_BIAS: return launch3<GROUPED, FA, FB, TE_EPI_BIAS>(p, out, grid, stream);
+    default: return launch3<GROUPED, FA, FB, TE_EPI_BIAS_GELU_AUX>(p, out, grid, stream);
+  }
+}
+
+template <bool GROUPED>
+te_status launch(const GemmParams& p, te_dtype fa, te_dtype fb, te_epilogue epi, te_dtype out, dim3 grid,
+                 hipStream_t stream) {
+  if (fa == TE_E4M3 && fb == TE_E4M3) return launch2<GROUPED, TE_E4M3, TE_E4M3>(p, epi, out, grid, stream);
+  if (fa == TE_E5M2 && fb == TE_E4M3) return launch2<GROUPED, TE_E5M2, TE_E4M3>(p, epi, out, grid, stream);
+  return launch2<GROUPED, TE_E4M3, TE_E5M2>(p, epi, out, grid, stream);
+}
+
+te_status check_common(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,
+                       const uint8_t* b_scale, te_dtype b_fmt, void* d, te_dtype d_dtype, te_epilogue epi,
+                       const uint16_t* bias, uint16_t* aux, bool any_rows, bool any_k) {
+  TE_REQUIRE(epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX, TE_ERR_VALUE);
+  TE_REQUIRE(is_fp8(a_fmt) && is_fp8(b_fmt), TE_ERR_DTYPE);
+  TE_REQUIRE(!(a_fmt == TE_E5M2 && b_fmt == TE_E5M2), TE_ERR_DTYPE);
+  TE_REQUIRE(d_dtype == TE_BF16 || d_dtype == TE_FP32, TE_ERR_DTYPE);
+  TE_REQUIRE((epi != TE_EPI_NONE) == (bias != nullptr), TE_ERR_NULL);
+  TE_REQUIRE((epi == TE_EPI_BIAS_GELU_AUX) == (aux != nullptr), TE_ERR_NULL);
+  if (!any_rows) return TE_OK;
+  TE_REQUIRE(d != nullptr, TE_ERR_NULL);
+  TE_REQUIRE(aligned16(d), TE_ERR_ALIGN);
+  if (any_k) {  // with K == 0 the operands are never read
+    TE_REQUIRE(a && a_scale && b && b_scale, TE_ERR_NULL);
+    TE_REQUIRE(aligned16(a) && aligned16(b), TE_ERR_ALIGN);
+    TE_REQUIRE(((uintptr_t)a_scale & 3u) == 0 && ((uintptr_t)b_scale & 3u) == 0, TE_ERR_ALIGN);
+  }
+  TE_REQUIRE(bias == nullptr || ((uintptr_t)bias & 7u) == 0, TE_ERR_ALIGN);
+  TE_REQUIRE(aux == nullptr || aligned16(aux), TE_ERR_ALIGN);
+  return TE_OK;
+}
+
+}  // namespace
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) cu = 256;
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
+
+}  // namespace temx
+
+using namespace temx;
+
+extern "C" size_t te_mxfp8_gemm_workspace_size(int64_t, int64_t, int64_t) { return 0; }
+
+extern "C" te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,
+                                   const uint8_t* b_scale, te_dtype b_fmt, int64_t M, int64_t N, int64_t K, void* d,
+                                   te_dtype d_dtype, te_epilogue epi, const uint16_t* bias, uint16_t* aux,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  TE_REQUIRE(M >= 0 && N >= 0 && K >= 0, TE_ERR_SHAPE);
+  TE_REQUIRE(K % 128 == 0 && M % 16 == 0 && N % 16 == 0, TE_ERR_SHAPE);
+  TE_REQUIRE(M <= ((int64_t)1 << 31) - BM && N <= ((int64_t)1 << 31) - BN && K <= ((int64_t)1 << 31) - BK,
+             TE_ERR_SHAPE);
+  const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  TE_REQUIRE(ntiles < ((int64_t)1 << 31), TE_ERR_SHAPE);
+  te_status st = check_common(a, a_scale, a_fmt, b, b_scale, b_fmt, d, d_dtype, epi, bias, aux, M > 0 && N > 0, K > 0);
+  if (st != TE_OK) return st;
+  if (M == 0 || N == 0) return TE_OK;
+  GemmParams p{a, a_scale, b, b_scale, d, bias, aux, M, N, K, nullptr, 0};
+  return launch<false>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)ntiles), stream);
+}
+
+extern "C" te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_splits, int64_t total_m,
+                                           const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt,
+                                           const uint8_t* b, const uint8_t* b_scale, te_dtype b_fmt, int64_t N,
+                                           int64_t K, void* d, te_dtype d_dtype, te_epilogue epi,
+                                           const uint16_t* bias, uint16_t* aux, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  TE_REQUIRE(num_groups >= 1 && num_groups <= kMaxGroups, TE_ERR_SHAPE);
+  TE_REQUIRE(total_m >= 0 && N > 0 && K > 0, TE_ERR_SHAPE);
+  TE_REQUIRE(K % 128 == 0 && N % 16 == 0, TE_ERR_SHAPE);
+  TE_REQUIRE(total_m <= ((int64_t)1 << 31) - BM && N <= ((int64_t)1 << 31) - BN && K <= ((int64_t)1 << 31) - BK,
+             TE_ERR_SHAPE);
+  TE_REQUIRE((total_m / BM + num_groups) * ((N + BN - 1) / BN) < ((int64_t)1 << 31), TE_ERR_SHAPE);
+  TE_REQUIRE(m_splits != nullptr, TE_ERR_NULL);
+  TE_REQUIRE(((uintptr_t)m_splits & 3u) == 0, TE_ERR_ALIGN);
+  te_status st = check_common(a, a_scale, a_fmt, b, b_scale, b_fmt, d, d_dtype, epi, bias, aux, total_m > 0, true);
+  if (st != TE_OK) return st;
+  if (total_m == 0) return TE_OK;
+  GemmParams p{a, a_scale, b, b_scale, d, bias, aux, total_m, N, K, m_splits, num_groups};
+  int grid = device_cu_count();
+  grid = grid < 8 ? 8 : (grid / 8) * 8;
+  return launch<true>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)grid), stream);
+}

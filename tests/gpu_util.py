@@ -1,0 +1,78 @@
+"""Helpers for the GPU parity tests: host <-> device copies of bit patterns."""
+
+import numpy as np
+import torch
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    """numpy array -> torch CUDA tensor with the same bytes (uint16 travels as int16)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    a = t.detach().cpu()
+    if a.dtype == torch.int16:
+        return a.numpy().view(np.uint16)
+    if a.dtype == torch.bfloat16:
+        return a.view(torch.int16).numpy().view(np.uint16)
+    return a.numpy()
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode bf16 results (uint16) for comparison (test-side, not the oracle)."""
+    b = np.ascontiguousarray(bits.astype(np.uint32) << 16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def finite_bf16_patterns() -> np.ndarray:
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    return bits[((bits >> 7) & 0xFF) != 0xFF]
+
+
+GELU_SLOPE = 1.13  # max |d gelu_tanh / dx| (about 1.129 near x = 1.5)
+
+
+def gemm_within(got, ref, s, bias_bits, h, k, through_gelu=False):
+    """Acceptance of GEMM outputs against the float64 oracle.
+
+    |y - y_ref| <= 2^-8 |y_ref| + c (1e-5 (S + |bias|) + H + (K/16) 2^-24 S),
+    where H bounds the scaled MFMA's in-group truncation and (K/16) 2^-24 S
+    its K/16 fp32 accumulations (tests/mfma_model.py), and c = 1 for
+    pre-activation outputs, GELU_SLOPE for outputs taken through GELU (an
+    error in the pre-activation is scaled by at most |gelu'|).
+    Returns (mask within the bound, mask within the stated tolerance alone).
+    """
+    import oracle
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    stated = oracle.tolerance_bound(ref, s, bias_bits)
+    rel = 2.0 ** -8 * np.abs(ref)
+    c = GELU_SLOPE if through_gelu else 1.0
+    bound = rel + c * ((stated - rel) + h + (k / 16.0) * 2.0 ** -24 * s)
+    err = np.abs(got - ref)
+    return err <= bound, err <= stated
+
+
+def bf16_rne(x) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def model_outputs(acc32, bias_bits, epi):
+    """Expected (D, aux) from the fp32 accumulators the MFMA model gives:
+    fp32 bias add, bf16 rounding; D through GELU is returned in float64
+    (the kernel's fp32 GELU is checked to bf16 precision, not bit for bit)."""
+    acc32 = np.asarray(acc32, dtype=np.float32)
+    if epi == "none":
+        return bf16_rne(acc32), None
+    b = (np.asarray(bias_bits, dtype=np.uint32) << 16).view(np.float32)
+    pre = (acc32 + b[None, :]).astype(np.float32)
+    if epi == "bias":
+        return bf16_rne(pre), None
+    import oracle
+    return oracle.gelu_tanh(pre.astype(np.float64)), bf16_rne(pre)

@@ -1,0 +1,148 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point that
+include/temx.h declares, and rejects bad arguments on the host before any
+HIP call (only calls that fail validation are made here, with fake device
+addresses that are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_mixed_precision_amd as te
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "temx.h")
+
+P = 0x10000  # fake, 16-byte aligned device address (never dereferenced)
+P2 = 0x20000
+P3 = 0x30000
+BAD = 0x10004  # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:te_status|size_t|const char\*)\s+(te_\w+)\s*\(", text, re.M)))
+
+
+def test_header_symbols_are_exported():
+    names = declared_functions()
+    assert set(names) == set(te.EXPORTED)
+    lib = ctypes.CDLL(te._LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert te.te_status_str(te.TE_OK) == "TE_OK"
+    for s in range(1, 8):
+        assert te.te_status_str(s).startswith("TE_ERR_")
+    assert te.te_status_str(99) == "unknown te_status"
+
+
+def test_workspace_queries():
+    assert te.te_mxfp8_gemm_workspace_size(8192, 8192, 8192) == 0
+    assert te.te_amax_workspace_size(0) == 4
+    assert te.te_amax_workspace_size(8192 * 8192) == 4 * 1024
+    assert te.te_amax_workspace_size(4096) == 4
+
+
+L = te._lib
+
+
+def quant(x=P, rows=64, cols=64, fmt=te.TE_E4M3, d=te.TE_ROWWISE, qr=P2, sr=P3, qc=None, sc=None):
+    return L.te_mxfp8_quantize(x, rows, cols, fmt, d, qr, sr, qc, sc, None)
+
+
+def test_quantize_validation():
+    assert quant(d=0) == te.TE_ERR_VALUE
+    assert quant(d=4) == te.TE_ERR_VALUE
+    assert quant(fmt=te.TE_BF16) == te.TE_ERR_DTYPE
+    assert quant(fmt=te.TE_E8M0) == te.TE_ERR_DTYPE
+    assert quant(rows=-1) == te.TE_ERR_SHAPE
+    assert quant(cols=48) == te.TE_ERR_SHAPE                      # rowwise needs cols % 32
+    assert quant(d=te.TE_COLWISE, qr=None, sr=None, qc=P2, sc=P3, rows=48) == te.TE_ERR_SHAPE  # rows % 32
+    assert quant(d=te.TE_COLWISE, qr=None, sr=None, qc=P2, sc=P3, cols=36) == te.TE_ERR_SHAPE  # cols % 8
+    assert quant(sr=None) == te.TE_ERR_NULL
+    assert quant(qc=P2, sc=P3) == te.TE_ERR_NULL                 # colwise outputs given for rowwise
+    assert quant(d=te.TE_BOTH) == te.TE_ERR_NULL
+    assert quant(x=None) == te.TE_ERR_NULL
+    assert quant(x=BAD) == te.TE_ERR_ALIGN
+    assert quant(qr=BAD) == te.TE_ERR_ALIGN
+    # empty tensors succeed without touching the device
+    assert quant(rows=0) == te.TE_OK
+    assert quant(x=None, cols=0) == te.TE_OK
+
+
+def gemm(a=P, sa=P, fa=te.TE_E4M3, b=P, sb=P, fb=te.TE_E4M3, M=256, N=256, K=256, d=P2, dt=te.TE_BF16,
+         epi=te.TE_EPI_NONE, bias=None, aux=None):
+    return L.te_mxfp8_gemm(a, sa, fa, b, sb, fb, M, N, K, d, dt, epi, bias, aux, None, 0, None)
+
+
+def test_gemm_validation():
+    assert gemm(K=192) == te.TE_ERR_SHAPE       # K % 128
+    assert gemm(M=72) == te.TE_ERR_SHAPE        # M % 16
+    assert gemm(N=40) == te.TE_ERR_SHAPE        # N % 16
+    assert gemm(M=-16) == te.TE_ERR_SHAPE
+    assert gemm(fa=te.TE_E5M2, fb=te.TE_E5M2) == te.TE_ERR_DTYPE
+    assert gemm(fa=te.TE_BF16) == te.TE_ERR_DTYPE
+    assert gemm(dt=te.TE_E4M3) == te.TE_ERR_DTYPE
+    assert gemm(epi=5) == te.TE_ERR_VALUE
+    assert gemm(epi=te.TE_EPI_BIAS) == te.TE_ERR_NULL                       # bias missing
+    assert gemm(bias=P3) == te.TE_ERR_NULL                                  # bias without epilogue
+    assert gemm(epi=te.TE_EPI_BIAS_GELU_AUX, bias=P3) == te.TE_ERR_NULL     # aux missing
+    assert gemm(epi=te.TE_EPI_BIAS, bias=P3, aux=P3) == te.TE_ERR_NULL      # aux without GELU-aux
+    assert gemm(a=None) == te.TE_ERR_NULL
+    assert gemm(d=None) == te.TE_ERR_NULL
+    assert gemm(a=BAD) == te.TE_ERR_ALIGN
+    assert gemm(sa=P + 2) == te.TE_ERR_ALIGN
+    assert gemm(d=BAD) == te.TE_ERR_ALIGN
+    assert gemm(M=0) == te.TE_OK and gemm(N=0, a=None, d=None) == te.TE_OK
+
+
+def grouped(G=4, splits=P3, T=1024, a=P, sa=P, fa=te.TE_E4M3, b=P, sb=P, fb=te.TE_E4M3, N=256, K=256, d=P2,
+            dt=te.TE_BF16, epi=te.TE_EPI_NONE, bias=None, aux=None):
+    return L.te_mxfp8_grouped_gemm(G, splits, T, a, sa, fa, b, sb, fb, N, K, d, dt, epi, bias, aux, None, 0, None)
+
+
+def test_grouped_validation():
+    assert grouped(G=0) == te.TE_ERR_SHAPE
+    assert grouped(G=1025) == te.TE_ERR_SHAPE
+    assert grouped(T=-1) == te.TE_ERR_SHAPE
+    assert grouped(K=192) == te.TE_ERR_SHAPE
+    assert grouped(N=40) == te.TE_ERR_SHAPE
+    assert grouped(K=0) == te.TE_ERR_SHAPE
+    assert grouped(splits=None) == te.TE_ERR_NULL
+    assert grouped(splits=P3 + 2) == te.TE_ERR_ALIGN
+    assert grouped(fa=te.TE_E5M2, fb=te.TE_E5M2) == te.TE_ERR_DTYPE
+    assert grouped(epi=te.TE_EPI_BIAS_GELU_AUX, bias=P3) == te.TE_ERR_NULL
+    assert grouped(b=BAD) == te.TE_ERR_ALIGN
+    assert grouped(T=0) == te.TE_OK
+
+
+def test_amax_and_cast_validation():
+    ws = te.te_amax_workspace_size(1 << 20)
+    assert L.te_amax_reduce(P, -1, P2, P3, ws, None) == te.TE_ERR_SHAPE
+    assert L.te_amax_reduce(P, 1 << 20, None, P3, ws, None) == te.TE_ERR_NULL
+    assert L.te_amax_reduce(P, 1 << 20, P2, None, ws, None) == te.TE_ERR_NULL
+    assert L.te_amax_reduce(BAD, 1 << 20, P2, P3, ws, None) == te.TE_ERR_ALIGN
+    assert L.te_amax_reduce(P, 1 << 20, P2, P3, ws - 4, None) == te.TE_ERR_WORKSPACE
+    cast = L.te_fp8_cast_current_scaling
+    assert cast(P, 1024, te.TE_BF16, P2, P3, P3, P3, P3, 64, None) == te.TE_ERR_DTYPE
+    assert cast(P, 1024, te.TE_E4M3, None, P3, P3, P3, P3, 64, None) == te.TE_ERR_NULL
+    assert cast(P, 1024, te.TE_E4M3, P2, P3, None, P3, P3, 64, None) == te.TE_ERR_NULL
+    assert cast(P, 1024, te.TE_E4M3, BAD, P3, P3, P3, P3, 64, None) == te.TE_ERR_ALIGN
+    assert cast(P, 1 << 24, te.TE_E5M2, P2, P3, P3, P3, P3, 4, None) == te.TE_ERR_WORKSPACE
+
+
+def test_import_fails_loudly_without_library(tmp_path):
+    # the package refuses to import when libtemx.so is absent (no CPU fallback)
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "mxfp8_mixed_precision_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "mxfp8_mixed_precision_amd", "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import mxfp8_mixed_precision_amd"], cwd=tmp_path,
+                       capture_output=True, text=True)
+    assert r.returncode != 0 and "libtemx.so is missing" in r.stderr

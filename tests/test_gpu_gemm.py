@@ -1,0 +1,278 @@
+"""GPU parity of the MXFP8 GEMM, its epilogues and the grouped GEMM against
+the CPU oracle.
+
+* Exact-integer GEMMs (every partial sum is exact in fp32, so any summation
+  order gives the same fp32 result): bit-exact.  These pin the operand lane
+  layout, the scale-lane mapping and the format selectors.
+* Benchmark configurations: within |y - y_ref| <= 2^-8 |y_ref| +
+  c (1e-5 (S + |bias|) + H) for D and aux, where H bounds the scaled MFMA's
+  in-group product truncation (tests/mfma_model.py; c = 1.13 for outputs
+  taken through GELU), on full outputs where the oracle is fast and on
+  sampled rows x columns (first / last / tile-boundary / random) at the
+  full sizes, launched exactly as bench.py launches them.  The share of
+  outputs that also meet the stated tolerance without H is printed.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mfma_model
+import oracle
+import workloads
+from gpu_util import bf16_to_f64, dev, gemm_within, host, model_outputs
+
+pytestmark = pytest.mark.gpu
+
+
+def te():
+    import mxfp8_mixed_precision_amd as m
+    return m
+
+
+def exact_codes(rng, shape, fmt):
+    """Codes of values in {0, +-0.5, +-1, +-2, +-4}."""
+    table = {"e4m3": [0x00, 0x30, 0x38, 0x40, 0x48], "e5m2": [0x00, 0x38, 0x3C, 0x40, 0x44]}[fmt]
+    c = np.array(table, np.uint8)[rng.integers(0, 5, size=shape)]
+    return c | (rng.integers(0, 2, size=shape) * 0x80).astype(np.uint8)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (272, 304, 384), (16, 16, 256), (512, 768, 1024)])
+def test_gemm_exact_integer_bitexact(fa, fb, M, N, K):
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    qa, qb = exact_codes(rng, (M, K), fa), exact_codes(rng, (N, K), fb)
+    sa = rng.integers(125, 130, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(125, 130, size=(N, K // 32)).astype(np.uint8)
+    d, _ = te().mxfp8_gemm(dev(qa), dev(sa), fa, dev(qb), dev(sb), fb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.mx_gemm(qa, sa, oracle.format_by_name(fa), qb, sb, oracle.format_by_name(fb))
+    assert np.array_equal(host(d).astype(np.float64), ref)
+
+
+def test_gemm_k_zero_gives_epilogue_of_zero():
+    M, N = 64, 48
+    bias = workloads.normal_bf16(6, 1, (N,), 1.0)
+    empty = torch.zeros((M, 0), dtype=torch.uint8, device="cuda")
+    d, aux = te().mxfp8_gemm(empty, empty, "e4m3", empty[:N], empty[:N], "e4m3", "bias_gelu_aux", dev(bias))
+    torch.cuda.synchronize()
+    ref, ref_aux = oracle.epilogue(np.zeros((M, N)), bias, "bias_gelu_aux")
+    zero = np.zeros((M, N))
+    assert gemm_within(bf16_to_f64(host(aux)), ref_aux, zero, bias, zero, 0)[1].all()
+    assert gemm_within(bf16_to_f64(host(d)), ref, zero, bias, zero, 0, through_gelu=True)[1].all()
+
+
+def quantize_pair(spec, bits_a, bits_b):
+    """GPU-quantized operands of a GEMM spec, from device bf16 sources."""
+    m = te()
+    ta, tb = dev(bits_a), dev(bits_b)
+    if spec.a_dir == "row":
+        qa, sa, _, _ = m.mxfp8_quantize(ta, spec.fmt_a, "row")
+    else:
+        _, _, qa, sa = m.mxfp8_quantize(ta, spec.fmt_a, "col")
+    if spec.b_dir == "row":
+        qb, sb, _, _ = m.mxfp8_quantize(tb, spec.fmt_b, "row")
+    else:
+        _, _, qb, sb = m.mxfp8_quantize(tb, spec.fmt_b, "col")
+    return qa, sa, qb, sb
+
+
+def oracle_operand_rows(bits, direction, fmt, rows):
+    """Oracle MXFP8 rows (of the K-major operand) selected by `rows`."""
+    f = oracle.format_by_name(fmt)
+    if direction == "row":
+        return oracle.quantize_rowwise(np.ascontiguousarray(bits[rows]), f)
+    return oracle.quantize_colwise(np.ascontiguousarray(bits[:, rows]), f)
+
+
+def sample(n, tile=256, k=40, seed=0):
+    rng = np.random.default_rng(seed)
+    s = {0, n - 1, n // 2}
+    for t in range(tile, n, tile):
+        s.update({t - 1, t})
+    s = sorted(s)
+    if len(s) > k:
+        s = sorted(set(np.array(s)[np.linspace(0, len(s) - 1, k).astype(int)].tolist()) | {0, n - 1})
+    extra = rng.choice(n, min(k, n), replace=False)
+    return np.array(sorted(set(s) | set(extra.tolist())))
+
+
+def check_against_model(got_d, got_aux, qa, sa, Fa, qb, sb, Fb, bias, epi):
+    """Bit-exact check of bf16 D (none / bias) and aux against the MFMA model;
+    GELU outputs to bf16 precision."""
+    acc = mfma_model.hw_gemm_fp32(qa, sa, Fa, qb, sb, Fb)
+    want_d, want_aux = model_outputs(acc, bias, epi)
+    if epi == "bias_gelu_aux":
+        assert np.array_equal(got_aux, want_aux), "aux differs from the MFMA model"
+        g = bf16_to_f64(got_d)
+        assert np.all(np.abs(g - want_d) <= 2.0 ** -8 * np.abs(want_d) + 1e-30), "GELU output off"
+    else:
+        assert np.array_equal(got_d, want_d), "D differs from the MFMA model"
+
+
+def check_gemm_spec(spec, full: bool, model_rows: int = 32):
+    bits_a, bits_b = spec.a_src.make(), spec.b_src.make()
+    bias = spec.bias.make() if spec.bias is not None else None
+    qa, sa, qb, sb = quantize_pair(spec, bits_a, bits_b)
+    d, aux = te().mxfp8_gemm(qa, sa, spec.fmt_a, qb, sb, spec.fmt_b, spec.epilogue,
+                             None if bias is None else dev(bias))
+    torch.cuda.synchronize()
+    rows = np.arange(spec.M) if full else sample(spec.M, seed=1)
+    cols = np.arange(spec.N) if full else sample(spec.N, seed=2)
+    oqa, osa = oracle_operand_rows(bits_a, spec.a_dir, spec.fmt_a, rows)
+    oqb, osb = oracle_operand_rows(bits_b, spec.b_dir, spec.fmt_b, cols)
+    # the operands the GPU consumed are the oracle's, bit for bit
+    assert np.array_equal(host(qa[rows]), oqa) and np.array_equal(host(sa[rows]), osa)
+    assert np.array_equal(host(qb[cols]), oqb) and np.array_equal(host(sb[cols]), osb)
+    Fa, Fb = oracle.format_by_name(spec.fmt_a), oracle.format_by_name(spec.fmt_b)
+    ref_d, ref_aux, s = oracle.mx_gemm(oqa, osa, Fa, oqb, osb, Fb,
+                                       None if bias is None else bias[cols], spec.epilogue)
+    h = mfma_model.truncation_bound(oqa, osa, Fa, oqb, osb, Fb)
+    b = None if bias is None else bias[cols]
+    got_bits = host(d[rows][:, cols])
+    got_aux_bits = None if aux is None else host(aux[rows][:, cols])
+    mr = np.linspace(0, len(rows) - 1, min(model_rows, len(rows))).astype(int)
+    check_against_model(got_bits[mr], None if got_aux_bits is None else got_aux_bits[mr], oqa[mr], osa[mr], Fa,
+                        oqb, osb, Fb, b, spec.epilogue)
+    got = bf16_to_f64(got_bits)
+    ok, stated = gemm_within(got, ref_d, s, b, h, spec.K, through_gelu=spec.epilogue == "bias_gelu_aux")
+    print(f"{spec.name}: D {ok.mean():.6f} within bound, {stated.mean():.6f} within the stated tolerance alone")
+    assert ok.all(), f"{(~ok).sum()} of {ok.size} D outside the bound"
+    if ref_aux is not None:
+        got_aux = bf16_to_f64(got_aux_bits)
+        ok, stated = gemm_within(got_aux, ref_aux, s, b, h, spec.K)
+        print(f"{spec.name}: aux {ok.mean():.6f} within bound, {stated.mean():.6f} within the stated tolerance alone")
+        assert ok.all(), f"{(~ok).sum()} of {ok.size} aux outside the bound"
+
+
+def test_tiny_256_full():
+    check_gemm_spec(workloads.tiny().gemms[0], full=True)
+
+
+@pytest.mark.parametrize("name", ["qkv", "fc1", "fc2"])
+def test_decoder_forward_full(name):
+    spec = [g for g in workloads.decoder_forward().gemms if g.name == name][0]
+    check_gemm_spec(spec, full=True)
+
+
+def test_square_8192_sampled():
+    check_gemm_spec(workloads.large_square().gemms[0], full=False)
+
+
+@pytest.mark.parametrize("name", ["dgrad", "wgrad"])
+def test_hybrid_backward_sampled(name):
+    spec = [g for g in workloads.hybrid_backward().gemms if g.name == name][0]
+    check_gemm_spec(spec, full=False)
+
+
+@pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640)])
+def test_ragged_shapes_and_epilogues(epi, M, N, K):
+    spec = workloads.GemmSpec("ragged", M, N, K, "e4m3", "e4m3", epi,
+                              workloads.TensorSpec(50, M, (M, K), 1.0, 0.01),
+                              workloads.TensorSpec(51, N, (N, K), 0.05),
+                              bias=None if epi == "none" else workloads.TensorSpec(52, N, (N,), 0.5))
+    check_gemm_spec(spec, full=True)
+
+
+def test_fp32_output_and_canaries():
+    M, N, K = 272, 304, 512
+    a = workloads.normal_bf16(60, 0, (M, K), 1.0)
+    b = workloads.normal_bf16(60, 1, (N, K), 0.1)
+    qa, sa, _, _ = te().mxfp8_quantize(dev(a), "e4m3", "row")
+    qb, sb, _, _ = te().mxfp8_quantize(dev(b), "e4m3", "row")
+    # D carved out of a larger buffer filled with a canary pattern
+    buf = torch.full(((M + 64) * N,), 12345.0, dtype=torch.float32, device="cuda")
+    d = buf[32 * N:(32 + M) * N].view(M, N)
+    te().te_mxfp8_gemm(qa, sa, "e4m3", qb, sb, "e4m3", d)
+    torch.cuda.synchronize()
+    hb = host(buf)
+    assert np.all(hb[:32 * N] == 12345.0) and np.all(hb[(32 + M) * N:] == 12345.0)
+    oqa, osa = oracle.quantize_rowwise(a, oracle.E4M3)
+    oqb, osb = oracle.quantize_rowwise(b, oracle.E4M3)
+    # fp32 output: bit-exact against the instruction-sequence model
+    assert np.array_equal(host(d), mfma_model.hw_gemm_fp32(oqa, osa, oracle.E4M3, oqb, osb, oracle.E4M3))
+
+
+def test_gemm_is_deterministic():
+    spec = [g for g in workloads.decoder_forward().gemms if g.name == "fc1"][0]
+    qa, sa, qb, sb = quantize_pair(spec, spec.a_src.make(), spec.b_src.make())
+    bias = dev(spec.bias.make())
+    d1, x1 = te().mxfp8_gemm(qa, sa, "e4m3", qb, sb, "e4m3", "bias_gelu_aux", bias)
+    d2, x2 = te().mxfp8_gemm(qa, sa, "e4m3", qb, sb, "e4m3", "bias_gelu_aux", bias)
+    torch.cuda.synchronize()
+    assert torch.equal(d1, d2) and torch.equal(x1, x2)
+
+
+# ------------------------------------------------------------------ grouped
+
+def check_grouped(counts, N, K, epi, seed, full_cols=False, rows_per_expert=None):
+    G = len(counts)
+    T = int(sum(counts))
+    a = workloads.normal_bf16(seed, 1, (T, K), 1.0)
+    b = workloads.normal_bf16(seed, 2, (G * N, K), 0.02)
+    bias = workloads.normal_bf16(seed, 3, (G, N), 0.02) if epi != "none" else None
+    m = te()
+    qa, sa, _, _ = m.mxfp8_quantize(dev(a), "e4m3", "row")
+    qb, sb, _, _ = m.mxfp8_quantize(dev(b), "e4m3", "row")
+    splits = torch.tensor(np.asarray(counts, np.int32), device="cuda")
+    # D and aux sit inside canary-filled buffers
+    pad = 64 * N
+    dbuf = torch.full((T * N + 2 * pad,), -7.0, dtype=torch.bfloat16, device="cuda")
+    d = dbuf[pad:pad + T * N].view(T, N)
+    aux = None
+    if epi == "bias_gelu_aux":
+        abuf = torch.full((T * N + 2 * pad,), -7.0, dtype=torch.bfloat16, device="cuda")
+        aux = abuf[pad:pad + T * N].view(T, N)
+    m.te_mxfp8_grouped_gemm(splits, qa, sa, "e4m3", qb, sb, "e4m3", N, d, epi,
+                            None if bias is None else dev(bias), aux)
+    torch.cuda.synchronize()
+    canary = np.uint16(torch.tensor(-7.0, dtype=torch.bfloat16).view(torch.int16).item() & 0xFFFF)
+    for buf in [dbuf] + ([abuf] if aux is not None else []):
+        hb = host(buf)
+        assert np.all(hb[:pad] == canary) and np.all(hb[pad + T * N:] == canary)
+    rng = np.random.default_rng(seed)
+    cols = np.arange(N) if full_cols else sample(N, seed=seed + 1)
+    off = 0
+    for e, me in enumerate(counts):
+        if me == 0:
+            continue
+        if rows_per_expert is None or me <= rows_per_expert:
+            rows = np.arange(off, off + me)
+        else:
+            pick = {0, me - 1, min(255, me - 1), min(256, me - 1)} | set(rng.choice(me, rows_per_expert, replace=False).tolist())
+            rows = off + np.array(sorted(pick))
+        oqa, osa = oracle.quantize_rowwise(np.ascontiguousarray(a[rows]), oracle.E4M3)
+        oqb, osb = oracle.quantize_rowwise(np.ascontiguousarray(b[e * N + cols]), oracle.E4M3)
+        be = None if bias is None else bias[e][cols]
+        ref_d, ref_aux, s = oracle.mx_gemm(oqa, osa, oracle.E4M3, oqb, osb, oracle.E4M3, be, epi)
+        h = mfma_model.truncation_bound(oqa, osa, oracle.E4M3, oqb, osb, oracle.E4M3)
+        got_bits = host(d[rows][:, cols])
+        got_aux_bits = None if aux is None else host(aux[rows][:, cols])
+        check_against_model(got_bits, got_aux_bits, oqa, osa, oracle.E4M3, oqb, osb, oracle.E4M3, be, epi)
+        ok, _ = gemm_within(bf16_to_f64(got_bits), ref_d, s, be, h, K, through_gelu=epi == "bias_gelu_aux")
+        assert ok.all(), f"expert {e}: {(~ok).sum()} of {ok.size} outside the bound"
+        if ref_aux is not None:
+            ok, _ = gemm_within(bf16_to_f64(got_aux_bits), ref_aux, s, be, h, K)
+            assert ok.all(), f"expert {e} aux: {(~ok).sum()} outside the bound"
+        off += me
+
+
+@pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
+def test_grouped_small_ragged(epi):
+    check_grouped([5, 0, 300, 1, 256, 17], N=272, K=256, epi=epi, seed=31, full_cols=True)
+
+
+def test_grouped_single_group_matches_dense_rows():
+    check_grouped([700], N=512, K=384, epi="bias", seed=32, full_cols=True)
+
+
+def test_grouped_all_empty_but_one():
+    check_grouped([0, 0, 0, 33, 0], N=64, K=128, epi="bias_gelu_aux", seed=33, full_cols=True)
+
+
+def test_moe_grouped_full_size_sampled():
+    w = workloads.moe_grouped().grouped[0]
+    counts = workloads.moe_counts()
+    assert counts.sum() == w.total_m
+    check_grouped(counts.tolist(), N=w.N, K=w.K, epi=w.epilogue, seed=5, rows_per_expert=12)

@@ -1,0 +1,159 @@
+"""GPU parity of MXFP8 quantization, amax and the current-scaling cast against
+the CPU oracle: bit-exact codes, scales, amax, scale and scale_inv."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import dev, finite_bf16_patterns, host
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["e4m3", "e5m2"]
+
+
+def te():
+    import mxfp8_mixed_precision_amd as m
+    return m
+
+
+def check_quantize(bits: np.ndarray, fmt: str, direction: str = "both"):
+    f = oracle.format_by_name(fmt)
+    x = dev(bits)
+    qr, sr, qc, sc = te().mxfp8_quantize(x, fmt, direction)
+    torch.cuda.synchronize()
+    if qr is not None:
+        oq, os_ = oracle.quantize_rowwise(bits, f)
+        assert np.array_equal(host(sr), os_), "rowwise scales differ"
+        assert np.array_equal(host(qr), oq), "rowwise codes differ"
+    if qc is not None:
+        oq, os_ = oracle.quantize_colwise(bits, f)
+        assert np.array_equal(host(sc), os_), "colwise scales differ"
+        assert np.array_equal(host(qc), oq), "colwise codes differ"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_every_finite_bf16_random_blocks(fmt):
+    rng = np.random.default_rng(100)
+    p = rng.permutation(finite_bf16_patterns())
+    bits = np.zeros(256 * 256, np.uint16)
+    bits[:p.size] = p
+    check_quantize(bits.reshape(256, 256), fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_every_finite_bf16_magnitude_sorted_blocks(fmt):
+    # neighbours in magnitude share a block, so every element is encoded with
+    # a scale close to its own exponent (normals, subnormals, ties, saturation)
+    p = finite_bf16_patterns()
+    order = np.argsort(p & 0x7FFF, kind="stable")
+    rng = np.random.default_rng(101)
+    bits = np.zeros(256 * 256, np.uint16)
+    bits[:p.size] = p[order]
+    blocks = bits.reshape(-1, 32)
+    blocks = blocks[:, rng.permutation(32)]  # position of the block maximum varies
+    check_quantize(blocks.reshape(256, 256), fmt)
+    check_quantize(np.ascontiguousarray(blocks.reshape(256, 256).T), fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(1, 32), (33, 64), (96, 160), (160, 72), (32, 8), (4160, 200)])
+def test_quantize_ragged_shapes(fmt, shape):
+    rows, cols = shape
+    bits = workloads.normal_bf16(77, rows * 1000 + cols, shape, 3.0, 0.05)
+    if rows % 32 == 0 and cols % 32 == 0:
+        check_quantize(bits, fmt, "both")
+    if cols % 32 == 0:
+        check_quantize(bits, fmt, "row")
+    if rows % 32 == 0 and cols % 8 == 0:
+        check_quantize(bits, fmt, "col")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_special_blocks(fmt):
+    # zero blocks, negative zeros, subnormal-only blocks, huge blocks, single spikes
+    rows = []
+    rows.append(np.zeros(64, np.uint16))
+    rows.append(np.full(64, 0x8000, np.uint16))
+    rows.append(np.arange(1, 65, dtype=np.uint16))            # bf16 subnormals
+    rows.append((np.arange(64, dtype=np.uint16) | 0x7F00))    # near the top of the range
+    spike = np.full(64, 0x3F80, np.uint16)
+    spike[5] = 0x4700  # 32768
+    rows.append(spike)
+    bits = np.stack(rows * 8)[:32]
+    check_quantize(bits, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_decoder_activation(fmt):
+    # 4096 tokens x 1024 hidden, N(0,1) with 1% outlier columns x20
+    bits = workloads.normal_bf16(2, 0, (4096, 1024), 1.0, 0.01)
+    check_quantize(bits, fmt)
+
+
+def sampled_rows(n, k=48, seed=0):
+    rng = np.random.default_rng(seed)
+    s = set([0, 1, n - 1, n // 2]) | set(rng.choice(n, k, replace=False).tolist())
+    return np.array(sorted(s))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_8192_square_sampled(fmt):
+    # full-size standalone quantize of an 8192 x 8192 operand (both directions),
+    # checked on sampled output rows
+    spec = workloads.large_square().quantize[0][0]
+    bits = spec.make()
+    f = oracle.format_by_name(fmt)
+    x = dev(bits)
+    qr, sr, qc, sc = te().mxfp8_quantize(x, fmt, "both")
+    torch.cuda.synchronize()
+    rows = sampled_rows(8192, seed=1)
+    oq, os_ = oracle.quantize_rowwise(bits[rows], f)
+    assert np.array_equal(host(qr[rows]), oq) and np.array_equal(host(sr[rows]), os_)
+    cols = sampled_rows(8192, seed=2)
+    oq, os_ = oracle.quantize_colwise(np.ascontiguousarray(bits[:, cols]), f)
+    assert np.array_equal(host(qc[cols]), oq) and np.array_equal(host(sc[cols]), os_)
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 1000, 4096 * 8 + 3, 1 << 20, 4096 * 4096])
+def test_amax(n):
+    bits = workloads.normal_bf16(88, n, (n,), 1.5, 0.0) if n else np.zeros(0, np.uint16)
+    if n > 10:
+        bits[n // 3] = 0xC3A0  # -320.0 planted
+    x = dev(bits) if n else torch.zeros(0, dtype=torch.int16, device="cuda")
+    a = te().amax(x)
+    torch.cuda.synchronize()
+    assert host(a)[0] == oracle.amax(bits)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n", [1, 13, 4096 + 5, 4096 * 4096])
+def test_current_scaling_cast(fmt, n):
+    bits = workloads.normal_bf16(4, 2, (n,), 1.0, 0.0)
+    f = oracle.format_by_name(fmt)
+    q, a, s, si = te().fp8_cast_current_scaling(dev(bits), fmt)
+    torch.cuda.synchronize()
+    oq, oa, os_, osi = oracle.cast_current_scaling(bits, f)
+    assert host(a)[0] == oa and host(s)[0] == os_ and host(si)[0] == osi
+    assert np.array_equal(host(q), oq)
+
+
+def test_current_scaling_zero_and_subnormal_tensors():
+    for bits in (np.zeros(64, np.uint16), np.array([0x8000] * 63 + [0x0001], np.uint16)):
+        q, a, s, si = te().fp8_cast_current_scaling(dev(bits), "e4m3")
+        torch.cuda.synchronize()
+        oq, oa, os_, osi = oracle.cast_current_scaling(bits, oracle.E4M3)
+        assert host(a)[0] == oa and host(s)[0] == os_ and host(si)[0] == osi
+        assert np.array_equal(host(q), oq)
+
+
+def test_quantize_is_deterministic():
+    bits = workloads.normal_bf16(3, 0, (1024, 1024), 1.0, 0.01)
+    x = dev(bits)
+    r1 = te().mxfp8_quantize(x, "e4m3", "both")
+    r2 = te().mxfp8_quantize(x, "e4m3", "both")
+    torch.cuda.synchronize()
+    for u, v in zip(r1, r2):
+        assert torch.equal(u, v)
