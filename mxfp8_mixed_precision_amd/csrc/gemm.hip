@@ -19,15 +19,15 @@
 //   epilogue stores 8 bytes (bf16) per lane straight from registers.
 // * 256 x 256 workgroup tile, 4 waves in 2 x 2, 128 x 128 per wave (8 x 8
 //   MFMA tiles = 256 fp32 accumulators per lane), K step 128.
-// * A, B and their scale tiles are copied global -> LDS with the gfx950
-//   direct-to-LDS loads (global_load_lds_dwordx4 / _dword), double-buffered
-//   (2 x 66 KB).  16-byte chunks of a 128-byte LDS row are XOR-swizzled so
-//   the ds_read_b128 of 16 consecutive rows hit distinct banks.
+// * A, B and their scale tiles are copied global -> LDS with direct-to-LDS
+//   buffer loads (buffer_load_dwordx4 / _dword ... lds), double-buffered
+//   (2 x 66 KB).
 // * Workgroup -> tile mapping is XCD-aware: workgroups are dealt round-robin
 //   to the 8 XCDs, so each XCD is given a contiguous run of tiles (grouped in
 //   bands of 4 row-tiles) and its L2 sees the reuse.
-// * Ragged M / N tails: loads clamp the row index (valid memory, unused
-//   results), stores are masked.  The workspace is 0 bytes.
+// * Ragged M / N tails: each tile's copies go through buffer resources that
+//   cover only its valid rows, so rows past the end read as zeros; stores are
+//   masked.  The workspace is 0 bytes.
 #include "temx_device.h"
 
 namespace temx {
@@ -41,44 +41,120 @@ constexpr int kAData = BM * BK;
 constexpr int kBData = BN * BK;
 constexpr int kAScale = BM * 4;
 constexpr int kBScale = BN * 4;
-constexpr int kStage = kAData + kBData + kAScale + kBScale;
-constexpr int kLds = 2 * kStage;
 constexpr int kGroupM = 4;      // row-tile band of the raster order
 constexpr int kMaxGroups = 1024;
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// LDS data tile of one operand and stage: two K-halves (K bytes 0-63 and
+// 64-127 of the step), each [256 rows][64 bytes] = 16 KB.  In a half, the
+// four 16-byte chunks of row r are permuted by chunk ^ swz(r), so that the
+// ds_read_b128 of 8 (or 16) consecutive rows at one logical chunk hit
+// distinct banks for 128-byte (or 256-byte) bank rows.
+constexpr int kHalf = BM * 64;
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 
 template <int F> struct MfmaFmt;  // cbsz / blgp operand format codes
 template <> struct MfmaFmt<TE_E4M3> { static constexpr int v = 0; };
 template <> struct MfmaFmt<TE_E5M2> { static constexpr int v = 1; };
 
+// An operand tile as two buffer resources: rows [row0, row0 + rows) of the
+// data [*, K] and of the scales [*, K/32].  Reads past the valid rows (ragged
+// M / N / expert tails) return zeros from the buffer range check.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 struct Operand {
-  const uint8_t* data;   // [rows, K]
-  const uint8_t* scale;  // [rows, K/32]
-  int64_t row0;          // first row of the tile
-  int64_t last;          // last valid row (loads clamp to it)
+  i32x4 data;
+  i32x4 scale;
 };
 
-// Issue the direct-to-LDS copies of one 256 x 128 data tile and its 256 x 4
-// scale tile.  Wave w copies 8 of the 32 one-kilobyte slices (8 rows each)
-// and one of the four 256-byte scale slices.
-__device__ __forceinline__ void load_operand(uint8_t* lds_data, uint8_t* lds_scale, const Operand& op,
-                                             int64_t K, int kt, int wave, int lane) {
-  const int64_t kq = K / 32;
+constexpr int kRsrcWord3 = 0x00020000;  // raw byte buffer, 32-bit data format (gfx9 descriptor word 3)
+
+// The descriptor must live in SGPRs; its inputs are uniform over the wave
+// (tile coordinates), which readfirstlane states for the compiler.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), kRsrcWord3};
+}
+
+__device__ __forceinline__ Operand make_operand(const uint8_t* data, const uint8_t* scale, int64_t row0,
+                                                int64_t rows, int64_t K) {
+  rows = rows < 0 ? 0 : (rows > BM ? BM : rows);
+  return Operand{make_rsrc(data + row0 * K, rows * K), make_rsrc(scale + row0 * (K / 32), rows * (K / 32))};
+}
+
+// Direct-to-LDS buffer loads (buffer_load_dword{,x4} ... lds): lane l's
+// bytes land at LDS address m0 + size * l.  They are issued from inline asm
+// so that the compiler, which cannot tell the stage being filled from the
+// stage being read, does not wait for them before every LDS read; the K loop
+// orders them itself (s_waitcnt vmcnt(0) + barrier before a stage is read).
+// m0 is saved and restored around the copy (the LDS base is read at issue).
+__device__ __forceinline__ void lds_dma16(const i32x4& rsrc, uint32_t lds_addr, int voff, int soff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_dma4(const i32x4& rsrc, uint32_t lds_addr, int voff, int soff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+// LDS layout of one pipeline stage: A data, B data (two K-halves each, see
+// kHalf), A scales [256][4], B scales [256][4].  Two stages.
+constexpr int kOffBData = kAData;
+constexpr int kOffAScale = kAData + kBData;
+constexpr int kOffBScale = kOffAScale + kAScale;
+constexpr int kStage = kOffBScale + kBScale;
+constexpr int kLds = 2 * kStage;
+
+// Per-lane byte offsets of the tile copies.  A copy instruction fills one
+// 1-KB slice of a half: rows 16 b .. 16 b + 15, lane l landing at LDS byte
+// 16 l, i.e. row 16 b + l/4, physical chunk l % 4, which holds logical chunk
+// (l % 4) ^ swz(l/4) (swz only sees row bits 1-3).  Wave w copies the slices
+// b = w + 4 (i % 4) of half i / 4, i = 0..7, so one per-lane offset plus the
+// uniform 64 (i % 4) K + 64 (i / 4) + 128 kt serves every copy.  The scale
+// slice of wave w is rows 64 w .. 64 w + 63, four bytes (one K step) each.
+struct CopyOffsets {
+  int data;
+  int scale;
+};
+
+__device__ __forceinline__ CopyOffsets copy_offsets(int64_t K, int wave, int lane) {
+  const int sub = lane >> 2;
+  const int chunk = (lane & 3) ^ swz(sub);
+  CopyOffsets o;
+  o.data = (int)((16 * wave + sub) * K) + chunk * 16;
+  o.scale = (int)((64 * wave + lane) * (K / 32));
+  return o;
+}
+
+__device__ __forceinline__ void load_operand(uint32_t lds_data, uint32_t lds_scale, const Operand& op,
+                                             const CopyOffsets& off, int64_t K, int kt, int wave) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int q = wave + 4 * i;
-    const int row = 8 * q + (lane >> 3);
-    const int chunk = (lane & 7) ^ swz(row);
-    int64_t gr = op.row0 + row;
-    gr = gr < op.last ? gr : op.last;
-    const uint8_t* src = op.data + gr * K + (int64_t)kt * BK + chunk * 16;
-    __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)(lds_data + q * 1024), 16, 0, 0);
+    const int half = i >> 2, b = wave + 4 * (i & 3);
+    lds_dma16(op.data, lds_data + half * kHalf + b * 1024, off.data, (int)(64 * (i & 3) * K) + 64 * half + kt * BK);
   }
-  int64_t gr = op.row0 + 64 * wave + lane;
-  gr = gr < op.last ? gr : op.last;
-  const uint8_t* ssrc = op.scale + gr * kq + (int64_t)kt * 4;
-  __builtin_amdgcn_global_load_lds((global_void_t*)ssrc, (lds_void_t*)(lds_scale + wave * 256), 4, 0, 0);
+  lds_dma4(op.scale, lds_scale + wave * 256, off.scale, kt * 4);
+}
+
+__device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, const Operand& B,
+                                           const CopyOffsets& off, int64_t K, int kt, int wave) {
+  load_operand(stage, stage + kOffAScale, A, off, K, kt, wave);
+  load_operand(stage + kOffBData, stage + kOffBScale, B, off, K, kt, wave);
 }
 
 struct Frag {
@@ -86,31 +162,49 @@ struct Frag {
   int s;
 };
 
-// Two 16-byte chunks (K 16g.. and 64+16g..) of LDS row `row`, and the E8M0
-// byte of block g of that row in the low byte of s.
-__device__ __forceinline__ Frag read_frag(const uint8_t* data, const uint8_t* scale, int row, int g, int sw) {
-  const uint8_t* p = data + row * BK;
-  const uint4 lo = *reinterpret_cast<const uint4*>(p + ((g ^ sw) << 4));
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + (((g + 4) ^ sw) << 4));
+// Per-lane LDS read offsets of a wave, computed once.  Fragment j of a
+// wave's 128 rows is 16 j rows further (1 KB of data, 64 B of scales), which
+// the reads take as immediate offsets.  The empty asm statement keeps each
+// offset a single opaque VGPR so that the compiler does not re-associate it
+// into per-fragment address registers.
+struct ReadOffsets {
+  int a_data, b_data, a_scale, b_scale, shift;
+};
+
+__device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  const int lane_off = r * 64 + ((g ^ swz(r)) << 4);
+  ReadOffsets o;
+  o.a_data = wm * WT * 64 + lane_off;
+  o.b_data = kOffBData + wn * WT * 64 + lane_off;
+  o.a_scale = kOffAScale + (wm * WT + r) * 4;
+  o.b_scale = kOffBScale + (wn * WT + r) * 4;
+  o.shift = 8 * g;
+  asm volatile("" : "+v"(o.a_data), "+v"(o.b_data), "+v"(o.a_scale), "+v"(o.b_scale), "+v"(o.shift));
+  return o;
+}
+
+// Fragment j: two 16-byte chunks (K 16g.. of each half of the step) of row
+// 16 j + r of the wave's rows, and the E8M0 byte of block g of that row in the
+// low byte of s.
+__device__ __forceinline__ Frag read_frag(const uint8_t* stage, int data_off, int scale_off, int shift, int j) {
+  const uint8_t* p = stage + data_off + j * 1024;
+  const uint4 lo = *reinterpret_cast<const uint4*>(p);
+  const uint4 hi = *reinterpret_cast<const uint4*>(p + kHalf);
   Frag f;
   f.v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  f.s = (int)(*reinterpret_cast<const uint32_t*>(scale + row * 4) >> (8 * g));
+  f.s = (int)(*reinterpret_cast<const uint32_t*>(stage + scale_off + j * 64) >> shift);
   return f;
 }
 
 template <int FA, int FB>
-__device__ __forceinline__ void compute_stage(const uint8_t* stage, v4f (&acc)[FR][FR], int wm, int wn, int lane) {
-  const uint8_t* a_data = stage;
-  const uint8_t* b_data = stage + kAData;
-  const uint8_t* a_scale = stage + kAData + kBData;
-  const uint8_t* b_scale = a_scale + kAScale;
-  const int g = lane >> 4, r = lane & 15, sw = swz(r);
+__device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[FR][FR], const ReadOffsets& ro) {
   Frag bop[FR];
 #pragma unroll
-  for (int j = 0; j < FR; ++j) bop[j] = read_frag(a_data, a_scale, wm * WT + 16 * j + r, g, sw);
+  for (int j = 0; j < FR; ++j) bop[j] = read_frag(stage, ro.a_data, ro.a_scale, ro.shift, j);
 #pragma unroll
   for (int i = 0; i < FR; ++i) {
-    const Frag aop = read_frag(b_data, b_scale, wn * WT + 16 * i + r, g, sw);
+    const Frag aop = read_frag(stage, ro.b_data, ro.b_scale, ro.shift, i);
 #pragma unroll
     for (int j = 0; j < FR; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop.v, bop[j].v, acc[i][j], MfmaFmt<FB>::v,
@@ -118,6 +212,10 @@ __device__ __forceinline__ void compute_stage(const uint8_t* stage, v4f (&acc)[F
   }
 }
 
+// Double-buffered K loop: the copies of step kt+1 are in flight while step
+// kt computes; each stage is read only after s_waitcnt vmcnt(0) and a barrier
+// (all waves' copies landed), and refilled only after the next barrier (all
+// waves finished reading it).
 template <int FA, int FB>
 __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[FR][FR], const Operand& A, const Operand& B,
                                          int64_t K, int wave, int lane) {
@@ -128,17 +226,15 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[FR][FR], const
     for (int j = 0; j < FR; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const int kt_n = (int)(K / BK);
   if (kt_n == 0) return;
-  load_operand(lds, lds + kAData + kBData, A, K, 0, wave, lane);
-  load_operand(lds + kAData, lds + kAData + kBData + kAScale, B, K, 0, wave, lane);
+  const CopyOffsets off = copy_offsets(K, wave, lane);
+  const ReadOffsets ro = read_offsets(wm, wn, lane);
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  load_stage(lds_addr, A, B, off, K, 0, wave);
   for (int kt = 0; kt < kt_n; ++kt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < kt_n) {
-      uint8_t* nx = lds + ((kt + 1) & 1) * kStage;
-      load_operand(nx, nx + kAData + kBData, A, K, kt + 1, wave, lane);
-      load_operand(nx + kAData, nx + kAData + kBData + kAScale, B, K, kt + 1, wave, lane);
-    }
-    compute_stage<FA, FB>(lds + (kt & 1) * kStage, acc, wm, wn, lane);
+    if (kt + 1 < kt_n) load_stage(lds_addr + ((kt + 1) & 1) * kStage, A, B, off, K, kt + 1, wave);
+    compute<FA, FB>(lds + (kt & 1) * kStage, acc, ro);
   }
 }
 
@@ -165,7 +261,13 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[FR][FR], void* d, uint
     for (int j = 0; j < FR; ++j) {
       const int64_t m = m0 + wm * WT + 16 * j + r;
       if (m >= m_end) continue;
-      float v0 = acc[i][j][0] + b0, v1 = acc[i][j][1] + b1, v2 = acc[i][j][2] + b2, v3 = acc[i][j][3] + b3;
+      float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
+      if constexpr (EPI != TE_EPI_NONE) {
+        v0 += b0;
+        v1 += b1;
+        v2 += b2;
+        v3 += b3;
+      }
       if constexpr (EPI == TE_EPI_BIAS_GELU_AUX) {
         *reinterpret_cast<uint2*>(aux + m * N + n) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
         v0 = gelu_tanh(v0);
@@ -217,8 +319,8 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(GemmParams p) {
   const int tm = first_tm + in_band % band_rows;
   const int tn = in_band / band_rows;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  Operand A{p.a, p.a_scale, m0, p.M - 1};
-  Operand B{p.b, p.b_scale, n0, p.N - 1};
+  const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K);
+  const Operand B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K);
   v4f acc[FR][FR];
   mainloop<FA, FB>(lds, acc, A, B, p.K, wave, lane);
   epilogue<EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
@@ -268,8 +370,9 @@ __global__ __launch_bounds__(kThreads) void mx_grouped_gemm_kernel(GemmParams p)
     const int64_t m0 = row_off[e] + (int64_t)(rt - tile_prefix[e]) * BM;
     const int64_t m_end = row_off[e + 1];
     const int64_t n0 = (int64_t)tn * BN;
-    Operand A{p.a, p.a_scale, m0, m_end - 1};
-    Operand B{p.b + (int64_t)e * p.N * p.K, p.b_scale + (int64_t)e * p.N * (p.K / 32), n0, p.N - 1};
+    const Operand A = make_operand(p.a, p.a_scale, m0, m_end - m0, p.K);
+    const Operand B = make_operand(p.b + (int64_t)e * p.N * p.K, p.b_scale + (int64_t)e * p.N * (p.K / 32), n0,
+                                   p.N - n0, p.K);
     v4f acc[FR][FR];
     __syncthreads();  // the previous tile's last reads of stage 0/1 are done
     mainloop<FA, FB>(lds, acc, A, B, p.K, wave, lane);

@@ -36,6 +36,26 @@ GELU_SLOPE = 1.13  # max |d gelu_tanh / dx| (about 1.129 near x = 1.5)
 
 
 def gemm_within(got, ref, s, bias_bits, h, k, through_gelu=False):
+    """See gemm_check; h is the full [M, N] truncation bound."""
+    return _within(got, ref, s, bias_bits, h, k, through_gelu)
+
+
+def gemm_check(got, ref, s, bias_bits, k, h_pairs, through_gelu=False):
+    """gemm_within, computing the truncation bound only for the outputs that
+    miss the stated tolerance (h_pairs(rows, cols) -> bounds)."""
+    import oracle
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    stated = np.abs(got - ref) <= oracle.tolerance_bound(ref, s, bias_bits)
+    h = np.zeros(got.shape)
+    bad_r, bad_c = np.nonzero(~stated)
+    if bad_r.size:
+        h[bad_r, bad_c] = h_pairs(bad_r, bad_c)
+    ok, _ = _within(got, ref, s, bias_bits, h, k, through_gelu)
+    return ok, stated
+
+
+def _within(got, ref, s, bias_bits, h, k, through_gelu=False):
     """Acceptance of GEMM outputs against the float64 oracle.
 
     |y - y_ref| <= 2^-8 |y_ref| + c (1e-5 (S + |bias|) + H + (K/16) 2^-24 S),

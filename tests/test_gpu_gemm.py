@@ -20,7 +20,7 @@ import torch
 import mfma_model
 import oracle
 import workloads
-from gpu_util import bf16_to_f64, dev, gemm_within, host, model_outputs
+from gpu_util import bf16_to_f64, dev, gemm_check, gemm_within, host, model_outputs
 
 pytestmark = pytest.mark.gpu
 
@@ -127,7 +127,8 @@ def check_gemm_spec(spec, full: bool, model_rows: int = 32):
     Fa, Fb = oracle.format_by_name(spec.fmt_a), oracle.format_by_name(spec.fmt_b)
     ref_d, ref_aux, s = oracle.mx_gemm(oqa, osa, Fa, oqb, osb, Fb,
                                        None if bias is None else bias[cols], spec.epilogue)
-    h = mfma_model.truncation_bound(oqa, osa, Fa, oqb, osb, Fb)
+    def h_pairs(ri, ci):
+        return mfma_model.truncation_bound_pairs(oqa, osa, Fa, oqb, osb, Fb, ri, ci)
     b = None if bias is None else bias[cols]
     got_bits = host(d[rows][:, cols])
     got_aux_bits = None if aux is None else host(aux[rows][:, cols])
@@ -135,12 +136,12 @@ def check_gemm_spec(spec, full: bool, model_rows: int = 32):
     check_against_model(got_bits[mr], None if got_aux_bits is None else got_aux_bits[mr], oqa[mr], osa[mr], Fa,
                         oqb, osb, Fb, b, spec.epilogue)
     got = bf16_to_f64(got_bits)
-    ok, stated = gemm_within(got, ref_d, s, b, h, spec.K, through_gelu=spec.epilogue == "bias_gelu_aux")
+    ok, stated = gemm_check(got, ref_d, s, b, spec.K, h_pairs, through_gelu=spec.epilogue == "bias_gelu_aux")
     print(f"{spec.name}: D {ok.mean():.6f} within bound, {stated.mean():.6f} within the stated tolerance alone")
     assert ok.all(), f"{(~ok).sum()} of {ok.size} D outside the bound"
     if ref_aux is not None:
         got_aux = bf16_to_f64(got_aux_bits)
-        ok, stated = gemm_within(got_aux, ref_aux, s, b, h, spec.K)
+        ok, stated = gemm_check(got_aux, ref_aux, s, b, spec.K, h_pairs)
         print(f"{spec.name}: aux {ok.mean():.6f} within bound, {stated.mean():.6f} within the stated tolerance alone")
         assert ok.all(), f"{(~ok).sum()} of {ok.size} aux outside the bound"
 
@@ -246,14 +247,15 @@ def check_grouped(counts, N, K, epi, seed, full_cols=False, rows_per_expert=None
         oqb, osb = oracle.quantize_rowwise(np.ascontiguousarray(b[e * N + cols]), oracle.E4M3)
         be = None if bias is None else bias[e][cols]
         ref_d, ref_aux, s = oracle.mx_gemm(oqa, osa, oracle.E4M3, oqb, osb, oracle.E4M3, be, epi)
-        h = mfma_model.truncation_bound(oqa, osa, oracle.E4M3, oqb, osb, oracle.E4M3)
+        def h_pairs(ri, ci):
+            return mfma_model.truncation_bound_pairs(oqa, osa, oracle.E4M3, oqb, osb, oracle.E4M3, ri, ci)
         got_bits = host(d[rows][:, cols])
         got_aux_bits = None if aux is None else host(aux[rows][:, cols])
         check_against_model(got_bits, got_aux_bits, oqa, osa, oracle.E4M3, oqb, osb, oracle.E4M3, be, epi)
-        ok, _ = gemm_within(bf16_to_f64(got_bits), ref_d, s, be, h, K, through_gelu=epi == "bias_gelu_aux")
+        ok, _ = gemm_check(bf16_to_f64(got_bits), ref_d, s, be, K, h_pairs, through_gelu=epi == "bias_gelu_aux")
         assert ok.all(), f"expert {e}: {(~ok).sum()} of {ok.size} outside the bound"
         if ref_aux is not None:
-            ok, _ = gemm_within(bf16_to_f64(got_aux_bits), ref_aux, s, be, h, K)
+            ok, _ = gemm_check(bf16_to_f64(got_aux_bits), ref_aux, s, be, K, h_pairs)
             assert ok.all(), f"expert {e} aux: {(~ok).sum()} outside the bound"
         off += me
 
