@@ -34,9 +34,20 @@ namespace temx {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int kThreads = 256;
-constexpr int WT = 128;        // wave tile edge
-constexpr int FR = WT / 16;    // MFMA tiles per wave edge
+
+// Wave layout of the 256 x 256 workgroup tile: NWM x NWN waves, each
+// computing a (256 / NWM) x (256 / NWN) block as FRM x FRN MFMA tiles of
+// 16 x 16.  Layout<2, 2>: 4 waves of 128 x 128 (256 accumulators each, one
+// wave per SIMD).  Layout<4, 2>: 8 waves of 64 x 128 (128 accumulators,
+// two waves per SIMD, so one wave's MFMAs cover the other's LDS reads).
+template <int NWM_, int NWN_>
+struct Layout {
+  static constexpr int NWM = NWM_, NWN = NWN_, NW = NWM * NWN, kThreads = 64 * NW;
+  static constexpr int WTM = BM / NWM, WTN = BN / NWN;
+  static constexpr int FRM = WTM / 16, FRN = WTN / 16;
+};
+using L4 = Layout<2, 2>;
+using L8 = Layout<4, 2>;
 constexpr int kAData = BM * BK;
 constexpr int kBData = BN * BK;
 constexpr int kAScale = BM * 4;
@@ -44,13 +55,14 @@ constexpr int kBScale = BN * 4;
 constexpr int kGroupM = 4;      // row-tile band of the raster order
 constexpr int kMaxGroups = 1024;
 
-// LDS data tile of one operand and stage: two K-halves (K bytes 0-63 and
-// 64-127 of the step), each [256 rows][64 bytes] = 16 KB.  In a half, the
-// four 16-byte chunks of row r are permuted by chunk ^ swz(r), so that the
-// ds_read_b128 of 8 (or 16) consecutive rows at one logical chunk hit
-// distinct banks for 128-byte (or 256-byte) bank rows.
-constexpr int kHalf = BM * 64;
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// LDS data tile of one operand and stage: [256 rows][128 bytes] (the step's
+// 128 K bytes of each row).  The eight 16-byte chunks of row r are permuted
+// by chunk ^ swz(r).  A fragment read has lane 16 g + r fetch logical chunks
+// g and g + 4 of row r; with swz(r) = (r >> 1) & 7 these ds_read_b128 run
+// without bank conflicts on gfx950 (measured: 4.2 clocks per wave
+// instruction, the same as a linear 1-KB read; unswizzled 128-byte rows take
+// 14.5).  Chunk g + 4 is at chunk g's address XOR 64.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 template <int F> struct MfmaFmt;  // cbsz / blgp operand format codes
 template <> struct MfmaFmt<TE_E4M3> { static constexpr int v = 0; };
@@ -112,8 +124,8 @@ __device__ __forceinline__ void lds_dma4(const i32x4& rsrc, uint32_t lds_addr, i
       : "memory");
 }
 
-// LDS layout of one pipeline stage: A data, B data (two K-halves each, see
-// kHalf), A scales [256][4], B scales [256][4].  Two stages.
+// LDS layout of one pipeline stage: A data [256][128], B data [256][128],
+// A scales [256][4], B scales [256][4].  Two stages.
 constexpr int kOffBData = kAData;
 constexpr int kOffAScale = kAData + kBData;
 constexpr int kOffBScale = kOffAScale + kAScale;
@@ -121,40 +133,51 @@ constexpr int kStage = kOffBScale + kBScale;
 constexpr int kLds = 2 * kStage;
 
 // Per-lane byte offsets of the tile copies.  A copy instruction fills one
-// 1-KB slice of a half: rows 16 b .. 16 b + 15, lane l landing at LDS byte
-// 16 l, i.e. row 16 b + l/4, physical chunk l % 4, which holds logical chunk
-// (l % 4) ^ swz(l/4) (swz only sees row bits 1-3).  Wave w copies the slices
-// b = w + 4 (i % 4) of half i / 4, i = 0..7, so one per-lane offset plus the
-// uniform 64 (i % 4) K + 64 (i / 4) + 128 kt serves every copy.  The scale
-// slice of wave w is rows 64 w .. 64 w + 63, four bytes (one K step) each.
+// 1-KB slice: rows 8 q .. 8 q + 7, lane l landing at LDS byte 16 l, i.e. row
+// 8 q + l/8, physical chunk l % 8, which holds logical chunk
+// (l % 8) ^ swz(8 q + l/8) = (l % 8) ^ (l / 16) ^ (4 if q is odd).  Each
+// instruction reads 8 whole 128-byte lines.  The 32 slices of an operand
+// tile are dealt to the NW waves as q = w + NW i; q has wave w's parity, so
+// one per-lane offset plus the uniform 8 NW i K + 128 kt serves every copy.
+// Scale slices are rows 64 s .. 64 s + 63 of the 256 x 4-byte scale tile:
+// with 4 waves wave w copies slice w of both operands, with 8 waves waves 0-3
+// copy A's and 4-7 copy B's.
 struct CopyOffsets {
   int data;
   int scale;
 };
 
+template <class LY>
 __device__ __forceinline__ CopyOffsets copy_offsets(int64_t K, int wave, int lane) {
-  const int sub = lane >> 2;
-  const int chunk = (lane & 3) ^ swz(sub);
+  const int chunk = (lane & 7) ^ (lane >> 4) ^ ((wave & 1) << 2);
   CopyOffsets o;
-  o.data = (int)((16 * wave + sub) * K) + chunk * 16;
-  o.scale = (int)((64 * wave + lane) * (K / 32));
+  o.data = (int)((8 * wave + (lane >> 3)) * K) + chunk * 16;
+  o.scale = (int)((64 * (wave & 3) + lane) * (K / 32));
   return o;
 }
 
-__device__ __forceinline__ void load_operand(uint32_t lds_data, uint32_t lds_scale, const Operand& op,
-                                             const CopyOffsets& off, int64_t K, int kt, int wave) {
+template <class LY>
+__device__ __forceinline__ void load_data(uint32_t lds_data, const Operand& op, const CopyOffsets& off, int64_t K,
+                                          int kt, int wave) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int half = i >> 2, b = wave + 4 * (i & 3);
-    lds_dma16(op.data, lds_data + half * kHalf + b * 1024, off.data, (int)(64 * (i & 3) * K) + 64 * half + kt * BK);
+  for (int i = 0; i < 32 / LY::NW; ++i) {
+    const int q = wave + LY::NW * i;
+    lds_dma16(op.data, lds_data + q * 1024, off.data, (int)(8 * LY::NW * i * K) + kt * BK);
   }
-  lds_dma4(op.scale, lds_scale + wave * 256, off.scale, kt * 4);
 }
 
+template <class LY>
 __device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, const Operand& B,
                                            const CopyOffsets& off, int64_t K, int kt, int wave) {
-  load_operand(stage, stage + kOffAScale, A, off, K, kt, wave);
-  load_operand(stage + kOffBData, stage + kOffBScale, B, off, K, kt, wave);
+  load_data<LY>(stage, A, off, K, kt, wave);
+  load_data<LY>(stage + kOffBData, B, off, K, kt, wave);
+  if constexpr (LY::NW == 4) {
+    lds_dma4(A.scale, stage + kOffAScale + wave * 256, off.scale, kt * 4);
+    lds_dma4(B.scale, stage + kOffBScale + wave * 256, off.scale, kt * 4);
+  } else {
+    if (wave < 4) lds_dma4(A.scale, stage + kOffAScale + wave * 256, off.scale, kt * 4);
+    else lds_dma4(B.scale, stage + kOffBScale + (wave - 4) * 256, off.scale, kt * 4);
+  }
 }
 
 struct Frag {
@@ -168,45 +191,49 @@ struct Frag {
 // offset a single opaque VGPR so that the compiler does not re-associate it
 // into per-fragment address registers.
 struct ReadOffsets {
-  int a_data, b_data, a_scale, b_scale, shift;
+  int a_data, a_data2, b_data, b_data2, a_scale, b_scale, shift;
 };
 
+template <class LY>
 __device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) {
   const int g = lane >> 4, r = lane & 15;
-  const int lane_off = r * 64 + ((g ^ swz(r)) << 4);
+  const int lane_off = r * BK + ((g ^ swz(r)) << 4);
   ReadOffsets o;
-  o.a_data = wm * WT * 64 + lane_off;
-  o.b_data = kOffBData + wn * WT * 64 + lane_off;
-  o.a_scale = kOffAScale + (wm * WT + r) * 4;
-  o.b_scale = kOffBScale + (wn * WT + r) * 4;
+  o.a_data = wm * LY::WTM * BK + lane_off;
+  o.a_data2 = o.a_data ^ 64;
+  o.b_data = kOffBData + wn * LY::WTN * BK + lane_off;
+  o.b_data2 = o.b_data ^ 64;
+  o.a_scale = kOffAScale + (wm * LY::WTM + r) * 4;
+  o.b_scale = kOffBScale + (wn * LY::WTN + r) * 4;
   o.shift = 8 * g;
-  asm volatile("" : "+v"(o.a_data), "+v"(o.b_data), "+v"(o.a_scale), "+v"(o.b_scale), "+v"(o.shift));
+  asm volatile("" : "+v"(o.a_data), "+v"(o.a_data2), "+v"(o.b_data), "+v"(o.b_data2), "+v"(o.a_scale),
+               "+v"(o.b_scale), "+v"(o.shift));
   return o;
 }
 
-// Fragment j: two 16-byte chunks (K 16g.. of each half of the step) of row
+// Fragment j: two 16-byte chunks (K 16g.. and 64 + 16g.. of the step) of row
 // 16 j + r of the wave's rows, and the E8M0 byte of block g of that row in the
-// low byte of s.
-__device__ __forceinline__ Frag read_frag(const uint8_t* stage, int data_off, int scale_off, int shift, int j) {
-  const uint8_t* p = stage + data_off + j * 1024;
-  const uint4 lo = *reinterpret_cast<const uint4*>(p);
-  const uint4 hi = *reinterpret_cast<const uint4*>(p + kHalf);
+// low byte of s.  Rows 16 j further are 2 KB further (an immediate offset).
+__device__ __forceinline__ Frag read_frag(const uint8_t* stage, int data_off, int data_off2, int scale_off, int shift,
+                                          int j) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(stage + data_off + j * 16 * BK);
+  const uint4 hi = *reinterpret_cast<const uint4*>(stage + data_off2 + j * 16 * BK);
   Frag f;
   f.v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   f.s = (int)(*reinterpret_cast<const uint32_t*>(stage + scale_off + j * 64) >> shift);
   return f;
 }
 
-template <int FA, int FB>
-__device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[FR][FR], const ReadOffsets& ro) {
-  Frag bop[FR];
+template <class LY, int FA, int FB>
+__device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN][LY::FRM], const ReadOffsets& ro) {
+  Frag bop[LY::FRM];
 #pragma unroll
-  for (int j = 0; j < FR; ++j) bop[j] = read_frag(stage, ro.a_data, ro.a_scale, ro.shift, j);
+  for (int j = 0; j < LY::FRM; ++j) bop[j] = read_frag(stage, ro.a_data, ro.a_data2, ro.a_scale, ro.shift, j);
 #pragma unroll
-  for (int i = 0; i < FR; ++i) {
-    const Frag aop = read_frag(stage, ro.b_data, ro.b_scale, ro.shift, i);
+  for (int i = 0; i < LY::FRN; ++i) {
+    const Frag aop = read_frag(stage, ro.b_data, ro.b_data2, ro.b_scale, ro.shift, i);
 #pragma unroll
-    for (int j = 0; j < FR; ++j)
+    for (int j = 0; j < LY::FRM; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop.v, bop[j].v, acc[i][j], MfmaFmt<FB>::v,
                                                                    MfmaFmt<FA>::v, 0, aop.s, 0, bop[j].s);
   }
@@ -216,38 +243,40 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[FR][FR]
 // kt computes; each stage is read only after s_waitcnt vmcnt(0) and a barrier
 // (all waves' copies landed), and refilled only after the next barrier (all
 // waves finished reading it).
-template <int FA, int FB>
-__device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[FR][FR], const Operand& A, const Operand& B,
-                                         int64_t K, int wave, int lane) {
-  const int wm = wave >> 1, wn = wave & 1;
+template <class LY, int FA, int FB>
+__device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::FRM], const Operand& A,
+                                         const Operand& B, int64_t K, int wave, int lane) {
+  const int wm = wave / LY::NWN, wn = wave % LY::NWN;
 #pragma unroll
-  for (int i = 0; i < FR; ++i)
+  for (int i = 0; i < LY::FRN; ++i)
 #pragma unroll
-    for (int j = 0; j < FR; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < LY::FRM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const int kt_n = (int)(K / BK);
   if (kt_n == 0) return;
-  const CopyOffsets off = copy_offsets(K, wave, lane);
-  const ReadOffsets ro = read_offsets(wm, wn, lane);
+  const CopyOffsets off = copy_offsets<LY>(K, wave, lane);
+  const ReadOffsets ro = read_offsets<LY>(wm, wn, lane);
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-  load_stage(lds_addr, A, B, off, K, 0, wave);
+  load_stage<LY>(lds_addr, A, B, off, K, 0, wave);
   for (int kt = 0; kt < kt_n; ++kt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kt + 1 < kt_n) load_stage(lds_addr + ((kt + 1) & 1) * kStage, A, B, off, K, kt + 1, wave);
-    compute<FA, FB>(lds + (kt & 1) * kStage, acc, ro);
+    if (kt + 1 < kt_n) load_stage<LY>(lds_addr + ((kt + 1) & 1) * kStage, A, B, off, K, kt + 1, wave);
+
+    compute<LY, FA, FB>(lds + (kt & 1) * kStage, acc, ro);
   }
 }
 
 // Epilogue from registers.  acc[i][j][e] is D[m][n] with
-// m = m0 + 128 wm + 16 j + (lane & 15), n = n0 + 128 wn + 16 i + 4 (lane >> 4) + e.
-template <int EPI, int OUT>
-__device__ __forceinline__ void epilogue(const v4f (&acc)[FR][FR], void* d, uint16_t* aux, const uint16_t* bias,
-                                         int64_t m0, int64_t m_end, int64_t n0, int64_t N, int wave, int lane) {
-  const int wm = wave >> 1, wn = wave & 1;
+// m = m0 + WTM wm + 16 j + (lane & 15), n = n0 + WTN wn + 16 i + 4 (lane >> 4) + e.
+template <class LY, int EPI, int OUT>
+__device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], void* d, uint16_t* aux,
+                                         const uint16_t* bias, int64_t m0, int64_t m_end, int64_t n0, int64_t N,
+                                         int wave, int lane) {
+  const int wm = wave / LY::NWN, wn = wave % LY::NWN;
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
-  for (int i = 0; i < FR; ++i) {
-    const int64_t n = n0 + wn * WT + 16 * i + 4 * g;
+  for (int i = 0; i < LY::FRN; ++i) {
+    const int64_t n = n0 + wn * LY::WTN + 16 * i + 4 * g;
     if (n >= N) continue;
     float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
     if constexpr (EPI != TE_EPI_NONE) {
@@ -258,8 +287,8 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[FR][FR], void* d, uint
       b3 = bf16_bits_to_float(bb.y >> 16);
     }
 #pragma unroll
-    for (int j = 0; j < FR; ++j) {
-      const int64_t m = m0 + wm * WT + 16 * j + r;
+    for (int j = 0; j < LY::FRM; ++j) {
+      const int64_t m = m0 + wm * LY::WTM + 16 * j + r;
       if (m >= m_end) continue;
       float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
       if constexpr (EPI != TE_EPI_NONE) {
@@ -299,8 +328,8 @@ struct GemmParams {
 };
 
 // Dense: one workgroup per 256 x 256 tile.
-template <int FA, int FB, int EPI, int OUT>
-__global__ __launch_bounds__(kThreads) void mx_gemm_kernel(GemmParams p) {
+template <class LY, int FA, int FB, int EPI, int OUT>
+__global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -321,15 +350,15 @@ __global__ __launch_bounds__(kThreads) void mx_gemm_kernel(GemmParams p) {
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K);
   const Operand B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K);
-  v4f acc[FR][FR];
-  mainloop<FA, FB>(lds, acc, A, B, p.K, wave, lane);
-  epilogue<EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
+  v4f acc[LY::FRN][LY::FRM];
+  mainloop<LY, FA, FB>(lds, acc, A, B, p.K, wave, lane);
+  epilogue<LY, EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
 }
 
 // Grouped: a persistent grid walks the flat list of (expert row-tile,
 // n-tile) pairs, built in LDS from the device-resident splits.
-template <int FA, int FB, int EPI, int OUT>
-__global__ __launch_bounds__(kThreads) void mx_grouped_gemm_kernel(GemmParams p) {
+template <class LY, int FA, int FB, int EPI, int OUT>
+__global__ __launch_bounds__(LY::kThreads) void mx_grouped_gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
   __shared__ int tile_prefix[kMaxGroups + 1];
   __shared__ int64_t row_off[kMaxGroups + 1];
@@ -373,20 +402,26 @@ __global__ __launch_bounds__(kThreads) void mx_grouped_gemm_kernel(GemmParams p)
     const Operand A = make_operand(p.a, p.a_scale, m0, m_end - m0, p.K);
     const Operand B = make_operand(p.b + (int64_t)e * p.N * p.K, p.b_scale + (int64_t)e * p.N * (p.K / 32), n0,
                                    p.N - n0, p.K);
-    v4f acc[FR][FR];
+    v4f acc[LY::FRN][LY::FRM];
     __syncthreads();  // the previous tile's last reads of stage 0/1 are done
-    mainloop<FA, FB>(lds, acc, A, B, p.K, wave, lane);
-    epilogue<EPI, OUT>(acc, p.d, p.aux, EPI == TE_EPI_NONE ? nullptr : p.bias + (int64_t)e * p.N, m0, m_end, n0,
-                       p.N, wave, lane);
+    mainloop<LY, FA, FB>(lds, acc, A, B, p.K, wave, lane);
+    epilogue<LY, EPI, OUT>(acc, p.d, p.aux, EPI == TE_EPI_NONE ? nullptr : p.bias + (int64_t)e * p.N, m0, m_end,
+                           n0, p.N, wave, lane);
   }
 }
+
+#ifndef TEMX_GEMM_LAYOUT
+#define TEMX_GEMM_LAYOUT L8
+#endif
+using KLayout = TEMX_GEMM_LAYOUT;
 
 template <bool GROUPED, int FA, int FB, int EPI, int OUT>
 te_status launch4(const GemmParams& p, dim3 grid, hipStream_t stream) {
   if constexpr (GROUPED)
-    hipLaunchKernelGGL((mx_grouped_gemm_kernel<FA, FB, EPI, OUT>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((mx_grouped_gemm_kernel<KLayout, FA, FB, EPI, OUT>), grid, dim3(KLayout::kThreads), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((mx_gemm_kernel<FA, FB, EPI, OUT>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((mx_gemm_kernel<KLayout, FA, FB, EPI, OUT>), grid, dim3(KLayout::kThreads), 0, stream, p);
   return launch_status();
 }
 
