@@ -39,18 +39,30 @@ PEAK_FP8_TFLOPS = 5000.0      # dense FP8 / MXFP8 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0         # HBM3E, MI355X
 METRIC = "MXFP8 GEMM TFLOP/s + % of MI355X FP8 MFMA peak; quantize GB/s % of HBM"
 ROTATE = 4                     # copies of each bandwidth-bound input / output
+# kernels each kind of op launches, in order (names as the profiler reports them)
+KERNELS = {"quantize_row": ["quantize_rowwise_kernel"], "quantize_col": ["quantize_colwise_kernel"],
+           "gemm": ["mx_gemm_kernel"], "grouped": ["mx_grouped_gemm_kernel"],
+           "cast": ["amax_partial_kernel", "amax_final_kernel", "cast_kernel"]}
+CALIBRATION_BYTES = 512 << 20  # one device-to-device copy of this many bytes reads and writes it once
 
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--workload", default="square_8192",
                    choices=["square_8192", "decoder_fwd", "hybrid_bwd", "moe_grouped", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, copy a 512 MiB buffer 3 times (counter calibration)")
+    p.add_argument("--record-ops", metavar="PATH",
+                   help="write the op / kernel launch order and this run's line to PATH (for profile summaries)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/")
+    p.add_argument("--stats-from", metavar="DIR",
+                   help="no GPU: turn a rocprofv3 --kernel-trace --stats run into profiles/")
+    p.add_argument("--command", default="", help="the profiling command, recorded with --stats-from")
     return p.parse_args()
 
 
@@ -62,9 +74,11 @@ class Step:
     def __init__(self, name):
         self.name = name
         self.ops = []      # (label, kind, fn(rot), flops, bytes)
+        self.kernels = []  # per op: names of the kernels it launches, in launch order
 
-    def add(self, label, kind, fn, flops=0.0, nbytes=0.0):
+    def add(self, label, kind, fn, flops=0.0, nbytes=0.0, kernels=None):
         self.ops.append((label, kind, fn, flops, nbytes))
+        self.kernels.append(list(kernels or KERNELS[kind]))
 
     @property
     def flops(self):
@@ -124,7 +138,7 @@ def build_step(workload, torch, te, workloads):
                 te.te_mxfp8_quantize(src[r], fmt, "row", q, s, None, None)
             else:
                 te.te_mxfp8_quantize(src[r], fmt, "col", None, None, q, s)
-        step.add(label, "quantize", fn, 0.0, q_bytes(rows, cols))
+        step.add(label, "quantize", fn, 0.0, q_bytes(rows, cols), KERNELS["quantize_" + direction])
         quantized[key] = bufs
         return bufs
 
@@ -156,7 +170,7 @@ def build_step(workload, torch, te, workloads):
                                      g.epilogue, bias, aux)
         flops = 2.0 * g.total_m * g.N * g.K
         step.add(f"grouped_gemm_{g.name}_{g.experts}x{g.N}x{g.K}", "gemm", fn, flops,
-                 gemm_bytes(g.total_m, g.N, g.K, g.epilogue, g.experts))
+                 gemm_bytes(g.total_m, g.N, g.K, g.epilogue, g.experts), KERNELS["grouped"])
 
     for spec, fmt in w.current_scaling:
         src = rotated(spec.make())
@@ -247,6 +261,9 @@ def cpu_baseline(workload, workloads):
 
 # ------------------------------------------------------------------ traffic
 
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
 def kernel_sources_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "mxfp8_mixed_precision_amd", "csrc")
@@ -256,25 +273,152 @@ def kernel_sources_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(label):
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def measured_traffic(workload, label):
+    """HBM bytes per launch of one op from the committed counter summary, if it
+    was taken on the current kernel sources; else None."""
     try:
-        with open(path) as fh:
+        with open(TRAFFIC_JSON) as fh:
             data = json.load(fh)
     except (OSError, ValueError):
         return None
-    entry = data.get("kernels", {}).get(label)
-    if not entry or data.get("sources_hash") != kernel_sources_hash():
+    if data.get("sources_hash") != kernel_sources_hash():
         return None
-    return entry.get("bytes_per_launch")
+    entry = data.get("workloads", {}).get(workload, {}).get("ops", {}).get(label)
+    return None if entry is None else entry["bytes_per_launch"]
+
+
+def _read_counters(csv_path, counter):
+    """Dispatches of one rocprofv3 --pmc CSV: [(kernel name, value in KiB)] in dispatch order."""
+    import csv
+    with open(csv_path) as fh:
+        rows = [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows]
+
+
+def _per_op(dispatches, record):
+    """Sum the counter over each op's kernels, averaged over the recorded passes.
+
+    The library's dispatches come in the order bench.py launched them:
+    (warmup + steps) passes over the ops, each op launching its kernels in order."""
+    ours = [(n, v) for n, v in dispatches if "temx::" in n]
+    seq = [(op["label"], k) for op in record["ops"] for k in op["kernels"]]
+    passes = record["warmup"] + record["steps"]
+    if len(ours) != passes * len(seq):
+        raise SystemExit(f"expected {passes} x {len(seq)} library dispatches, found {len(ours)}")
+    totals = {op["label"]: 0.0 for op in record["ops"]}
+    for i, (name, v) in enumerate(ours):
+        label, kern = seq[i % len(seq)]
+        if kern not in name:
+            raise SystemExit(f"dispatch {i}: expected {kern}, found {name[:80]}")
+        totals[label] += v
+    return {k: v / passes for k, v in totals.items()}
+
+
+def _calibration(dispatches, record):
+    """KiB the counter reads for one copy of CALIBRATION_BYTES (the copies bench.py makes last)."""
+    copies = [v for n, v in dispatches if "copyBuffer" in n][-record["calibration_copies"]:]
+    return sum(copies) / len(copies)
+
+
+def traffic_from(fetch_dir, write_dir):
+    """Write the per-op HBM traffic of two counter runs into the committed summary."""
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        with open(os.path.join(d, "ops.json")) as fh:
+            record = json.load(fh)
+        csvs = [os.path.join(r, f) for r, _, fs in os.walk(d) for f in fs if f.endswith("counter_collection.csv")]
+        disp = _read_counters(csvs[0], counter)
+        copy_kib = _calibration(disp, record)
+        factor = CALIBRATION_BYTES / (copy_kib * 1024.0)
+        out[counter] = (record, copy_kib, factor, _per_op(disp, record))
+    record = out["FETCH_SIZE"][0]
+    wl = record["workload"]
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        data = {}
+    if data.get("sources_hash") != kernel_sources_hash():
+        data = {"sources_hash": kernel_sources_hash(), "workloads": {}}
+    ops = {}
+    for op in record["ops"]:
+        lab = op["label"]
+        fb = out["FETCH_SIZE"][3][lab] * 1024.0 * out["FETCH_SIZE"][2]
+        wb = out["WRITE_SIZE"][3][lab] * 1024.0 * out["WRITE_SIZE"][2]
+        ops[lab] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+                    "algorithmic_bytes": round(op["bytes"]) if op["bytes"] else None}
+    data["workloads"][wl] = {
+        "calibration": {"copy_bytes": CALIBRATION_BYTES,
+                        "fetch_kib_per_copy": out["FETCH_SIZE"][1], "fetch_factor": round(out["FETCH_SIZE"][2], 4),
+                        "write_kib_per_copy": out["WRITE_SIZE"][1], "write_factor": round(out["WRITE_SIZE"][2], 4)},
+        "commands": [out[c][0]["command"].replace("PMC", c) for c in ("FETCH_SIZE", "WRITE_SIZE")],
+        "ops": ops}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(data, fh, indent=1)
+    md = [f"# HBM traffic per launch, workload {wl}", "",
+          "Counters FETCH_SIZE and WRITE_SIZE (KiB per dispatch), one rocprofv3 --pmc run each, scaled by",
+          f"what the same counter reads for a device-to-device copy of {CALIBRATION_BYTES >> 20} MiB made in the "
+          "same run:", ""]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        md.append(f"- {c}: {out[c][1]:.1f} KiB per copy -> factor {out[c][2]:.4f}")
+    md += ["", "Commands (from the repository root, GPU box):", ""]
+    md += ["    " + c for c in data["workloads"][wl]["commands"]]
+    md += ["", "| op | fetch MB | write MB | total MB | algorithmic MB | total / algorithmic |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for lab, e in ops.items():
+        alg = e["algorithmic_bytes"]
+        md.append(f"| {lab} | {e['fetch_bytes'] / 1e6:.2f} | {e['write_bytes'] / 1e6:.2f} | "
+                  f"{e['bytes_per_launch'] / 1e6:.2f} | {alg / 1e6 if alg else float('nan'):.2f} | "
+                  f"{e['bytes_per_launch'] / alg if alg else float('nan'):.3f} |")
+    md += ["", f"Kernel sources hash: {data['sources_hash']}", ""]
+    path = os.path.join(ROOT, "profiles", f"{wl}_traffic.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(md))
+    print(f"wrote {TRAFFIC_JSON} and {path}")
+
+
+def stats_from(stats_dir, command):
+    """Summarise a rocprofv3 --kernel-trace --stats CSV next to the bench line it profiled."""
+    import csv
+    csvs = [os.path.join(r, f) for r, _, fs in os.walk(stats_dir) for f in fs if f.endswith("kernel_stats.csv")]
+    with open(csvs[0]) as fh:
+        rows = list(csv.DictReader(fh))
+    with open(os.path.join(stats_dir, "ops.json")) as fh:
+        record = json.load(fh)
+    wl = record["workload"]
+    md = [f"# Kernel time, workload {wl}", "", "Command (from the repository root, GPU box):", "",
+          "    " + command, "", "rocprofv3 kernel statistics:", "",
+          "| kernel | calls | avg us | min us | max us | total % |", "|---|---:|---:|---:|---:|---:|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"]
+        short = name.replace("void ", "").replace("temx::(anonymous namespace)::", "").split("(")[0]
+        md.append(f"| `{short[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    if record.get("bench_line"):
+        md += ["", "Per-op averages from HIP events in the same run (bench.py):", "",
+               "| op | avg us |", "|---|---:|"]
+        for k in record["bench_line"]["kernels"]:
+            md.append(f"| {k['name']} | {k['avg_ms'] * 1e3:.2f} |")
+        md += ["", "bench.py line of this run:", "", "    " + json.dumps(record["bench_line"]["summary"])]
+    md += ["", f"Kernel sources hash: {kernel_sources_hash()}", ""]
+    path = os.path.join(ROOT, "profiles", f"{wl}_kernel_stats.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(md))
+    print(f"wrote {path}")
 
 
 # --------------------------------------------------------------------- main
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
+    if args.stats_from:
+        stats_from(args.stats_from, args.command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the MXFP8 Linear path is built and measured on a single MI355X "
@@ -335,12 +479,12 @@ def main():
         roof = {"bound": "hbm", "achieved": round(dbytes / (dms * 1e-3) / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(dlabel)
+    w = workloads.ALL[args.workload]()
+    roof["traffic"] = measured_traffic(w.name, dlabel)
     roof["kernel"] = dlabel
 
     value = step.flops / (ms_per_step * 1e-3) / 1e12
     qk = [k for k in kernels if k["kind"] == "quantize"]
-    w = workloads.ALL[args.workload]()
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -352,9 +496,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3/e5m2 x e8m0 -> fp32 acc, bf16 out",
+        "dtype": "fp8",
         "data": "synthetic (seeded N(0, sigma) bf16, outlier columns per config)",
         "config": {"workload": w.name, "gemm_flops_per_step": step.flops, "parallelism": "single GPU",
+                   "arithmetic": "MXFP8 (E4M3/E5M2 codes, E8M0 block scales) products, fp32 accumulate",
                    "rotating_buffers": ROTATE},
         "roofline": roof,
         "quantize_gbs_min": min((k["gbs"] for k in qk), default=None),
@@ -362,13 +507,28 @@ def main():
         "kernels": kernels,
     }
     if args.copy_calibration:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        src = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, workloads)
+    if args.record_ops:
+        summary = {k: v for k, v in out.items() if k != "kernels"}
+        rdir = os.path.relpath(os.path.dirname(os.path.abspath(args.record_ops)), ROOT)
+        rec = {"workload": w.name, "warmup": args.warmup, "steps": args.steps,
+               "calibration_copies": 3 if args.copy_calibration else 0,
+               "command": f"timeout -s KILL 120 rocprofv3 --pmc PMC --output-format csv -d {rdir} -o run -- "
+                          f"python bench.py --workload {args.workload} --steps {args.steps} "
+                          f"--warmup {args.warmup} --no-cpu-baseline --copy-calibration "
+                          f"--record-ops {os.path.relpath(os.path.abspath(args.record_ops), ROOT)}",
+               "ops": [{"label": o[0], "kind": o[1], "bytes": o[4], "kernels": k}
+                       for o, k in zip(step.ops, step.kernels)],
+               "bench_line": {"kernels": kernels, "summary": summary}}
+        os.makedirs(os.path.dirname(os.path.abspath(args.record_ops)), exist_ok=True)
+        with open(args.record_ops, "w") as fh:
+            json.dump(rec, fh)
     print(json.dumps(out), flush=True)
 
 
