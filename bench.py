@@ -191,9 +191,10 @@ def build_step(workload, torch, te, workloads):
 def cpu_baseline(workload, workloads):
     """Time the oracle on a bounded sample of the step and scale it to the full step.
 
-    Sample: the oracle's step restricted to the first S rows of every operand
-    (S = 1024 for 8192-sized operands): the quantizes of those rows and the
-    GEMM block D[:S, :S].  The full-step time is estimated as
+    Sample: the oracle's step restricted to the first rows of every operand
+    (up to 4096, fewer where one sampled GEMM block would exceed 2.5e11
+    flop): the quantizes of those rows and the GEMM block they produce; about
+    10-20 s of host work.  The full-step time is estimated as
     quantize_time * (full quantize elements / sampled ones) +
     gemm_time * (full GEMM flops / sampled ones).
     """
@@ -207,11 +208,16 @@ def cpu_baseline(workload, workloads):
     w = workloads.ALL[workload]()
     q_time = q_elems_s = q_elems_full = 0.0
     g_time = g_flops_s = g_flops_full = 0.0
-    S = 1024
+    S = 4096
     gemms = list(w.gemms)
     for g in gemms:
         a, b = g.a_src.make(), g.b_src.make()
         sm, sn = min(S, g.M), min(S, g.N)
+        while 2.0 * sm * sn * g.K > 2.5e11:
+            if sm >= sn:
+                sm //= 2
+            else:
+                sn //= 2
         fa, fb = oracle.format_by_name(g.fmt_a), oracle.format_by_name(g.fmt_b)
         t0 = time.perf_counter()
         qa, sa = (oracle.quantize_rowwise(a[:sm], fa) if g.a_dir == "row"
@@ -252,7 +258,7 @@ def cpu_baseline(workload, workloads):
         g_flops_full += 2.0 * g.total_m * g.N * g.K
     est = q_time * (q_elems_full / max(q_elems_s, 1)) + g_time * (g_flops_full / max(g_flops_s, 1))
     return {"value": g_flops_full / est / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"oracle (numpy fp64) on the first {S} rows of each operand: quantize "
+            "sample": (f"oracle (numpy fp64) on the first rows of each operand (up to {S}): quantize "
                        f"{q_elems_s:.3g} elements in {q_time:.2f} s (1 thread), GEMM {g_flops_s:.3g} flop in "
                        f"{g_time:.2f} s ({threads} BLAS threads); full step estimated at {est:.1f} s by scaling "
                        f"each part to the full step's elements / flops"),
@@ -297,22 +303,32 @@ def _read_counters(csv_path, counter):
 
 
 def _per_op(dispatches, record):
-    """Sum the counter over each op's kernels, averaged over the recorded passes.
+    """Average the counter over each op's launches (an op's kernels summed).
 
-    The library's dispatches come in the order bench.py launched them:
-    (warmup + steps) passes over the ops, each op launching its kernels in order."""
+    The library's dispatches come in the order bench.py made them: the
+    (warmup + steps) passes over the step's ops, then, op by op, the
+    attribution launches (1 + steps each)."""
     ours = [(n, v) for n, v in dispatches if "temx::" in n]
-    seq = [(op["label"], k) for op in record["ops"] for k in op["kernels"]]
-    passes = record["warmup"] + record["steps"]
-    if len(ours) != passes * len(seq):
-        raise SystemExit(f"expected {passes} x {len(seq)} library dispatches, found {len(ours)}")
+    order = []
+    for _ in range(record["warmup"] + record["steps"]):
+        order += [op for op in record["ops"]]
+    for op in record["ops"]:
+        order += [op] * (1 + record["steps"])
+    expected = sum(len(op["kernels"]) for op in order)
+    if len(ours) != expected:
+        raise SystemExit(f"expected {expected} library dispatches, found {len(ours)}")
     totals = {op["label"]: 0.0 for op in record["ops"]}
-    for i, (name, v) in enumerate(ours):
-        label, kern = seq[i % len(seq)]
-        if kern not in name:
-            raise SystemExit(f"dispatch {i}: expected {kern}, found {name[:80]}")
-        totals[label] += v
-    return {k: v / passes for k, v in totals.items()}
+    launches = {op["label"]: 0 for op in record["ops"]}
+    i = 0
+    for op in order:
+        for kern in op["kernels"]:
+            name, v = ours[i]
+            if kern not in name:
+                raise SystemExit(f"dispatch {i}: expected {kern}, found {name[:80]}")
+            totals[op["label"]] += v
+            i += 1
+        launches[op["label"]] += 1
+    return {k: totals[k] / launches[k] for k in totals}
 
 
 def _calibration(dispatches, record):
@@ -436,30 +452,35 @@ def main():
     stream = torch.cuda.current_stream()
     nops = len(step.ops)
 
-    def run(i, events=None):
+    def run(i):
         r = i % ROTATE
-        for k, (_, _, fn, _, _) in enumerate(step.ops):
-            if events is not None:
-                events[k].record(stream)
+        for _, _, fn, _, _ in step.ops:
             fn(r)
-        if events is not None:
-            events[nops].record(stream)
 
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        run(i, ev[i])
+        run(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
+    # Per-op attribution, right after the timed region on the same stream: each
+    # op launched `steps` times back to back (rotating buffers as in the step),
+    # bracketed by two HIP events, so no marker sits between its launches.
     kernels = []
-    for k, (label, kind, _, flops, nbytes) in enumerate(step.ops):
-        ms = sum(ev[i][k].elapsed_time(ev[i][k + 1]) for i in range(args.steps)) / args.steps
+    for label, kind, fn, flops, nbytes in step.ops:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        fn(0)
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i % ROTATE)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
         ent = {"name": label, "kind": kind, "avg_ms": round(ms, 5)}
         if flops:
             ent["tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)

@@ -41,59 +41,165 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rowwise_kernel(
     const uint32_t code = e8m0_code_from_amax_bits<FMT>(amax_bits);
     const uint2 r = cvt8_scaled<FMT>(v[u], e8m0_to_float(code));
     if (c < nchunks) {
-      q[c] = r;
+      store_nt8(q + c, r);
       if ((threadIdx.x & 3) == 0) s[c >> 2] = (uint8_t)code;
     }
   }
 }
 
-// Columnwise (transposed): a 128-row x 64-column bf16 tile is staged through
-// LDS with coalesced 16-byte loads; wave w then encodes rows 32w..32w+31 of
-// the tile (one block) and lane l owns column l, so each lane writes the 32
-// codes of its block contiguously into row c of the transposed output.
-constexpr int kColTileR = 128;
-constexpr int kColTileC = 64;
-constexpr int kColPitch = kColTileC + 8;  // bf16 elements; 144-byte rows keep 16-byte stores aligned
+// Columnwise (transposed), without an LDS round trip for the input.
+//
+// A workgroup of 8 waves covers 128 columns; wave w takes the 64-column
+// strip (w & 1) and the row range (w >> 1) of the workgroup's 4 consecutive
+// row ranges, each `cpw` chunks of 128 rows.  Lane (rq, g) = (lane >> 3,
+// lane & 7) loads rows 4rq..4rq+3 of each 32-row block straight into
+// registers, 8 columns (16 bytes) each, so every load instruction still
+// covers eight whole 128-byte row segments.  The block amax of a column is
+// the max over the 8 lanes with the same g (DPP row rotate by 8, a swizzle
+// across 16 lanes, a permute across 32).  Each lane then packs the values of
+// one column from row pairs, converts them with that column's scale, and
+// holds 4 codes (rows 4rq..4rq+3) per column.
+//
+// Codes go through a wave-private LDS stage of 64 output rows x 128 bytes
+// (one 128-row chunk): a lane writes 4 bytes per column at row offset
+// (32 (block & 3) + 4 rq) XOR (16 g), which spreads the 64 lanes over the
+// banks (2-way at most) and leaves every 16-byte piece whole, so the stage
+// drains with 16-byte stores covering whole 128-byte lines.  These stores
+// are ordinary (cached) ones: measured on gfx950, streaming stores of this
+// scattered line pattern are ~10% slower, while the input loads, read once,
+// are streaming.  The
+// E8M0 codes of the workgroup's 128 columns collect in LDS and leave after
+// one barrier as runs of up to 32 bytes per column (a partial line costs a
+// full 64-byte memory write; shorter runs would cost more).
+constexpr int kColWaves = 8;
+constexpr int kColThreads = 64 * kColWaves;
+constexpr int kColStrip = 64;          // columns per wave
+constexpr int kColWgCols = 2 * kColStrip;
+constexpr int kColChunk = 128;         // rows per staged chunk
+constexpr int kColMaxChunks = 2;       // chunks per wave at most
+constexpr int kColScaleRun = 4 * kColMaxChunks * 4;  // scale codes per column and workgroup, at most
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
+}
+
+// max over the 8 lanes l, l^8, l^16, ..., l^56 (packed u16 halves)
+__device__ __forceinline__ uint32_t max_over_row_quads(uint32_t v, int lane) {
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false));   // row_ror:8 = lane ^ 8
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F));                // lane ^ 16
+  v = pk_max_u16(v, (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, (int)v));      // lane ^ 32
+  return v;
+}
 
 template <int FMT>
-__global__ __launch_bounds__(256) void quantize_colwise_kernel(
+__device__ __forceinline__ uint32_t cvt4_scaled(uint32_t rows01, uint32_t rows23, float scale) {
+  v2s r = {0, 0};
+  if constexpr (FMT == TE_E4M3) {
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf, rows01), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(v2bf, rows23), scale, true);
+  } else {
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(v2bf, rows01), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(v2bf, rows23), scale, true);
+  }
+  return saturate_bytes<FMT>(__builtin_bit_cast(uint32_t, r));
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kColThreads) void quantize_colwise_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ qc, uint8_t* __restrict__ sc,
-    int64_t rows, int64_t cols) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kColTileR * kColPitch];
-  const int64_t r0 = (int64_t)blockIdx.y * kColTileR;
-  const int64_t c0 = (int64_t)blockIdx.x * kColTileC;
-  // 128 rows x 8 chunks of 16 bytes; 256 threads x 4
+    int64_t rows, int64_t cols, int cpw) {
+  __shared__ __attribute__((aligned(16))) uint8_t stage_all[kColWaves][kColStrip * kColChunk];
+  __shared__ uint8_t scodes[kColWgCols * kColScaleRun];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int cs = wave & 1, rg = wave >> 1;
+  const int rq = lane >> 3, g = lane & 7;
+  const int64_t wg_rows = 4 * (int64_t)cpw * kColChunk;
+  const int64_t R0 = (int64_t)blockIdx.y * wg_rows;
+  const int64_t c0 = (int64_t)blockIdx.x * kColWgCols;
+  const int64_t r0w = R0 + (int64_t)rg * cpw * kColChunk;  // first row of this wave
+  const int64_t c0w = c0 + kColStrip * cs;                   // first column of this wave
+  const int64_t gcol = c0w + 8 * g;                           // this lane's 8 columns
+  const bool col_ok = gcol < cols;
+  int nblocks = (int)max((int64_t)0, min((int64_t)cpw * 4, (rows - r0w) / 32));
+  if (c0w >= cols) nblocks = 0;
+  uint8_t* stage = stage_all[wave];
+  const int64_t lane_row = r0w + 4 * rq;
+
+  auto load = [&](u32x4 (&v)[4], int k) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    const int r = idx >> 3, ch = idx & 7;
-    const int64_t gr = r0 + r, gc = c0 + ch * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (gr < rows && gc < cols) v = load_nt16(x + gr * cols + gc);
-    *reinterpret_cast<uint4*>(&tile[r * kColPitch + ch * 8]) = v;
+    for (int i = 0; i < 4; ++i)
+      v[i] = col_ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (lane_row + 32 * k + i) * cols + gcol))
+                    : u32x4{0, 0, 0, 0};
+  };
+
+  auto process = [&](const u32x4 (&v)[4], int k) {
+    uint32_t m[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      m[d] = pk_max_u16(pk_max_u16(v[0][d] & 0x7FFF7FFFu, v[1][d] & 0x7FFF7FFFu),
+                        pk_max_u16(v[2][d] & 0x7FFF7FFFu, v[3][d] & 0x7FFF7FFFu));
+      m[d] = max_over_row_quads(m[d], lane);
+    }
+    const int row_off = (32 * (k & 3) + 4 * rq) ^ (16 * g);
+    uint32_t my_code = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = j >> 1;
+      const uint32_t amax_bits = (j & 1) ? (m[d] >> 16) : (m[d] & 0xFFFFu);
+      const uint32_t code = e8m0_code_from_amax_bits<FMT>(amax_bits);
+      const float scale = e8m0_to_float(code);
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;  // high or low bf16 halves of two rows
+      const uint32_t q = cvt4_scaled<FMT>(__builtin_amdgcn_perm(v[1][d], v[0][d], sel),
+                                          __builtin_amdgcn_perm(v[3][d], v[2][d], sel), scale);
+      *reinterpret_cast<uint32_t*>(&stage[(8 * g + j) * kColChunk + row_off]) = q;
+      my_code = rq == j ? code : my_code;
+    }
+    scodes[(kColStrip * cs + 8 * g + rq) * kColScaleRun + rg * cpw * 4 + k] = (uint8_t)my_code;
+    if ((k & 3) == 3 || k == nblocks - 1) {
+      // drain the chunk: 64 output rows, 16-byte pieces, 8 lanes per 128-byte segment
+      const int valid = 32 * ((k & 3) + 1);
+      const int64_t out_row0 = r0w + kColChunk * (k >> 2);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's stage writes have landed
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int piece = lane + 64 * kk;
+        const int orow = piece >> 3, seg = piece & 7;
+        const uint4 val = *reinterpret_cast<const uint4*>(&stage[orow * kColChunk + ((16 * seg) ^ (16 * (orow >> 3)))]);
+        if (16 * seg < valid && c0w + orow < cols)
+          *reinterpret_cast<uint4*>(qc + (c0w + orow) * rows + out_row0 + 16 * seg) = val;
+      }
+      asm volatile("" ::: "memory");  // the next chunk's stage writes stay after these reads
+    }
+  };
+
+  u32x4 va[4], vb[4];
+  if (nblocks > 0) load(va, 0);
+  for (int k = 0; k < nblocks; k += 2) {
+    if (k + 1 < nblocks) load(vb, k + 1);
+    process(va, k);
+    if (k + 1 < nblocks) {
+      if (k + 2 < nblocks) load(va, k + 2);
+      process(vb, k + 1);
+    }
   }
+
   __syncthreads();
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int64_t gc = c0 + l;
-  const int64_t gr = r0 + 32 * w;
-  if (gr >= rows || gc >= cols) return;
-  uint4 v[4];
-  uint32_t* vw = reinterpret_cast<uint32_t*>(v);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t lo = tile[(32 * w + 2 * i) * kColPitch + l];
-    const uint32_t hi = tile[(32 * w + 2 * i + 1) * kColPitch + l];
-    vw[i] = lo | (hi << 16);
+  // the workgroup's scale codes: column c, blocks R0/32 .. R0/32 + nbw - 1, consecutive threads on consecutive bytes
+  const int nbw = (int)max((int64_t)0, min(wg_rows, rows - R0) / 32);
+  const int64_t sstride = rows / 32;
+  for (int idx = threadIdx.x; idx < kColWgCols * nbw; idx += kColThreads) {
+    const int c = idx / nbw, b = idx - c * nbw;
+    if (c0 + c < cols) sc[(c0 + c) * sstride + R0 / 32 + b] = scodes[c * kColScaleRun + b];
   }
-  const uint32_t amax_bits = max(max(absmax_bits8(v[0]), absmax_bits8(v[1])), max(absmax_bits8(v[2]), absmax_bits8(v[3])));
-  const uint32_t code = e8m0_code_from_amax_bits<FMT>(amax_bits);
-  const float scale = e8m0_to_float(code);
-  const uint2 a = cvt8_scaled<FMT>(v[0], scale), b = cvt8_scaled<FMT>(v[1], scale);
-  const uint2 c = cvt8_scaled<FMT>(v[2], scale), d = cvt8_scaled<FMT>(v[3], scale);
-  uint4* out = reinterpret_cast<uint4*>(qc + gc * rows + gr);
-  out[0] = make_uint4(a.x, a.y, b.x, b.y);
-  out[1] = make_uint4(c.x, c.y, d.x, d.y);
-  sc[gc * (rows / 32) + gr / 32] = (uint8_t)code;
+}
+
+// Chunks of 128 rows per colwise wave: two (32-byte scale runs) when the grid
+// still has two workgroups per CU, else one.
+int colwise_chunks_per_wave(int64_t rows, int64_t cols) {
+  const int64_t col_tiles = (cols + kColWgCols - 1) / kColWgCols;
+  const int64_t row_tiles_2 = (rows + 4 * 2 * kColChunk - 1) / (4 * 2 * kColChunk);
+  return col_tiles * row_tiles_2 >= 2 * (int64_t)device_cu_count() ? 2 : 1;
 }
 
 template <int FMT>
@@ -108,8 +214,11 @@ te_status launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, te_qdir
     if (launch_status() != TE_OK) return TE_ERR_HIP;
   }
   if (dir & TE_COLWISE) {
-    dim3 grid((unsigned)((cols + kColTileC - 1) / kColTileC), (unsigned)((rows + kColTileR - 1) / kColTileR));
-    hipLaunchKernelGGL(quantize_colwise_kernel<FMT>, grid, dim3(256), 0, stream, x, q_col, s_col, rows, cols);
+    const int cpw = colwise_chunks_per_wave(rows, cols);
+    const int64_t rows_per_wg = 4 * (int64_t)cpw * kColChunk;
+    dim3 grid((unsigned)((cols + kColWgCols - 1) / kColWgCols), (unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
+    hipLaunchKernelGGL(quantize_colwise_kernel<FMT>, grid, dim3(kColThreads), 0, stream, x, q_col, s_col, rows, cols,
+                       cpw);
     if (launch_status() != TE_OK) return TE_ERR_HIP;
   }
   return TE_OK;

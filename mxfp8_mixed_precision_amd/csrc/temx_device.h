@@ -27,6 +27,15 @@ __device__ __forceinline__ uint4 load_nt16(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Streaming stores (non-temporal: the output is not read again by this kernel).
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_nt16(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store_nt8(void* p, uint2 v) {
+  __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<u32x2*>(p));
+}
+
 // Exponent of the largest finite value of the element format.
 template <int FMT> struct FmtTraits;
 template <> struct FmtTraits<TE_E4M3> {

@@ -117,6 +117,32 @@ def test_quantize_8192_square_sampled(fmt):
     assert np.array_equal(host(qc[cols]), oq) and np.array_equal(host(sc[cols]), os_)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [
+    (8288, 8232),    # 8192^2-sized strips (up to 8 chunks of 128 rows) with a 96-row and a 40-column tail
+    (4128, 14344),   # last strip chunk a single 32-row block, 8-column tail
+    (14336, 4096),   # the HYBRID backward W1 (dgrad B)
+    (4096, 14336),   # the HYBRID backward dY (wgrad A)
+    (4096, 4096),    # the HYBRID backward X (wgrad B)
+])
+def test_colwise_equals_rowwise_of_transpose_full_size(fmt, shape):
+    # colwise(X) == rowwise(X^T) element for element on the whole tensor (the
+    # rowwise kernel is pinned to the oracle above), plus sampled columns
+    # against the oracle itself
+    rows, cols = shape
+    bits = workloads.normal_bf16(90, rows + 7 * cols, shape, 1.0, 0.01)
+    x = dev(bits)
+    _, _, qc, sc = te().mxfp8_quantize(x, fmt, "col")
+    qr, sr, _, _ = te().mxfp8_quantize(x.t().contiguous(), fmt, "row")
+    torch.cuda.synchronize()
+    assert torch.equal(sc, sr), "colwise scales differ from rowwise of the transpose"
+    assert torch.equal(qc, qr), "colwise codes differ from rowwise of the transpose"
+    f = oracle.format_by_name(fmt)
+    sel = sampled_rows(cols, k=24, seed=3)
+    oq, os_ = oracle.quantize_colwise(np.ascontiguousarray(bits[:, sel]), f)
+    assert np.array_equal(host(sc[sel]), os_) and np.array_equal(host(qc[sel]), oq)
+
+
 @pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 1000, 4096 * 8 + 3, 1 << 20, 4096 * 4096])
 def test_amax(n):
     bits = workloads.normal_bf16(88, n, (n,), 1.5, 0.0) if n else np.zeros(0, np.uint16)
