@@ -18,7 +18,8 @@
 //   (m), so each lane ends with 4 consecutive output columns of one row: the
 //   epilogue stores 8 bytes (bf16) per lane straight from registers.
 // * 256 x 256 workgroup tile, 8 waves in 4 x 2 (two per SIMD), 64 x 128 per
-//   wave (4 x 8 MFMA tiles = 128 fp32 accumulators per lane), K step 128.
+//   wave (4 x 8 MFMA tiles = 128 fp32 accumulators per lane), K step 128;
+//   a 128 x 128 tile (4 waves of 64 x 64) for grids the big tile cannot fill.
 // * A, B and their scale tiles are copied global -> LDS with direct-to-LDS
 //   buffer loads (buffer_load_dwordx4 / _dword ... lds), double-buffered
 //   (2 x 66 KB), issued by one wave per SIMD.
@@ -33,29 +34,39 @@
 namespace temx {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int BK = 128;
 
-// Wave layout of the 256 x 256 workgroup tile: NWM x NWN waves, each
-// computing a (256 / NWM) x (256 / NWN) block as FRM x FRN MFMA tiles of
-// 16 x 16.  Layout<2, 2>: 4 waves of 128 x 128 (256 accumulators each, one
-// wave per SIMD).  Layout<4, 2>: 8 waves of 64 x 128 (128 accumulators,
-// two waves per SIMD, so one wave's MFMAs cover the other's LDS reads).
-template <int NWM_, int NWN_>
-struct Layout {
-  static constexpr int NWM = NWM_, NWN = NWN_, NW = NWM * NWN, kThreads = 64 * NW;
+// Workgroup tile configurations.  A BM x BN tile is computed by NWM x NWN
+// waves, each a (BM / NWM) x (BN / NWN) block of FRM x FRN MFMA tiles of
+// 16 x 16; the last NCOPY waves issue the stage copies.  One stage in LDS is
+// A data [BM][128], B data [BN][128], A scales [BM][4], B scales [BN][4];
+// two stages.
+//   Big:   256 x 256, 8 waves of 64 x 128 (two per SIMD, 128 accumulators),
+//          waves 4-7 copy; 132 KB of LDS, one workgroup per CU.
+//   Small: 128 x 128, 4 waves of 64 x 64 (64 accumulators), all four copy;
+//          66 KB of LDS, two workgroups per CU.  For grids the big tile
+//          cannot fill (few or ragged row tiles).
+template <int BM_, int BN_, int NWM_, int NWN_, int NCOPY_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_, NW = NWM * NWN, kThreads = 64 * NW;
+  static constexpr int NCOPY = NCOPY_;
   static constexpr int WTM = BM / NWM, WTN = BN / NWN;
   static constexpr int FRM = WTM / 16, FRN = WTN / 16;
+  static constexpr int kAData = BM * BK, kBData = BN * BK, kAScale = BM * 4, kBScale = BN * 4;
+  static constexpr int kOffBData = kAData;
+  static constexpr int kOffAScale = kAData + kBData;
+  static constexpr int kOffBScale = kOffAScale + kAScale;
+  static constexpr int kStage = kOffBScale + kBScale;
+  static constexpr int kLds = 2 * kStage;
+  static_assert(BM == BN, "one row clamp and one copy scheme serve both operands");
+  static_assert(NCOPY % 2 == 0 && (BM / 8) % NCOPY == 0 && (BM / 64) <= NCOPY, "copy slices per copier wave");
 };
-using L4 = Layout<2, 2>;
-using L8 = Layout<4, 2>;
-constexpr int kAData = BM * BK;
-constexpr int kBData = BN * BK;
-constexpr int kAScale = BM * 4;
-constexpr int kBScale = BN * 4;
+using Big = Cfg<256, 256, 4, 2, 4>;
+using Small = Cfg<128, 128, 2, 2, 4>;
 constexpr int kGroupM = 4;      // row-tile band of the raster order
 constexpr int kMaxGroups = 1024;
 
-// LDS data tile of one operand and stage: [256 rows][128 bytes] (the step's
+// LDS data tile of one operand and stage: [BM rows][128 bytes] (the step's
 // 128 K bytes of each row).  The eight 16-byte chunks of row r are permuted
 // by chunk ^ swz(r).  A fragment read has lane 16 g + r fetch logical chunks
 // g and g + 4 of row r; with swz(r) = (r >> 1) & 7 these ds_read_b128 run
@@ -89,8 +100,8 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
 }
 
 __device__ __forceinline__ Operand make_operand(const uint8_t* data, const uint8_t* scale, int64_t row0,
-                                                int64_t rows, int64_t K) {
-  rows = rows < 0 ? 0 : (rows > BM ? BM : rows);
+                                                int64_t rows, int64_t K, int64_t tile_rows) {
+  rows = rows < 0 ? 0 : (rows > tile_rows ? tile_rows : rows);
   return Operand{make_rsrc(data + row0 * K, rows * K), make_rsrc(scale + row0 * (K / 32), rows * (K / 32))};
 }
 
@@ -124,59 +135,42 @@ __device__ __forceinline__ void lds_dma4(const i32x4& rsrc, uint32_t lds_addr, i
       : "memory");
 }
 
-// LDS layout of one pipeline stage: A data [256][128], B data [256][128],
-// A scales [256][4], B scales [256][4].  Two stages.
-constexpr int kOffBData = kAData;
-constexpr int kOffAScale = kAData + kBData;
-constexpr int kOffBScale = kOffAScale + kAScale;
-constexpr int kStage = kOffBScale + kBScale;
-constexpr int kLds = 2 * kStage;
-
 // Per-lane byte offsets of the tile copies.  A copy instruction fills one
 // 1-KB slice: rows 8 q .. 8 q + 7, lane l landing at LDS byte 16 l, i.e. row
 // 8 q + l/8, physical chunk l % 8, which holds logical chunk
 // (l % 8) ^ swz(8 q + l/8) = (l % 8) ^ (l / 16) ^ (4 if q is odd).  Each
-// instruction reads 8 whole 128-byte lines.  The 32 slices of an operand
-// tile are dealt to the NW waves as q = w + NW i; q has wave w's parity, so
-// one per-lane offset plus the uniform 8 NW i K + 128 kt serves every copy.
-// Scale slices are rows 64 s .. 64 s + 63 of the 256 x 4-byte scale tile:
-// with 4 waves wave w copies slice w of both operands, with 8 waves waves 0-3
-// copy A's and 4-7 copy B's.
+// instruction reads 8 whole 128-byte lines.  The BM/8 slices of an operand
+// tile are dealt to the NCOPY copier waves as q = c + NCOPY i; with NCOPY
+// even, q has copier c's parity, so one per-lane offset plus the uniform
+// 8 NCOPY i K + 128 kt serves every copy.  Scale slices are rows
+// 64 s .. 64 s + 63 of the BM x 4-byte scale tile; copier c < BM/64 copies
+// scale slice c of both operands.
 struct CopyOffsets {
   int data;
   int scale;
 };
 
-template <class LY>
-__device__ __forceinline__ CopyOffsets copy_offsets(int64_t K, int wave, int lane) {
-  const int chunk = (lane & 7) ^ (lane >> 4) ^ ((wave & 1) << 2);
+__device__ __forceinline__ CopyOffsets copy_offsets(int64_t K, int c, int lane) {
+  const int chunk = (lane & 7) ^ (lane >> 4) ^ ((c & 1) << 2);
   CopyOffsets o;
-  o.data = (int)((8 * wave + (lane >> 3)) * K) + chunk * 16;
-  o.scale = (int)((64 * (wave & 3) + lane) * (K / 32));
+  o.data = (int)((8 * c + (lane >> 3)) * K) + chunk * 16;
+  o.scale = (int)((64 * c + lane) * (K / 32));
   return o;
 }
 
-template <class LY>
-__device__ __forceinline__ void load_data(uint32_t lds_data, const Operand& op, const CopyOffsets& off, int64_t K,
-                                          int kt, int wave) {
-#pragma unroll
-  for (int i = 0; i < 32 / LY::NW; ++i) {
-    const int q = wave + LY::NW * i;
-    lds_dma16(op.data, lds_data + q * 1024, off.data, (int)(8 * LY::NW * i * K) + kt * BK);
-  }
-}
-
-template <class LY>
+template <class C>
 __device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, const Operand& B,
-                                           const CopyOffsets& off, int64_t K, int kt, int wave) {
-  load_data<LY>(stage, A, off, K, kt, wave);
-  load_data<LY>(stage + kOffBData, B, off, K, kt, wave);
-  if constexpr (LY::NW == 4) {
-    lds_dma4(A.scale, stage + kOffAScale + wave * 256, off.scale, kt * 4);
-    lds_dma4(B.scale, stage + kOffBScale + wave * 256, off.scale, kt * 4);
-  } else {
-    if (wave < 4) lds_dma4(A.scale, stage + kOffAScale + wave * 256, off.scale, kt * 4);
-    else lds_dma4(B.scale, stage + kOffBScale + (wave - 4) * 256, off.scale, kt * 4);
+                                           const CopyOffsets& off, int64_t K, int kt, int c) {
+#pragma unroll
+  for (int i = 0; i < C::BM / 8 / C::NCOPY; ++i) {
+    const int q = c + C::NCOPY * i;
+    const int so = (int)(8 * C::NCOPY * i * K) + kt * BK;
+    lds_dma16(A.data, stage + q * 1024, off.data, so);
+    lds_dma16(B.data, stage + C::kOffBData + q * 1024, off.data, so);
+  }
+  if (c < C::BM / 64) {
+    lds_dma4(A.scale, stage + C::kOffAScale + c * 256, off.scale, kt * 4);
+    lds_dma4(B.scale, stage + C::kOffBScale + c * 256, off.scale, kt * 4);
   }
 }
 
@@ -195,16 +189,16 @@ struct ReadOffsets {
 };
 
 template <class LY>
-__device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) {
+__device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) {  // LY: a Cfg
   const int g = lane >> 4, r = lane & 15;
   const int lane_off = r * BK + ((g ^ swz(r)) << 4);
   ReadOffsets o;
   o.a_data = wm * LY::WTM * BK + lane_off;
   o.a_data2 = o.a_data ^ 64;
-  o.b_data = kOffBData + wn * LY::WTN * BK + lane_off;
+  o.b_data = LY::kOffBData + wn * LY::WTN * BK + lane_off;
   o.b_data2 = o.b_data ^ 64;
-  o.a_scale = kOffAScale + (wm * LY::WTM + r) * 4;
-  o.b_scale = kOffBScale + (wn * LY::WTN + r) * 4;
+  o.a_scale = LY::kOffAScale + (wm * LY::WTM + r) * 4;
+  o.b_scale = LY::kOffBScale + (wn * LY::WTN + r) * 4;
   o.shift = 8 * g;
   asm volatile("" : "+v"(o.a_data), "+v"(o.a_data2), "+v"(o.b_data), "+v"(o.b_data2), "+v"(o.a_scale),
                "+v"(o.b_scale), "+v"(o.shift));
@@ -244,17 +238,15 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN
 // (all copies landed), and refilled only after the next barrier (all waves
 // finished reading it).
 //
-// Only waves 4-7 (one per SIMD) issue the copies, a quarter stage each in the
-// 4-wave slice scheme.  A direct-to-LDS buffer load holds up the wave that
-// issues it for ~70-90 clocks (measured on gfx950, whether the data is in L2
-// or not), so a wave issuing 18 of them stalls for most of a step; with the
-// copies on one wave per SIMD, the other wave of the SIMD keeps the MFMA pipe
-// busy meanwhile (measured: 8192^3 GEMM ~10% faster than with all 8 waves
-// copying).
+// Only the last NCOPY waves issue the copies.  A direct-to-LDS buffer load
+// holds up the wave that issues it for ~70-90 clocks (measured on gfx950,
+// whether the data is in L2 or not), so a wave issuing many of them stalls
+// for much of a step.  In the big tile the copiers are waves 4-7, one per
+// SIMD, and the other wave of each SIMD keeps the MFMA pipe busy meanwhile
+// (measured: 8192^3 GEMM ~10% faster than with all 8 waves copying).
 template <class LY, int FA, int FB>
 __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::FRM], const Operand& A,
                                          const Operand& B, int64_t K, int wave, int lane) {
-  static_assert(LY::NW == 8, "the copy split assumes two waves per SIMD");
   const int wm = wave / LY::NWN, wn = wave % LY::NWN;
 #pragma unroll
   for (int i = 0; i < LY::FRN; ++i)
@@ -262,17 +254,18 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
     for (int j = 0; j < LY::FRM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const int kt_n = (int)(K / BK);
   if (kt_n == 0) return;
-  const bool copier = wave >= 4;
-  const CopyOffsets off = copy_offsets<L4>(K, wave & 3, lane);
+  const int c = wave - (LY::NW - LY::NCOPY);
+  const bool copier = c >= 0;
+  const CopyOffsets off = copy_offsets(K, copier ? c : 0, lane);
   const ReadOffsets ro = read_offsets<LY>(wm, wn, lane);
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-  if (copier) load_stage<L4>(lds_addr, A, B, off, K, 0, wave & 3);
+  if (copier) load_stage<LY>(lds_addr, A, B, off, K, 0, c);
   for (int kt = 0; kt < kt_n; ++kt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (copier && kt + 1 < kt_n) load_stage<L4>(lds_addr + ((kt + 1) & 1) * kStage, A, B, off, K, kt + 1, wave & 3);
+    if (copier && kt + 1 < kt_n) load_stage<LY>(lds_addr + ((kt + 1) & 1) * LY::kStage, A, B, off, K, kt + 1, c);
 
-    compute<LY, FA, FB>(lds + (kt & 1) * kStage, acc, ro);
+    compute<LY, FA, FB>(lds + (kt & 1) * LY::kStage, acc, ro);
   }
 }
 
@@ -337,10 +330,11 @@ struct GemmParams {
   int32_t groups;           // grouped only
 };
 
-// Dense: one workgroup per 256 x 256 tile.
+// Dense: one workgroup per tile.
 template <class LY, int FA, int FB, int EPI, int OUT>
 __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+  constexpr int BM = LY::BM, BN = LY::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ntm = (int)((p.M + BM - 1) / BM), ntn = (int)((p.N + BN - 1) / BN);
@@ -358,8 +352,8 @@ __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
   const int tm = first_tm + in_band % band_rows;
   const int tn = in_band / band_rows;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K);
-  const Operand B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K);
+  const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, BM);
+  const Operand B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, BN);
   v4f acc[LY::FRN][LY::FRM];
   mainloop<LY, FA, FB>(lds, acc, A, B, p.K, wave, lane);
   epilogue<LY, EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
@@ -369,7 +363,8 @@ __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
 // n-tile) pairs, built in LDS from the device-resident splits.
 template <class LY, int FA, int FB, int EPI, int OUT>
 __global__ __launch_bounds__(LY::kThreads) void mx_grouped_gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kLds];
+  constexpr int BM = LY::BM, BN = LY::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
   __shared__ int tile_prefix[kMaxGroups + 1];
   __shared__ int64_t row_off[kMaxGroups + 1];
   const int lane = threadIdx.x & 63;
@@ -409,9 +404,9 @@ __global__ __launch_bounds__(LY::kThreads) void mx_grouped_gemm_kernel(GemmParam
     const int64_t m0 = row_off[e] + (int64_t)(rt - tile_prefix[e]) * BM;
     const int64_t m_end = row_off[e + 1];
     const int64_t n0 = (int64_t)tn * BN;
-    const Operand A = make_operand(p.a, p.a_scale, m0, m_end - m0, p.K);
+    const Operand A = make_operand(p.a, p.a_scale, m0, m_end - m0, p.K, BM);
     const Operand B = make_operand(p.b + (int64_t)e * p.N * p.K, p.b_scale + (int64_t)e * p.N * (p.K / 32), n0,
-                                   p.N - n0, p.K);
+                                   p.N - n0, p.K, BN);
     v4f acc[LY::FRN][LY::FRM];
     __syncthreads();  // the previous tile's last reads of stage 0/1 are done
     mainloop<LY, FA, FB>(lds, acc, A, B, p.K, wave, lane);
@@ -420,39 +415,48 @@ __global__ __launch_bounds__(LY::kThreads) void mx_grouped_gemm_kernel(GemmParam
   }
 }
 
-using KLayout = L8;
-
-template <bool GROUPED, int FA, int FB, int EPI, int OUT>
-te_status launch4(const GemmParams& p, dim3 grid, hipStream_t stream) {
+template <class C, bool GROUPED, int FA, int FB, int EPI, int OUT>
+te_status launch5(const GemmParams& p, dim3 grid, hipStream_t stream) {
   if constexpr (GROUPED)
-    hipLaunchKernelGGL((mx_grouped_gemm_kernel<KLayout, FA, FB, EPI, OUT>), grid, dim3(KLayout::kThreads), 0, stream,
-                       p);
+    hipLaunchKernelGGL((mx_grouped_gemm_kernel<C, FA, FB, EPI, OUT>), grid, dim3(C::kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((mx_gemm_kernel<KLayout, FA, FB, EPI, OUT>), grid, dim3(KLayout::kThreads), 0, stream, p);
+    hipLaunchKernelGGL((mx_gemm_kernel<C, FA, FB, EPI, OUT>), grid, dim3(C::kThreads), 0, stream, p);
   return launch_status();
 }
 
-template <bool GROUPED, int FA, int FB, int EPI>
-te_status launch3(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stream) {
-  return out == TE_BF16 ? launch4<GROUPED, FA, FB, EPI, TE_BF16>(p, grid, stream)
-                        : launch4<GROUPED, FA, FB, EPI, TE_FP32>(p, grid, stream);
+template <class C, bool GROUPED, int FA, int FB, int EPI>
+te_status launch4(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stream) {
+  return out == TE_BF16 ? launch5<C, GROUPED, FA, FB, EPI, TE_BF16>(p, grid, stream)
+                        : launch5<C, GROUPED, FA, FB, EPI, TE_FP32>(p, grid, stream);
 }
 
-template <bool GROUPED, int FA, int FB>
-te_status launch2(const GemmParams& p, te_epilogue epi, te_dtype out, dim3 grid, hipStream_t stream) {
+template <class C, bool GROUPED, int FA, int FB>
+te_status launch3(const GemmParams& p, te_epilogue epi, te_dtype out, dim3 grid, hipStream_t stream) {
   switch (epi) {
-    case TE_EPI_NONE: return launch3<GROUPED, FA, FB, TE_EPI_NONE>(p, out, grid, stream);
-    case TE_EPI_BIAS: return launch3<GROUPED, FA, FB, TE_EPI_BIAS>(p, out, grid, stream);
-    default: return launch3<GROUPED, FA, FB, TE_EPI_BIAS_GELU_AUX>(p, out, grid, stream);
+    case TE_EPI_NONE: return launch4<C, GROUPED, FA, FB, TE_EPI_NONE>(p, out, grid, stream);
+    case TE_EPI_BIAS: return launch4<C, GROUPED, FA, FB, TE_EPI_BIAS>(p, out, grid, stream);
+    default: return launch4<C, GROUPED, FA, FB, TE_EPI_BIAS_GELU_AUX>(p, out, grid, stream);
   }
 }
 
-template <bool GROUPED>
-te_status launch(const GemmParams& p, te_dtype fa, te_dtype fb, te_epilogue epi, te_dtype out, dim3 grid,
-                 hipStream_t stream) {
-  if (fa == TE_E4M3 && fb == TE_E4M3) return launch2<GROUPED, TE_E4M3, TE_E4M3>(p, epi, out, grid, stream);
-  if (fa == TE_E5M2 && fb == TE_E4M3) return launch2<GROUPED, TE_E5M2, TE_E4M3>(p, epi, out, grid, stream);
-  return launch2<GROUPED, TE_E4M3, TE_E5M2>(p, epi, out, grid, stream);
+template <class C, bool GROUPED>
+te_status launch2(const GemmParams& p, te_dtype fa, te_dtype fb, te_epilogue epi, te_dtype out, dim3 grid,
+                  hipStream_t stream) {
+  if (fa == TE_E4M3 && fb == TE_E4M3) return launch3<C, GROUPED, TE_E4M3, TE_E4M3>(p, epi, out, grid, stream);
+  if (fa == TE_E5M2 && fb == TE_E4M3) return launch3<C, GROUPED, TE_E5M2, TE_E4M3>(p, epi, out, grid, stream);
+  return launch3<C, GROUPED, TE_E4M3, TE_E5M2>(p, epi, out, grid, stream);
+}
+
+// The big tile unless its grid leaves CUs idle.  Measured on MI355X (256 CUs):
+// the small tile (4x the tiles, two workgroups per CU) is faster with fewer
+// 256 x 256 tiles than CUs (4096 x 1024 x 4096: 33 vs 56 us; 4096 x 3072 x
+// 1024: 24 vs 26 us), and with up to two tiles per CU when K is short
+// (4096 x 4096 x 1024 + GELU aux: 42 vs 48 us, where the small tiles overlap
+// one round's output stores with the next round's MFMAs); the big tile wins
+// with long K (4096 x 4096 x 14336: 215 vs 299 us) and on larger grids.
+inline bool use_small_tile(int64_t big_tiles, int64_t K) {
+  const int64_t cus = device_cu_count();
+  return big_tiles < cus || (big_tiles < 2 * cus && K <= 4096);
 }
 
 te_status check_common(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,
@@ -506,15 +510,18 @@ extern "C" te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_
   (void)workspace_bytes;
   TE_REQUIRE(M >= 0 && N >= 0 && K >= 0, TE_ERR_SHAPE);
   TE_REQUIRE(K % 128 == 0 && M % 16 == 0 && N % 16 == 0, TE_ERR_SHAPE);
-  TE_REQUIRE(M <= ((int64_t)1 << 31) - BM && N <= ((int64_t)1 << 31) - BN && K <= ((int64_t)1 << 31) - BK,
+  TE_REQUIRE(M <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 31) - BK,
              TE_ERR_SHAPE);
-  const int64_t ntiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  TE_REQUIRE(ntiles < ((int64_t)1 << 31), TE_ERR_SHAPE);
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  TE_REQUIRE(((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 31), TE_ERR_SHAPE);
   te_status st = check_common(a, a_scale, a_fmt, b, b_scale, b_fmt, d, d_dtype, epi, bias, aux, M > 0 && N > 0, K > 0);
   if (st != TE_OK) return st;
   if (M == 0 || N == 0) return TE_OK;
   GemmParams p{a, a_scale, b, b_scale, d, bias, aux, M, N, K, nullptr, 0};
-  return launch<false>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)ntiles), stream);
+  if (use_small_tile(big_tiles, K))
+    return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_dtype,
+                                 dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))), stream);
+  return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)big_tiles), stream);
 }
 
 extern "C" te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_splits, int64_t total_m,
@@ -528,9 +535,9 @@ extern "C" te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_
   TE_REQUIRE(num_groups >= 1 && num_groups <= kMaxGroups, TE_ERR_SHAPE);
   TE_REQUIRE(total_m >= 0 && N > 0 && K > 0, TE_ERR_SHAPE);
   TE_REQUIRE(K % 128 == 0 && N % 16 == 0, TE_ERR_SHAPE);
-  TE_REQUIRE(total_m <= ((int64_t)1 << 31) - BM && N <= ((int64_t)1 << 31) - BN && K <= ((int64_t)1 << 31) - BK,
+  TE_REQUIRE(total_m <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 31) - BK,
              TE_ERR_SHAPE);
-  TE_REQUIRE((total_m / BM + num_groups) * ((N + BN - 1) / BN) < ((int64_t)1 << 31), TE_ERR_SHAPE);
+  TE_REQUIRE((total_m / 128 + num_groups) * ((N + 127) / 128) < ((int64_t)1 << 31), TE_ERR_SHAPE);
   TE_REQUIRE(m_splits != nullptr, TE_ERR_NULL);
   TE_REQUIRE(((uintptr_t)m_splits & 3u) == 0, TE_ERR_ALIGN);
   te_status st = check_common(a, a_scale, a_fmt, b, b_scale, b_fmt, d, d_dtype, epi, bias, aux, total_m > 0, true);
@@ -539,5 +546,11 @@ extern "C" te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_
   GemmParams p{a, a_scale, b, b_scale, d, bias, aux, total_m, N, K, m_splits, num_groups};
   int grid = device_cu_count();
   grid = grid < 8 ? 8 : (grid / 8) * 8;
-  return launch<true>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)grid), stream);
+  // the splits stay on the device: estimate the big-tile count from the total
+  // rows, counting one ragged tail tile per group (32 experts x ~512 rows x
+  // 1536 columns: big tiles 172 us, small 222 us)
+  const int64_t big_tiles = (total_m / 256 + num_groups) * ((N + 255) / 256);
+  if (use_small_tile(big_tiles, K))
+    return launch2<Small, true>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)(2 * grid)), stream);
+  return launch2<Big, true>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)grid), stream);
 }

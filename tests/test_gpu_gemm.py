@@ -176,6 +176,19 @@ def test_ragged_shapes_and_epilogues(epi, M, N, K):
     check_gemm_spec(spec, full=True)
 
 
+@pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
+def test_big_tile_ragged_edges(epi):
+    # enough 256 x 256 tiles (17 x 17) that the big-tile kernel runs, with a
+    # 48-row and an 80-column tail; sampled rows / columns include every tile
+    # boundary and the last row and column
+    M, N, K = 4096 + 48, 4096 + 80, 256
+    spec = workloads.GemmSpec("big_ragged", M, N, K, "e4m3", "e4m3", epi,
+                              workloads.TensorSpec(53, M, (M, K), 1.0, 0.01),
+                              workloads.TensorSpec(54, N, (N, K), 0.05),
+                              bias=None if epi == "none" else workloads.TensorSpec(55, N, (N,), 0.5))
+    check_gemm_spec(spec, full=False)
+
+
 def test_fp32_output_and_canaries():
     M, N, K = 272, 304, 512
     a = workloads.normal_bf16(60, 0, (M, K), 1.0)
