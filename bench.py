@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--stats-from", metavar="DIR",
                    help="no GPU: turn a rocprofv3 --kernel-trace --stats run into profiles/")
     p.add_argument("--command", default="", help="the profiling command, recorded with --stats-from")
+    p.add_argument("--no-graph", action="store_true",
+                   help="launch every op from Python instead of replaying captured HIP graphs")
     return p.parse_args()
 
 
@@ -306,14 +308,14 @@ def _per_op(dispatches, record):
     """Average the counter over each op's launches (an op's kernels summed).
 
     The library's dispatches come in the order bench.py made them: the
-    (warmup + steps) passes over the step's ops, then, op by op, the
-    attribution launches (1 + steps each)."""
+    (pre + warmup + steps) passes over the step's ops, then, op by op, its
+    attribution launches."""
     ours = [(n, v) for n, v in dispatches if "temx::" in n]
     order = []
-    for _ in range(record["warmup"] + record["steps"]):
+    for _ in range(record.get("pre", 0) + record["warmup"] + record["steps"]):
         order += [op for op in record["ops"]]
-    for op in record["ops"]:
-        order += [op] * (1 + record["steps"])
+    for op, n in zip(record["ops"], record.get("attr_launches", [1 + record["steps"]] * len(record["ops"]))):
+        order += [op] * n
     expected = sum(len(op["kernels"]) for op in order)
     if len(ours) != expected:
         raise SystemExit(f"expected {expected} library dispatches, found {len(ours)}")
@@ -452,10 +454,34 @@ def main():
     stream = torch.cuda.current_stream()
     nops = len(step.ops)
 
-    def run(i):
+    def run_eager(i):
         r = i % ROTATE
         for _, _, fn, _, _ in step.ops:
             fn(r)
+
+    # Eager steps first (the library's cached device queries happen here),
+    # then, unless --no-graph, one HIP graph per buffer rotation holding the
+    # step's launches: replaying them removes the host-side launch cost from
+    # the timed region, which matters for the small kernels.
+    pre = 2 * ROTATE
+    for i in range(pre):
+        run_eager(i)
+    torch.cuda.synchronize()
+    graphs = None
+    if not args.no_graph:
+        graphs = []
+        for r in range(ROTATE):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _, _, fn, _, _ in step.ops:
+                    fn(r)
+            graphs.append(g)
+
+    def run(i):
+        if graphs is None:
+            run_eager(i)
+        else:
+            graphs[i % ROTATE].replay()
 
     for i in range(args.warmup):
         run(i)
@@ -468,19 +494,35 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     # Per-op attribution, right after the timed region on the same stream: each
-    # op launched `steps` times back to back (rotating buffers as in the step),
-    # bracketed by two HIP events, so no marker sits between its launches.
+    # op launched back to back over the rotating buffers (a captured graph of
+    # its ROTATE launches, replayed), bracketed by two HIP events, so no
+    # marker sits between its launches.
+    reps = max(1, args.steps // ROTATE)
     kernels = []
+    attr_launches = []
     for label, kind, fn, flops, nbytes in step.ops:
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        fn(0)
-        e0.record(stream)
-        for i in range(args.steps):
-            fn(i % ROTATE)
-        e1.record(stream)
+        if graphs is None:
+            fn(0)
+            e0.record(stream)
+            for i in range(reps * ROTATE):
+                fn(i % ROTATE)
+            e1.record(stream)
+            attr_launches.append(1 + reps * ROTATE)
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for r in range(ROTATE):
+                    fn(r)
+            g.replay()
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            attr_launches.append((1 + reps) * ROTATE)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
+        ms = e0.elapsed_time(e1) / (reps * ROTATE)
         ent = {"name": label, "kind": kind, "avg_ms": round(ms, 5)}
         if flops:
             ent["tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
@@ -520,6 +562,7 @@ def main():
         "dtype": "fp8",
         "data": "synthetic (seeded N(0, sigma) bf16, outlier columns per config)",
         "config": {"workload": w.name, "gemm_flops_per_step": step.flops, "parallelism": "single GPU",
+                   "launch": "eager" if graphs is None else "HIP graph replay (one graph per buffer rotation)",
                    "arithmetic": "MXFP8 (E4M3/E5M2 codes, E8M0 block scales) products, fp32 accumulate",
                    "rotating_buffers": ROTATE},
         "roofline": roof,
@@ -538,7 +581,8 @@ def main():
     if args.record_ops:
         summary = {k: v for k, v in out.items() if k != "kernels"}
         rdir = os.path.relpath(os.path.dirname(os.path.abspath(args.record_ops)), ROOT)
-        rec = {"workload": w.name, "warmup": args.warmup, "steps": args.steps,
+        rec = {"workload": w.name, "pre": pre, "warmup": args.warmup, "steps": args.steps,
+               "attr_launches": attr_launches,
                "calibration_copies": 3 if args.copy_calibration else 0,
                "command": f"timeout -s KILL 120 rocprofv3 --pmc PMC --output-format csv -d {rdir} -o run -- "
                           f"python bench.py --workload {args.workload} --steps {args.steps} "
