@@ -460,14 +460,18 @@ def main():
             fn(r)
 
     # Eager steps first (the library's cached device queries happen here),
-    # then, unless --no-graph, one HIP graph per buffer rotation holding the
-    # step's launches: replaying them removes the host-side launch cost from
-    # the timed region, which matters for the small kernels.
+    # then, unless --no-graph, HIP graphs of the step's launches: one per
+    # buffer rotation, and one of all ROTATE rotations in order.  Replaying
+    # them removes the host-side launch cost from the timed region, which
+    # matters for the small kernels; a graph replay itself costs a few us
+    # (measured: ~1.2 us per kernel with 4-kernel graphs, none with 48), so
+    # whole rotation cycles replay as one graph.
     pre = 2 * ROTATE
     for i in range(pre):
         run_eager(i)
     torch.cuda.synchronize()
     graphs = None
+    graph_cycle = None
     if not args.no_graph:
         graphs = []
         for r in range(ROTATE):
@@ -476,27 +480,38 @@ def main():
                 for _, _, fn, _, _ in step.ops:
                     fn(r)
             graphs.append(g)
+        graph_cycle = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_cycle):
+            for r in range(ROTATE):
+                for _, _, fn, _, _ in step.ops:
+                    fn(r)
 
-    def run(i):
-        if graphs is None:
-            run_eager(i)
-        else:
-            graphs[i % ROTATE].replay()
+    def run_steps(first, n):
+        # exactly n steps, the i-th on buffer rotation i % ROTATE
+        i = first
+        while i < first + n:
+            if graphs is None:
+                run_eager(i)
+                i += 1
+            elif i % ROTATE == 0 and first + n - i >= ROTATE:
+                graph_cycle.replay()
+                i += ROTATE
+            else:
+                graphs[i % ROTATE].replay()
+                i += 1
 
-    for i in range(args.warmup):
-        run(i)
+    run_steps(0, args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        run(args.warmup + i)
+    run_steps(args.warmup, args.steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     # Per-op attribution, right after the timed region on the same stream: each
-    # op launched back to back over the rotating buffers (a captured graph of
-    # its ROTATE launches, replayed), bracketed by two HIP events, so no
-    # marker sits between its launches.
+    # op launched back to back over the rotating buffers (one captured graph of
+    # all its timed launches, replayed once to warm up and once timed),
+    # bracketed by two HIP events, so no marker sits between its launches.
     reps = max(1, args.steps // ROTATE)
     kernels = []
     attr_launches = []
@@ -513,14 +528,13 @@ def main():
         else:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for r in range(ROTATE):
-                    fn(r)
+                for i in range(reps * ROTATE):
+                    fn(i % ROTATE)
             g.replay()
             e0.record(stream)
-            for _ in range(reps):
-                g.replay()
+            g.replay()
             e1.record(stream)
-            attr_launches.append((1 + reps) * ROTATE)
+            attr_launches.append(2 * reps * ROTATE)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / (reps * ROTATE)
         ent = {"name": label, "kind": kind, "avg_ms": round(ms, 5)}
@@ -562,7 +576,7 @@ def main():
         "dtype": "fp8",
         "data": "synthetic (seeded N(0, sigma) bf16, outlier columns per config)",
         "config": {"workload": w.name, "gemm_flops_per_step": step.flops, "parallelism": "single GPU",
-                   "launch": "eager" if graphs is None else "HIP graph replay (one graph per buffer rotation)",
+                   "launch": "eager" if graphs is None else "HIP graph replay (a graph per cycle of the 4 buffer rotations)",
                    "arithmetic": "MXFP8 (E4M3/E5M2 codes, E8M0 block scales) products, fp32 accumulate",
                    "rotating_buffers": ROTATE},
         "roofline": roof,

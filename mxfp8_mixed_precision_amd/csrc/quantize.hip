@@ -49,9 +49,15 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rowwise_kernel(
 
 // Columnwise (transposed), without an LDS round trip for the input.
 //
-// A workgroup of 8 waves covers 128 columns; wave w takes the 64-column
-// strip (w & 1) and the row range (w >> 1) of the workgroup's 4 consecutive
-// row ranges, each `cpw` chunks of 128 rows.  Lane (rq, g) = (lane >> 3,
+// A workgroup of 8 waves covers 256 columns, as 4 strips of 64 columns x 2
+// row groups: wave w takes strip w % 4 and row group w / 4.  The workgroup
+// spans cpw x 256 rows; its chunk c covers rows 256 c .. 256 c + 255, and row
+// group r takes rows 128 r .. 128 r + 127 of each chunk, so the 8 waves work
+// on one 256 x 256 tile at a time.  At any moment a workgroup thus reads
+// 512-byte runs of 256 consecutive rows (measured on MI355X, 8192^2: 36 us,
+// against 38-40 us for 128 columns x 4 row groups of 256 consecutive rows
+// each; the backward shapes 14336 x 4096 and 4096 x 14336 gain 8-10% too).
+// Lane (rq, g) = (lane >> 3,
 // lane & 7) loads rows 4rq..4rq+3 of each 32-row block straight into
 // registers, 8 columns (16 bytes) each, so every load instruction still
 // covers eight whole 128-byte row segments.  The block amax of a column is
@@ -68,16 +74,19 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rowwise_kernel(
 // are ordinary (cached) ones: measured on gfx950, streaming stores of this
 // scattered line pattern are ~10% slower, while the input loads, read once,
 // are streaming.  The
-// E8M0 codes of the workgroup's 128 columns collect in LDS and leave after
-// one barrier as runs of up to 32 bytes per column (a partial line costs a
-// full 64-byte memory write; shorter runs would cost more).
+// E8M0 codes of the workgroup's 256 columns collect in LDS and leave after
+// one barrier as runs of 8 or 16 bytes per column (cpw 1 or 2).  Staging a
+// whole 512-row tile in a workgroup-shared LDS buffer, so that every output
+// row is written as one 512-byte run, measured no faster.
 constexpr int kColWaves = 8;
 constexpr int kColThreads = 64 * kColWaves;
 constexpr int kColStrip = 64;          // columns per wave
-constexpr int kColWgCols = 2 * kColStrip;
+constexpr int kColStrips = 4;          // column strips per workgroup
+constexpr int kColGroups = kColWaves / kColStrips;  // row groups per workgroup
+constexpr int kColWgCols = kColStrips * kColStrip;
 constexpr int kColChunk = 128;         // rows per staged chunk
 constexpr int kColMaxChunks = 2;       // chunks per wave at most
-constexpr int kColScaleRun = 4 * kColMaxChunks * 4;  // scale codes per column and workgroup, at most
+constexpr int kColScaleRun = kColGroups * kColMaxChunks * 4;  // scale codes per column and workgroup, at most
 
 __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a), __builtin_bit_cast(u16x2, b)));
@@ -111,24 +120,27 @@ __global__ __launch_bounds__(kColThreads) void quantize_colwise_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t stage_all[kColWaves][kColStrip * kColChunk];
   __shared__ uint8_t scodes[kColWgCols * kColScaleRun];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int cs = wave & 1, rg = wave >> 1;
+  const int cs = wave % kColStrips, rg = wave / kColStrips;
   const int rq = lane >> 3, g = lane & 7;
-  const int64_t wg_rows = 4 * (int64_t)cpw * kColChunk;
+  const int64_t wg_rows = kColGroups * (int64_t)cpw * kColChunk;
   const int64_t R0 = (int64_t)blockIdx.y * wg_rows;
   const int64_t c0 = (int64_t)blockIdx.x * kColWgCols;
-  const int64_t r0w = R0 + (int64_t)rg * cpw * kColChunk;  // first row of this wave
   const int64_t c0w = c0 + kColStrip * cs;                   // first column of this wave
   const int64_t gcol = c0w + 8 * g;                           // this lane's 8 columns
   const bool col_ok = gcol < cols;
-  int nblocks = (int)max((int64_t)0, min((int64_t)cpw * 4, (rows - r0w) / 32));
+  // first row of this wave's part of chunk c; the wave's blocks k = 4 c + b
+  // (b < 4) run up the rows, so the valid ones are a prefix
+  auto chunk_row = [&](int c) { return R0 + (int64_t)c * kColGroups * kColChunk + (int64_t)rg * kColChunk; };
+  int nblocks = 0;
+  for (int k = 0; k < cpw * 4; ++k) nblocks += (chunk_row(k >> 2) + 32 * (k & 3) + 32 <= rows) ? 1 : 0;
   if (c0w >= cols) nblocks = 0;
   uint8_t* stage = stage_all[wave];
-  const int64_t lane_row = r0w + 4 * rq;
 
   auto load = [&](u32x4 (&v)[4], int k) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      v[i] = col_ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (lane_row + 32 * k + i) * cols + gcol))
+      v[i] = col_ok ? __builtin_nontemporal_load(
+                          reinterpret_cast<const u32x4*>(x + (chunk_row(k >> 2) + 32 * (k & 3) + 4 * rq + i) * cols + gcol))
                     : u32x4{0, 0, 0, 0};
   };
 
@@ -154,11 +166,12 @@ __global__ __launch_bounds__(kColThreads) void quantize_colwise_kernel(
       *reinterpret_cast<uint32_t*>(&stage[(8 * g + j) * kColChunk + row_off]) = q;
       my_code = rq == j ? code : my_code;
     }
-    scodes[(kColStrip * cs + 8 * g + rq) * kColScaleRun + rg * cpw * 4 + k] = (uint8_t)my_code;
+    scodes[(kColStrip * cs + 8 * g + rq) * kColScaleRun + (k >> 2) * kColGroups * 4 + rg * 4 + (k & 3)] =
+        (uint8_t)my_code;
     if ((k & 3) == 3 || k == nblocks - 1) {
       // drain the chunk: 64 output rows, 16-byte pieces, 8 lanes per 128-byte segment
       const int valid = 32 * ((k & 3) + 1);
-      const int64_t out_row0 = r0w + kColChunk * (k >> 2);
+      const int64_t out_row0 = chunk_row(k >> 2);
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's stage writes have landed
       asm volatile("" ::: "memory");
 #pragma unroll
@@ -194,12 +207,14 @@ __global__ __launch_bounds__(kColThreads) void quantize_colwise_kernel(
   }
 }
 
-// Chunks of 128 rows per colwise wave: two (32-byte scale runs) when the grid
-// still has two workgroups per CU, else one.
+// Chunks of 128 rows per colwise wave: two (16-byte scale runs per column)
+// when that grid still has 1.5 workgroups per CU, else one.  Measured on
+// MI355X: 8192^2 36.0 vs 36.4 us, 14336 x 4096 33.5 vs 35.3 us, 4096 x 14336
+// 34.4 vs 35.3 us with two; 4096^2 12.6 vs 17.3 us with one.
 int colwise_chunks_per_wave(int64_t rows, int64_t cols) {
   const int64_t col_tiles = (cols + kColWgCols - 1) / kColWgCols;
-  const int64_t row_tiles_2 = (rows + 4 * 2 * kColChunk - 1) / (4 * 2 * kColChunk);
-  return col_tiles * row_tiles_2 >= 2 * (int64_t)device_cu_count() ? 2 : 1;
+  const int64_t row_tiles_2 = (rows + kColGroups * 2 * kColChunk - 1) / (kColGroups * 2 * kColChunk);
+  return 2 * col_tiles * row_tiles_2 >= 3 * (int64_t)device_cu_count() ? 2 : 1;
 }
 
 template <int FMT>
@@ -215,7 +230,7 @@ te_status launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, te_qdir
   }
   if (dir & TE_COLWISE) {
     const int cpw = colwise_chunks_per_wave(rows, cols);
-    const int64_t rows_per_wg = 4 * (int64_t)cpw * kColChunk;
+    const int64_t rows_per_wg = kColGroups * (int64_t)cpw * kColChunk;
     dim3 grid((unsigned)((cols + kColWgCols - 1) / kColWgCols), (unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
     hipLaunchKernelGGL(quantize_colwise_kernel<FMT>, grid, dim3(kColThreads), 0, stream, x, q_col, s_col, rows, cols,
                        cpw);
