@@ -12,7 +12,8 @@ Sources (web pages, cited by title and section):
 * "Transformer Engine On ROCm and AMDGPU" (ROCm/TransformerEngine README):
   sections "MXFP8 support on ROCm (gfx95x only)", "Blockwise FP8 GEMM
   support on ROCm" (scales cast to E8M0, power of two), "Two-stage amax
-  Kernel".
+  Kernel", "Experimental Triton Kernels on ROCm" (cast_transpose and
+  cast_transpose_bgrad).
 * "Getting Started" (Transformer Engine JAX quickstart): the baseline MLP
   (GELU with the tanh approximation) and "Enabling Quantization" (HYBRID
   format, DelayedScaling with margin 0).
@@ -38,6 +39,7 @@ hand-worked golden blocks).  No function is parity-unpinned.
 from .formats import E4M3, E5M2, FP8Format, decode, encode, e8m0_decode, format_by_name
 from .mx import block_scale_code, quantize_rowwise, quantize_colwise, dequantize
 from .current_scaling import amax, current_scale, cast_current_scaling
+from .bgrad import column_sums, column_abs_sums
 from .gemm import mx_gemm, gelu_tanh, epilogue, grouped_mx_gemm, within_tolerance, tolerance_bound
 
 __all__ = [
