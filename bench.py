@@ -42,7 +42,8 @@ ROTATE = 4                     # copies of each bandwidth-bound input / output
 # kernels each kind of op launches, in order (names as the profiler reports them)
 KERNELS = {"quantize_row": ["quantize_rowwise_kernel"], "quantize_col": ["quantize_colwise_kernel"],
            "gemm": ["mx_gemm_kernel"], "grouped": ["mx_grouped_gemm_kernel"],
-           "cast": ["amax_partial_kernel", "amax_final_kernel", "cast_kernel"]}
+           "cast": ["amax_partial_kernel", "amax_final_kernel", "cast_kernel"],
+           "quantize_bgrad": ["quantize_colwise_kernel", "bgrad_final_kernel"]}
 CALIBRATION_BYTES = 512 << 20  # one device-to-device copy of this many bytes reads and writes it once
 
 
@@ -52,7 +53,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--workload", default="square_8192",
-                   choices=["square_8192", "decoder_fwd", "hybrid_bwd", "moe_grouped", "tiny"])
+                   choices=["square_8192", "decoder_fwd", "hybrid_bwd", "hybrid_bwd_fused", "moe_grouped", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, copy a 512 MiB buffer 3 times (counter calibration)")
@@ -147,6 +148,21 @@ def build_step(workload, torch, te, workloads):
     for spec, fmt, direction in w.quantize:
         add_quantize(spec, fmt, direction, f"quantize_{direction}_{spec.shape[0]}x{spec.shape[1]}_t{spec.tensor_id}")
 
+    for spec, fmt in w.fused_bgrad:
+        src = rotated(spec.make())
+        rows, cols = spec.shape
+        rbufs, cbufs = qbufs(rows, cols, "row"), qbufs(rows, cols, "col")
+        bgrads = [torch.empty(cols, dtype=torch.float32, device=dev) for _ in range(ROTATE)]
+        ws = torch.empty(te.te_mxfp8_quantize_bgrad_workspace_size(rows, cols), dtype=torch.uint8, device=dev)
+
+        def fn(r, src=src, rbufs=rbufs, cbufs=cbufs, bgrads=bgrads, ws=ws, fmt=fmt):
+            te.te_mxfp8_quantize_bgrad(src[r], fmt, rbufs[r][0], rbufs[r][1], cbufs[r][0], cbufs[r][1], bgrads[r], ws)
+        # read bf16 once; write both copies, their scales and the fp32 column sums
+        nbytes = rows * cols * (2 + 2 + 2 / 32) + 4 * cols
+        step.add(f"quantize_both_bgrad_{rows}x{cols}", "quantize", fn, 0.0, nbytes, KERNELS["quantize_bgrad"])
+        quantized[(spec, "row", fmt)] = rbufs
+        quantized[(spec, "col", fmt)] = cbufs
+
     for g in w.gemms:
         qa = add_quantize(g.a_src, g.fmt_a, g.a_dir, f"quantize_{g.a_dir}_{g.name}_A")
         qb = add_quantize(g.b_src, g.fmt_b, g.b_dir, f"quantize_{g.b_dir}_{g.name}_B")
@@ -239,6 +255,15 @@ def cpu_baseline(workload, workloads):
     for spec, fmt, direction in w.quantize:
         if any(spec in (g.a_src, g.b_src) for g in gemms):
             q_elems_full += spec.shape[0] * spec.shape[1]  # the other direction of an operand already timed
+    b_time = b_elems_s = b_elems_full = 0.0
+    for spec, fmt in w.fused_bgrad:
+        x = spec.make()
+        sr = min(S, spec.shape[0])
+        t0 = time.perf_counter()
+        oracle.column_sums(x[:sr])
+        b_time += time.perf_counter() - t0
+        b_elems_s += sr * spec.shape[1]
+        b_elems_full += spec.shape[0] * spec.shape[1]
     for g in w.grouped:
         counts = workloads.moe_counts(g.total_m, g.experts)
         a = g.a_src.make()
@@ -259,6 +284,7 @@ def cpu_baseline(workload, workloads):
         g_flops_s += 2.0 * sm * g.N * g.K
         g_flops_full += 2.0 * g.total_m * g.N * g.K
     est = q_time * (q_elems_full / max(q_elems_s, 1)) + g_time * (g_flops_full / max(g_flops_s, 1))
+    est += b_time * (b_elems_full / max(b_elems_s, 1))
     return {"value": g_flops_full / est / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"oracle (numpy fp64) on the first rows of each operand (up to {S}): quantize "
                        f"{q_elems_s:.3g} elements in {q_time:.2f} s (1 thread), GEMM {g_flops_s:.3g} flop in "

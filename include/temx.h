@@ -5,7 +5,8 @@
  * Engine's Linear / LayerNormMLP modules on ROCm:
  *   - per-tensor amax (two-stage, no atomics) and the current-scaling cast;
  *   - MXFP8 1-D block quantization of bf16 tensors, rowwise and transposed
- *     columnwise (32-element blocks, one E8M0 power-of-two scale per block);
+ *     columnwise (32-element blocks, one E8M0 power-of-two scale per block),
+ *     and the fused cast-transpose with bias gradient;
  *   - the MXFP8 x MXFP8 -> fp32-accumulate GEMM with bias, GELU(tanh) and
  *     GELU-aux (pre-activation) epilogues;
  *   - a single-launch grouped (MoE) variant over ragged expert row counts.
@@ -15,7 +16,8 @@
  *              README): "MXFP8 support on ROCm (gfx95x only)", "Blockwise FP8
  *              GEMM support on ROCm" (E8M0 power-of-two scales), "Two-stage
  *              amax Kernel", "Experimental Triton Kernels on ROCm"
- *              (cast_transpose), "Grouped GEMM using CK_Tile".
+ *              (cast_transpose, cast_transpose_bgrad), "Grouped GEMM using
+ *              CK_Tile".
  *   [TE-JAX]   "Getting Started" (Transformer Engine JAX quickstart): GELU
  *              with the tanh approximation; "Enabling Quantization" (HYBRID).
  *   [FP8-WF]   "Workflow: NVIDIA TransformerEngine FP8 Training Quickstart",
@@ -126,11 +128,36 @@ te_status te_fp8_cast_current_scaling(const uint16_t* x, int64_t n, te_dtype fmt
  *           transposed; needs rows % 32 == 0 and cols % 8 == 0.
  *           q_col uint8 [cols, rows], s_col uint8 [cols, rows/32]
  *   Output pointers of a direction not requested must be NULL.
+ *   TE_BOTH makes both copies in one pass (x is read once).
  *   rows, cols >= 0; an empty tensor enqueues nothing.
  */
 te_status te_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t cols, te_dtype fmt, te_qdir dir,
                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
                             hipStream_t stream);
+
+/*
+ * Cast-transpose with bias gradient, the fused kernel that [ROCm-TE]
+ * "Experimental Triton Kernels on ROCm" names cast_transpose_bgrad: one pass
+ * over an output gradient x = dY [rows = tokens, cols = features] writes
+ * both MXFP8 copies, exactly as te_mxfp8_quantize(dir = TE_BOTH), and
+ *   bgrad[c] = sum over r of x[r, c]
+ * (the gradient of the bias of the Linear whose output gradient is x),
+ * accumulated in fp32 in a fixed order, so the result is deterministic.
+ *   x           bf16 [rows, cols]; rows % 32 == 0 and cols % 32 == 0
+ *   fmt         TE_E4M3 or TE_E5M2 (E5M2 for gradients in HYBRID)
+ *   q_row, s_row, q_col, s_col   as te_mxfp8_quantize with TE_BOTH
+ *   bgrad       [cols], bgrad_dtype TE_FP32 (float) or TE_BF16 (round to
+ *               nearest even of the fp32 sum); aligned to its type
+ *   workspace   device scratch of at least
+ *               te_mxfp8_quantize_bgrad_workspace_size(rows, cols) bytes,
+ *               4-byte aligned (fp32 partial sums per workgroup row tile)
+ * rows == 0 writes zeros to bgrad; cols == 0 enqueues nothing.
+ */
+size_t te_mxfp8_quantize_bgrad_workspace_size(int64_t rows, int64_t cols);
+te_status te_mxfp8_quantize_bgrad(const uint16_t* x, int64_t rows, int64_t cols, te_dtype fmt,
+                                  uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                                  void* bgrad, te_dtype bgrad_dtype, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /*
  * MXFP8 GEMM, "TN" ([HK-PR] description and review threads):

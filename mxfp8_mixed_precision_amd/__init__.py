@@ -37,6 +37,9 @@ _SIGS = {
     "te_amax_reduce": (ctypes.c_int, [_vp, _i64, _vp, _vp, _sz, _vp]),
     "te_fp8_cast_current_scaling": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "te_mxfp8_quantize": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]),
+    "te_mxfp8_quantize_bgrad_workspace_size": (_sz, [_i64, _i64]),
+    "te_mxfp8_quantize_bgrad": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
+                                               _vp, _sz, _vp]),
     "te_mxfp8_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
     "te_mxfp8_gemm": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _i64, _i64, _i64,
                                      _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
@@ -106,6 +109,19 @@ def te_mxfp8_quantize(x, fmt, direction, q_row=None, s_row=None, q_col=None, s_c
         _ptr(x), rows, cols, _fmt(fmt), d, _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(stream)))
 
 
+def te_mxfp8_quantize_bgrad_workspace_size(rows: int, cols: int) -> int:
+    return int(_lib.te_mxfp8_quantize_bgrad_workspace_size(int(rows), int(cols)))
+
+
+def te_mxfp8_quantize_bgrad(x, fmt, q_row, s_row, q_col, s_col, bgrad, workspace, stream=None) -> None:
+    rows, cols = x.shape
+    b_dtype = TE_FP32 if bgrad.dtype == torch.float32 else TE_BF16
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("te_mxfp8_quantize_bgrad", _lib.te_mxfp8_quantize_bgrad(
+        _ptr(x), rows, cols, _fmt(fmt), _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _ptr(bgrad), b_dtype,
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def te_mxfp8_gemm_workspace_size(M: int, N: int, K: int) -> int:
     return int(_lib.te_mxfp8_gemm_workspace_size(M, N, K))
 
@@ -151,6 +167,21 @@ def mxfp8_quantize(x, fmt="e4m3", direction="row", stream=None):
         s_col = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
     te_mxfp8_quantize(x, fmt, d, q_row, s_row, q_col, s_col, stream)
     return q_row, s_row, q_col, s_col
+
+
+def mxfp8_quantize_bgrad(x, fmt="e5m2", bgrad_dtype=torch.float32, stream=None):
+    """bf16 [rows, cols] output gradient -> (q_row, s_row, q_col, s_col, bgrad), one pass; bgrad [cols] is
+    the column sum of x (fp32 accumulation), as float32 or bfloat16."""
+    rows, cols = x.shape
+    dev = x.device
+    q_row = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    s_row = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+    q_col = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    s_col = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
+    bgrad = torch.empty(cols, dtype=bgrad_dtype, device=dev)
+    ws = torch.empty(max(te_mxfp8_quantize_bgrad_workspace_size(rows, cols), 16), dtype=torch.uint8, device=dev)
+    te_mxfp8_quantize_bgrad(x, fmt, q_row, s_row, q_col, s_col, bgrad, ws, stream)
+    return q_row, s_row, q_col, s_col, bgrad
 
 
 def amax(x, stream=None):

@@ -100,6 +100,15 @@ __device__ __forceinline__ uint32_t max_over_row_quads(uint32_t v, int lane) {
   return v;
 }
 
+// sum over the 8 lanes l, l^8, l^16, ..., l^56 in a fixed butterfly order
+// (a + b == b + a in fp32, so every lane of the group ends with the same bits)
+__device__ __forceinline__ float sum_over_row_quads(float v, int lane) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));   // lane ^ 8
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));                // lane ^ 16
+  v += __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(v)));      // lane ^ 32
+  return v;
+}
+
 template <int FMT>
 __device__ __forceinline__ uint32_t cvt4_scaled(uint32_t rows01, uint32_t rows23, float scale) {
   v2s r = {0, 0};
@@ -113,9 +122,20 @@ __device__ __forceinline__ uint32_t cvt4_scaled(uint32_t rows01, uint32_t rows23
   return saturate_bytes<FMT>(__builtin_bit_cast(uint32_t, r));
 }
 
-template <int FMT>
-__global__ __launch_bounds__(kColThreads) void quantize_colwise_kernel(
+// ROW: the same pass also writes the rowwise copy (both directions from one
+// read of x).  Lane (rq, g) holds, for each of its 4 rows, 8 consecutive
+// columns, so the 4 lanes g = 4h .. 4h+3 (a DPP quad) hold one row's 32-block:
+// its amax is a quad max, and each lane encodes and stores its 8 codes.
+// These are plain stores: a wave writes 64 of each 128-byte line, the wave of
+// the neighbouring strip the other 64, and L2 merges them.
+// BGRAD: also the column sums of x in fp32 (the bias gradient when x is an
+// output gradient), per workgroup into ws[blockIdx.y][cols]: each lane adds
+// its 4 rows per block in block order, the 8 lanes of a column combine in a
+// fixed butterfly, then the two row groups in LDS; deterministic.
+template <int FMT, bool ROW, bool BGRAD>
+__global__ __launch_bounds__(kColThreads) __attribute__((amdgpu_waves_per_eu(4))) void quantize_colwise_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ qc, uint8_t* __restrict__ sc,
+    uint8_t* __restrict__ qr, uint8_t* __restrict__ sr, float* __restrict__ ws,
     int64_t rows, int64_t cols, int cpw) {
   __shared__ __attribute__((aligned(16))) uint8_t stage_all[kColWaves][kColStrip * kColChunk];
   __shared__ uint8_t scodes[kColWgCols * kColScaleRun];
@@ -135,6 +155,7 @@ __global__ __launch_bounds__(kColThreads) void quantize_colwise_kernel(
   for (int k = 0; k < cpw * 4; ++k) nblocks += (chunk_row(k >> 2) + 32 * (k & 3) + 32 <= rows) ? 1 : 0;
   if (c0w >= cols) nblocks = 0;
   uint8_t* stage = stage_all[wave];
+  float csum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 
   auto load = [&](u32x4 (&v)[4], int k) {
 #pragma unroll
@@ -145,6 +166,28 @@ __global__ __launch_bounds__(kColThreads) void quantize_colwise_kernel(
   };
 
   auto process = [&](const u32x4 (&v)[4], int k) {
+    if constexpr (ROW) {
+      const int64_t row0 = chunk_row(k >> 2) + 32 * (k & 3) + 4 * rq;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint4 xv = {v[u][0], v[u][1], v[u][2], v[u][3]};
+        const uint32_t code = e8m0_code_from_amax_bits<FMT>(quad_max(absmax_bits8(xv)));
+        const uint2 r = cvt8_scaled<FMT>(xv, e8m0_to_float(code));
+        if (col_ok) {
+          *reinterpret_cast<uint2*>(qr + (row0 + u) * cols + gcol) = r;
+          if ((g & 3) == 0) sr[(row0 + u) * (cols / 32) + gcol / 32] = (uint8_t)code;
+        }
+      }
+    }
+    if constexpr (BGRAD) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          csum[2 * d] += bf16_bits_to_float(v[u][d] & 0xFFFFu);
+          csum[2 * d + 1] += bf16_bits_to_float(v[u][d] >> 16);
+        }
+    }
     uint32_t m[4];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -205,6 +248,37 @@ __global__ __launch_bounds__(kColThreads) void quantize_colwise_kernel(
     const int c = idx / nbw, b = idx - c * nbw;
     if (c0 + c < cols) sc[(c0 + c) * sstride + R0 / 32 + b] = scodes[c * kColScaleRun + b];
   }
+
+  if constexpr (BGRAD) {
+    __shared__ float group_sums[kColGroups][kColWgCols];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) csum[j] = sum_over_row_quads(csum[j], lane);
+    if (rq == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) group_sums[rg][kColStrip * cs + 8 * g + j] = csum[j];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < kColWgCols; c += kColThreads) {
+      float t = group_sums[0][c];
+#pragma unroll
+      for (int r = 1; r < kColGroups; ++r) t += group_sums[r][c];
+      if (c0 + c < cols) ws[(int64_t)blockIdx.y * cols + c0 + c] = t;
+    }
+  }
+}
+
+// bgrad[c] = sum over the workgroup row tiles t (in order) of ws[t][c].
+template <int OUT>
+__global__ __launch_bounds__(256) void bgrad_final_kernel(const float* __restrict__ ws, int tiles, int64_t cols,
+                                                          void* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= cols) return;
+  float s = 0.f;
+  for (int t = 0; t < tiles; ++t) s += ws[(int64_t)t * cols + c];
+  if constexpr (OUT == TE_FP32)
+    static_cast<float*>(out)[c] = s;
+  else
+    static_cast<uint16_t*>(out)[c] = __builtin_bit_cast(uint16_t, (__bf16)s);
 }
 
 // Chunks of 128 rows per colwise wave: two (16-byte scale runs per column)
@@ -217,9 +291,30 @@ int colwise_chunks_per_wave(int64_t rows, int64_t cols) {
   return 2 * col_tiles * row_tiles_2 >= 3 * (int64_t)device_cu_count() ? 2 : 1;
 }
 
+// The colwise kernel over [rows, cols] (rows, cols > 0); `tiles` receives
+// the number of workgroup row tiles (the rows of the bgrad workspace).
+template <int FMT, bool ROW, bool BGRAD>
+te_status launch_colwise(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q_row, uint8_t* s_row,
+                         uint8_t* q_col, uint8_t* s_col, float* ws, hipStream_t stream, int* tiles) {
+  const int cpw = colwise_chunks_per_wave(rows, cols);
+  const int64_t rows_per_wg = kColGroups * (int64_t)cpw * kColChunk;
+  dim3 grid((unsigned)((cols + kColWgCols - 1) / kColWgCols), (unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
+  if (tiles) *tiles = (int)grid.y;
+  hipLaunchKernelGGL((quantize_colwise_kernel<FMT, ROW, BGRAD>), grid, dim3(kColThreads), 0, stream, x, q_col, s_col,
+                     q_row, s_row, ws, rows, cols, cpw);
+  return launch_status();
+}
+
+// Fewest rows a colwise workgroup covers (one chunk per wave): the bgrad
+// workspace is sized for the largest number of row tiles.
+constexpr int64_t kColMinWgRows = (int64_t)kColGroups * kColChunk;
+
 template <int FMT>
 te_status launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, te_qdir dir, uint8_t* q_row,
                           uint8_t* s_row, uint8_t* q_col, uint8_t* s_col, hipStream_t stream) {
+  // both directions: one pass, x read once
+  if (dir == TE_BOTH) return launch_colwise<FMT, true, false>(x, rows, cols, q_row, s_row, q_col, s_col, nullptr,
+                                                              stream, nullptr);
   if (dir & TE_ROWWISE) {
     const int64_t nchunks = rows * cols / 8;
     const int64_t per_block = (int64_t)kRowThreads * kRowUnroll;
@@ -228,14 +323,8 @@ te_status launch_quantize(const uint16_t* x, int64_t rows, int64_t cols, te_qdir
                        reinterpret_cast<const uint4*>(x), reinterpret_cast<uint2*>(q_row), s_row, nchunks);
     if (launch_status() != TE_OK) return TE_ERR_HIP;
   }
-  if (dir & TE_COLWISE) {
-    const int cpw = colwise_chunks_per_wave(rows, cols);
-    const int64_t rows_per_wg = kColGroups * (int64_t)cpw * kColChunk;
-    dim3 grid((unsigned)((cols + kColWgCols - 1) / kColWgCols), (unsigned)((rows + rows_per_wg - 1) / rows_per_wg));
-    hipLaunchKernelGGL(quantize_colwise_kernel<FMT>, grid, dim3(kColThreads), 0, stream, x, q_col, s_col, rows, cols,
-                       cpw);
-    if (launch_status() != TE_OK) return TE_ERR_HIP;
-  }
+  if (dir & TE_COLWISE) return launch_colwise<FMT, false, false>(x, rows, cols, nullptr, nullptr, q_col, s_col, nullptr,
+                                                                stream, nullptr);
   return TE_OK;
 }
 
@@ -263,4 +352,45 @@ extern "C" te_status te_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t 
   TE_REQUIRE(!col || aligned16(q_col), TE_ERR_ALIGN);
   return fmt == TE_E4M3 ? launch_quantize<TE_E4M3>(x, rows, cols, dir, q_row, s_row, q_col, s_col, stream)
                         : launch_quantize<TE_E5M2>(x, rows, cols, dir, q_row, s_row, q_col, s_col, stream);
+}
+
+extern "C" size_t te_mxfp8_quantize_bgrad_workspace_size(int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return 0;
+  const int64_t tiles = (rows + kColMinWgRows - 1) / kColMinWgRows;
+  return (size_t)(tiles * cols) * sizeof(float);
+}
+
+extern "C" te_status te_mxfp8_quantize_bgrad(const uint16_t* x, int64_t rows, int64_t cols, te_dtype fmt,
+                                             uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                                             void* bgrad, te_dtype bgrad_dtype, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+  TE_REQUIRE(is_fp8(fmt), TE_ERR_DTYPE);
+  TE_REQUIRE(bgrad_dtype == TE_FP32 || bgrad_dtype == TE_BF16, TE_ERR_DTYPE);
+  TE_REQUIRE(rows >= 0 && cols >= 0, TE_ERR_SHAPE);
+  TE_REQUIRE(rows <= (int64_t)1 << 31 && cols <= (int64_t)1 << 31, TE_ERR_SHAPE);
+  TE_REQUIRE(rows % 32 == 0 && cols % 32 == 0, TE_ERR_SHAPE);
+  if (cols == 0) return TE_OK;
+  TE_REQUIRE(bgrad != nullptr, TE_ERR_NULL);
+  TE_REQUIRE(((uintptr_t)bgrad & (bgrad_dtype == TE_FP32 ? 3u : 1u)) == 0, TE_ERR_ALIGN);
+  if (rows > 0) {
+    TE_REQUIRE(x && q_row && s_row && q_col && s_col && workspace, TE_ERR_NULL);
+    TE_REQUIRE(aligned16(x) && aligned16(q_row) && aligned16(q_col), TE_ERR_ALIGN);
+    TE_REQUIRE(((uintptr_t)workspace & 3u) == 0, TE_ERR_ALIGN);
+    TE_REQUIRE(workspace_bytes >= te_mxfp8_quantize_bgrad_workspace_size(rows, cols), TE_ERR_WORKSPACE);
+  }
+  int tiles = 0;
+  float* ws = static_cast<float*>(workspace);
+  if (rows > 0) {
+    const te_status st =
+        fmt == TE_E4M3
+            ? launch_colwise<TE_E4M3, true, true>(x, rows, cols, q_row, s_row, q_col, s_col, ws, stream, &tiles)
+            : launch_colwise<TE_E5M2, true, true>(x, rows, cols, q_row, s_row, q_col, s_col, ws, stream, &tiles);
+    if (st != TE_OK) return st;
+  }
+  const dim3 grid((unsigned)((cols + 255) / 256));
+  if (bgrad_dtype == TE_FP32)
+    hipLaunchKernelGGL(bgrad_final_kernel<TE_FP32>, grid, dim3(256), 0, stream, ws, tiles, cols, bgrad);
+  else
+    hipLaunchKernelGGL(bgrad_final_kernel<TE_BF16>, grid, dim3(256), 0, stream, ws, tiles, cols, bgrad);
+  return launch_status();
 }

@@ -74,6 +74,41 @@ def test_quantize_validation():
     assert quant(x=None, cols=0) == te.TE_OK
 
 
+def qbgrad(x=P, rows=64, cols=64, fmt=te.TE_E5M2, qr=P2, sr=P3, qc=P2, sc=P3, bgrad=P3, bdt=te.TE_FP32, ws=P,
+           ws_bytes=1 << 20):
+    return L.te_mxfp8_quantize_bgrad(x, rows, cols, fmt, qr, sr, qc, sc, bgrad, bdt, ws, ws_bytes, None)
+
+
+def test_quantize_bgrad_workspace_size():
+    # fp32 partial sums for each 256-row tile of the input
+    assert te.te_mxfp8_quantize_bgrad_workspace_size(0, 64) == 0
+    assert te.te_mxfp8_quantize_bgrad_workspace_size(64, 0) == 0
+    assert te.te_mxfp8_quantize_bgrad_workspace_size(32, 64) == 1 * 64 * 4
+    assert te.te_mxfp8_quantize_bgrad_workspace_size(256, 64) == 1 * 64 * 4
+    assert te.te_mxfp8_quantize_bgrad_workspace_size(288, 64) == 2 * 64 * 4
+    assert te.te_mxfp8_quantize_bgrad_workspace_size(4096, 14336) == 16 * 14336 * 4
+
+
+def test_quantize_bgrad_validation():
+    assert qbgrad(fmt=te.TE_BF16) == te.TE_ERR_DTYPE
+    assert qbgrad(bdt=te.TE_E4M3) == te.TE_ERR_DTYPE
+    assert qbgrad(rows=-32) == te.TE_ERR_SHAPE
+    assert qbgrad(rows=48) == te.TE_ERR_SHAPE          # rows % 32
+    assert qbgrad(cols=40) == te.TE_ERR_SHAPE          # cols % 32
+    assert qbgrad(bgrad=None) == te.TE_ERR_NULL
+    assert qbgrad(bgrad=P3 + 2) == te.TE_ERR_ALIGN     # fp32 output
+    assert qbgrad(x=None) == te.TE_ERR_NULL
+    assert qbgrad(qc=None) == te.TE_ERR_NULL
+    assert qbgrad(sr=None) == te.TE_ERR_NULL
+    assert qbgrad(ws=None) == te.TE_ERR_NULL
+    assert qbgrad(x=BAD) == te.TE_ERR_ALIGN
+    assert qbgrad(qr=BAD) == te.TE_ERR_ALIGN
+    assert qbgrad(ws=P + 2) == te.TE_ERR_ALIGN
+    assert qbgrad(ws_bytes=te.te_mxfp8_quantize_bgrad_workspace_size(64, 64) - 4) == te.TE_ERR_WORKSPACE
+    # no columns: nothing to compute or write
+    assert qbgrad(cols=0, x=None, qr=None, sr=None, qc=None, sc=None, bgrad=None, ws=None) == te.TE_OK
+
+
 def gemm(a=P, sa=P, fa=te.TE_E4M3, b=P, sb=P, fb=te.TE_E4M3, M=256, N=256, K=256, d=P2, dt=te.TE_BF16,
          epi=te.TE_EPI_NONE, bias=None, aux=None):
     return L.te_mxfp8_gemm(a, sa, fa, b, sb, fb, M, N, K, d, dt, epi, bias, aux, None, 0, None)

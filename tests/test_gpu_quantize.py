@@ -183,3 +183,125 @@ def test_quantize_is_deterministic():
     torch.cuda.synchronize()
     for u, v in zip(r1, r2):
         assert torch.equal(u, v)
+
+
+# ---------------------------------------------------------------- fused pass + bias gradient
+
+def bgrad_bound(bits, bgrad_dtype):
+    """|got - ref| allowed for the column sums: fp32 accumulation along a path
+    of at most 32 per-lane additions (4 rows x 8 blocks), 3 butterfly steps, 1
+    across row groups and 1 per 256-row tile, i.e. gamma_d * sum |x| with
+    d + 1 terms; bf16 output adds its rounding (2^-8 relative)."""
+    ref = oracle.column_sums(bits)
+    s = oracle.column_abs_sums(bits)
+    tiles = -(-bits.shape[0] // 256)
+    d = 32 + 3 + 1 + tiles + 1
+    b32 = d * 2.0 ** -24 * s
+    if bgrad_dtype == torch.bfloat16:
+        return ref, 2.0 ** -8 * (np.abs(ref) + b32) + b32
+    return ref, b32
+
+
+def bgrad_host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_quantize_bgrad(bits, fmt, bgrad_dtype, full_oracle=True):
+    x = dev(bits)
+    qr, sr, qc, sc, bg = te().mxfp8_quantize_bgrad(x, fmt, bgrad_dtype)
+    torch.cuda.synchronize()
+    f = oracle.format_by_name(fmt)
+    if full_oracle:
+        oq, os_ = oracle.quantize_rowwise(bits, f)
+        assert np.array_equal(host(sr), os_) and np.array_equal(host(qr), oq), "rowwise copy differs"
+        oq, os_ = oracle.quantize_colwise(bits, f)
+        assert np.array_equal(host(sc), os_) and np.array_equal(host(qc), oq), "colwise copy differs"
+    ref, bound = bgrad_bound(bits, bgrad_dtype)
+    got = bgrad_host(bg)
+    assert np.all(np.abs(got - ref) <= bound), f"bgrad off by up to {np.max(np.abs(got - ref) - bound)} beyond the bound"
+    return qr, sr, qc, sc, bg
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("bgrad_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(32, 32), (64, 96), (288, 224), (4160, 256), (1056, 4128)])
+def test_quantize_bgrad_ragged_shapes(fmt, bgrad_dtype, shape):
+    rows, cols = shape
+    bits = workloads.normal_bf16(78, rows * 1000 + cols, shape, 1e-3, 0.02)
+    check_quantize_bgrad(bits, fmt, bgrad_dtype)
+
+
+def test_quantize_bgrad_integer_columns_exact():
+    # small integers: every partial sum is an integer below 2^24, so any fp32 order is exact
+    rng = np.random.default_rng(79)
+    vals = rng.integers(-64, 65, size=(2048, 320)).astype(np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    _, _, _, _, bg = te().mxfp8_quantize_bgrad(dev(bits), "e5m2", torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(bgrad_host(bg), vals.astype(np.float64).sum(axis=0))
+
+
+def test_quantize_bgrad_single_element_lands_in_its_column():
+    rows, cols = 512, 288
+    bits = np.zeros((rows, cols), np.uint16)
+    for r, c in [(0, 0), (511, 287), (257, 33), (300, 255), (31, 256)]:
+        bits[r, c] = 0x3FC0  # 1.5
+    ref = oracle.column_sums(bits)
+    _, _, _, _, bg = te().mxfp8_quantize_bgrad(dev(bits), "e4m3", torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(bgrad_host(bg), ref)
+
+
+def test_quantize_bgrad_empty_rows_give_zeros():
+    x = torch.zeros((0, 96), dtype=torch.int16, device="cuda")
+    bg = torch.full((96,), 7.0, dtype=torch.float32, device="cuda")
+    te().te_mxfp8_quantize_bgrad(x, "e5m2", None, None, None, None, bg, None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(bg).item() == 0
+
+
+def test_quantize_bgrad_deterministic():
+    bits = workloads.normal_bf16(80, 0, (2048, 1536), 1e-3, 0.0)
+    x = dev(bits)
+    r1 = te().mxfp8_quantize_bgrad(x, "e5m2")
+    r2 = te().mxfp8_quantize_bgrad(x, "e5m2")
+    torch.cuda.synchronize()
+    for u, v in zip(r1, r2):
+        assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("bgrad_dtype", [torch.float32, torch.bfloat16])
+def test_quantize_bgrad_full_size_backward_dy(bgrad_dtype):
+    # the backward pass's output gradient dY [4096, 14336] (E5M2, N(0, 1e-3)):
+    # both copies equal the separate (oracle-pinned) kernels' outputs on the
+    # whole tensor, sampled rows / columns equal the oracle, bgrad within the bound
+    bits = workloads.hybrid_backward().gemms[0].a_src.make()
+    assert bits.shape == (4096, 14336)
+    x = dev(bits)
+    qr, sr, qc, sc, bg = te().mxfp8_quantize_bgrad(x, "e5m2", bgrad_dtype)
+    q2r, s2r, _, _ = te().mxfp8_quantize(x, "e5m2", "row")
+    _, _, q2c, s2c = te().mxfp8_quantize(x, "e5m2", "col")
+    torch.cuda.synchronize()
+    assert torch.equal(qr, q2r) and torch.equal(sr, s2r), "fused rowwise copy differs from the rowwise kernel"
+    assert torch.equal(qc, q2c) and torch.equal(sc, s2c), "fused colwise copy differs from the colwise kernel"
+    f = oracle.E5M2
+    rows = sampled_rows(4096, k=16, seed=5)
+    oq, os_ = oracle.quantize_rowwise(bits[rows], f)
+    assert np.array_equal(host(qr[rows]), oq) and np.array_equal(host(sr[rows]), os_)
+    ref, bound = bgrad_bound(bits, bgrad_dtype)
+    assert np.all(np.abs(bgrad_host(bg) - ref) <= bound)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(8192, 8192), (8288, 8224), (4096, 4096), (14336, 4096)])
+def test_both_directions_fused_equals_separate_full_size(fmt, shape):
+    # TE_BOTH runs the fused pass; it must equal the two single-direction kernels bit for bit
+    rows, cols = shape
+    bits = workloads.normal_bf16(91, rows + 3 * cols, shape, 1.0, 0.01)
+    x = dev(bits)
+    qr, sr, qc, sc = te().mxfp8_quantize(x, fmt, "both")
+    q2r, s2r, _, _ = te().mxfp8_quantize(x, fmt, "row")
+    _, _, q2c, s2c = te().mxfp8_quantize(x, fmt, "col")
+    torch.cuda.synchronize()
+    assert torch.equal(qr, q2r) and torch.equal(sr, s2r)
+    assert torch.equal(qc, q2c) and torch.equal(sc, s2c)

@@ -110,6 +110,9 @@ class Workload:
     grouped: list = field(default_factory=list)
     quantize: list = field(default_factory=list)     # (TensorSpec, fmt, dir) standalone quantizes
     current_scaling: list = field(default_factory=list)  # (TensorSpec, fmt)
+    # (TensorSpec, fmt): both MXFP8 copies and the column sums (bias gradient)
+    # in one pass; the GEMMs that take this tensor use those copies
+    fused_bgrad: list = field(default_factory=list)
 
 
 def tiny() -> Workload:
@@ -164,6 +167,16 @@ def hybrid_backward() -> Workload:
     ], current_scaling=[(x, "e4m3")])
 
 
+def hybrid_backward_fused() -> Workload:
+    """The same FFN backward, with dY's rowwise and columnwise quantization
+    done in one cast-transpose pass that also reduces dY into the bias
+    gradient db[f] = sum_t dY[t, f] (fp32)."""
+    w = hybrid_backward()
+    dy = w.gemms[0].a_src
+    return Workload("hybrid_bwd_fused_4096x4096x14336", gemms=w.gemms, current_scaling=w.current_scaling,
+                    fused_bgrad=[(dy, "e5m2")])
+
+
 def moe_grouped() -> Workload:
     """32 experts, hidden 4096 -> expert ffn 1536, bias + GELU aux, 16384 routed tokens."""
     E, T, N, K = 32, 16384, 1536, 4096
@@ -173,4 +186,4 @@ def moe_grouped() -> Workload:
 
 
 ALL = {"tiny": tiny, "decoder_fwd": decoder_forward, "square_8192": large_square,
-       "hybrid_bwd": hybrid_backward, "moe_grouped": moe_grouped}
+       "hybrid_bwd": hybrid_backward, "hybrid_bwd_fused": hybrid_backward_fused, "moe_grouped": moe_grouped}
