@@ -20,6 +20,13 @@ definition written out, in float64):
   acceptance tolerance below, not modelled.
 * Epilogues: none -> D = Y; bias -> D = Y + bias[n]; bias_gelu_aux ->
   pre = Y + bias[n], aux = pre, D = gelu_tanh(pre).
+* Backward epilogues (readings; the pages name the bias_gelu_aux forward
+  and the FP8 backward GEMMs, not these details):
+  - dgelu: the GEMM that produces the gradient of GELU's output multiplies
+    it by GELU's derivative at the saved pre-activation aux (bf16 [M, N]):
+    D = Y * gelu_tanh'(aux).  That is the gradient of the pre-activation.
+  - accumulate: the weight-gradient GEMM adds into an existing fp32 main
+    gradient C [M, N]: D = C + Y (beta = 1).
 * gelu_tanh(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) (the
   tanh approximation of Hendrycks and Gimpel, "Gaussian Error Linear
   Units", 2016; the pages only name the tanh approximation).
@@ -40,7 +47,7 @@ import numpy as np
 from .formats import FP8Format, bf16_to_float64
 from .mx import dequantize
 
-EPILOGUES = ("none", "bias", "bias_gelu_aux")
+EPILOGUES = ("none", "bias", "bias_gelu_aux", "dgelu", "accumulate")
 
 
 def gelu_tanh(x) -> np.ndarray:
@@ -57,15 +64,36 @@ def gelu_tanh(x) -> np.ndarray:
     return 0.5 * x * one_plus_tanh
 
 
-def epilogue(y, bias_bf16, epi: str):
+def dgelu_tanh(x) -> np.ndarray:
+    """d/dx gelu_tanh(x), from the product and chain rules.
+
+    With s = (1 + tanh(u)) / 2 = 1 / (1 + exp(-2u)) and u' = sqrt(2/pi) (1 + 3 * 0.044715 x^2):
+    gelu_tanh(x) = x s, and ds/dx = 2 s (1 - s) u', so the derivative is s + 2 x s (1 - s) u'.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    c = math.sqrt(2.0 / math.pi)
+    u = c * (x + 0.044715 * x * x * x)
+    du = c * (1.0 + 3.0 * 0.044715 * x * x)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-2.0 * u))
+    return s + 2.0 * x * s * (1.0 - s) * du
+
+
+def epilogue(y, bias_bf16, epi: str, aux_in=None, c_in=None):
     """Apply an epilogue to float64 GEMM results y [M, N].
 
+    aux_in: bf16 bit patterns [M, N] of the saved pre-activation (dgelu only);
+    c_in: the fp32 values [M, N] accumulated into (accumulate only).
     Returns (D, aux) as float64; aux is None unless epi == "bias_gelu_aux".
     """
     if epi not in EPILOGUES:
         raise ValueError(f"unknown epilogue {epi!r}")
     if epi == "none":
         return y, None
+    if epi == "dgelu":
+        return y * dgelu_tanh(bf16_to_float64(np.asarray(aux_in))), None
+    if epi == "accumulate":
+        return np.asarray(c_in, dtype=np.float64) + y, None
     b = bf16_to_float64(np.asarray(bias_bf16))
     pre = y + b[None, :]
     if epi == "bias":
@@ -73,7 +101,8 @@ def epilogue(y, bias_bf16, epi: str):
     return gelu_tanh(pre), pre
 
 
-def mx_gemm(qa, sa, fmt_a: FP8Format, qb, sb, fmt_b: FP8Format, bias_bf16=None, epi: str = "none"):
+def mx_gemm(qa, sa, fmt_a: FP8Format, qb, sb, fmt_b: FP8Format, bias_bf16=None, epi: str = "none",
+            aux_in=None, c_in=None):
     """D = epilogue(dequant(A) @ dequant(B)^T).
 
     qa [M, K] / sa [M, K/32] and qb [N, K] / sb [N, K/32] are MXFP8 codes and
@@ -84,7 +113,7 @@ def mx_gemm(qa, sa, fmt_a: FP8Format, qb, sb, fmt_b: FP8Format, bias_bf16=None, 
     b = dequantize(qb, sb, fmt_b)
     y = np.matmul(a, b.T)
     s = np.matmul(np.abs(a), np.abs(b).T)
-    d, aux = epilogue(y, bias_bf16, epi)
+    d, aux = epilogue(y, bias_bf16, epi, aux_in, c_in)
     return d, aux, s
 
 

@@ -23,7 +23,7 @@ import pytest
 import torch
 
 from oracle.formats import E4M3, E5M2, bf16_to_float64, decode
-from oracle.gemm import epilogue, gelu_tanh, grouped_mx_gemm, mx_gemm, tolerance_bound, within_tolerance
+from oracle.gemm import dgelu_tanh, epilogue, gelu_tanh, grouped_mx_gemm, mx_gemm, tolerance_bound, within_tolerance
 
 
 def rand_codes(rng, shape, fmt):
@@ -114,6 +114,43 @@ def test_gelu_tanh_against_torch_and_identities():
     assert np.all(np.abs(gelu_tanh(big) / big - 1) < 1e-15)
     # the tanh-form constant: at x = 1, 0.5 (1 + tanh(sqrt(2/pi) * 1.044715))
     assert math.isclose(float(gelu_tanh(1.0)), 0.5 * (1 + math.tanh(math.sqrt(2 / math.pi) * 1.044715)), rel_tol=1e-15)
+
+
+def test_dgelu_tanh_against_differences_autograd_and_limits():
+    x = np.linspace(-8, 8, 4001)
+    # central differences of the (separately pinned) gelu_tanh: error O(h^2)
+    h = 1e-5
+    fd = (gelu_tanh(x + h) - gelu_tanh(x - h)) / (2 * h)
+    assert np.allclose(dgelu_tanh(x), fd, rtol=0, atol=1e-8)
+    # torch autograd of its own tanh GELU, in float64
+    t = torch.from_numpy(x.copy()).requires_grad_(True)
+    torch.nn.functional.gelu(t, approximate="tanh").sum().backward()
+    assert np.allclose(dgelu_tanh(x), t.grad.numpy(), rtol=1e-12, atol=1e-14)
+    assert dgelu_tanh(0.0) == 0.5
+    assert abs(float(dgelu_tanh(12.0)) - 1.0) < 1e-15 and abs(float(dgelu_tanh(-12.0))) < 1e-15
+    # its maximum, ~1.1289 near x = 1.4 (also what bounds error propagation through GELU)
+    assert 1.128 < np.max(dgelu_tanh(x)) < 1.13
+
+
+def test_backward_epilogues():
+    rng = np.random.default_rng(13)
+    y = rng.standard_normal((3, 5))   # non-square: an elementwise mix-up of axes would fail
+    pre = (rng.standard_normal((3, 5)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    d, aux = epilogue(y, None, "dgelu", aux_in=pre)
+    assert aux is None and np.array_equal(d, y * dgelu_tanh(bf16_to_float64(pre)))
+    zeros = np.zeros((3, 5), np.uint16)
+    d, _ = epilogue(y, None, "dgelu", aux_in=zeros)
+    assert np.array_equal(d, 0.5 * y)   # gelu'(0) = 1/2
+    c = rng.standard_normal((3, 5)).astype(np.float32)
+    d, aux = epilogue(y, None, "accumulate", c_in=c)
+    assert aux is None and np.array_equal(d, c.astype(np.float64) + y)
+    # through mx_gemm: one-hot operands pick single products
+    qa = np.zeros((2, 128), np.uint8); qa[0, 3] = 0x38; qa[1, 70] = 0x40   # 1.0, 2.0 (E4M3)
+    qb = np.zeros((3, 128), np.uint8); qb[1, 3] = 0x38; qb[2, 70] = 0x38
+    sa = np.full((2, 4), 127, np.uint8); sb = np.full((3, 4), 127, np.uint8)
+    cc = np.arange(6, dtype=np.float32).reshape(2, 3)
+    d, _, _ = mx_gemm(qa, sa, E4M3, qb, sb, E4M3, epi="accumulate", c_in=cc)
+    assert np.array_equal(d, cc + np.array([[0, 1.0, 0], [0, 0, 2.0]]))
 
 
 def test_epilogue_bias_and_aux():
