@@ -77,7 +77,13 @@ typedef enum {
 
 typedef enum { TE_BF16 = 0, TE_FP32 = 1, TE_E4M3 = 2, TE_E5M2 = 3, TE_E8M0 = 4 } te_dtype;
 
-typedef enum { TE_EPI_NONE = 0, TE_EPI_BIAS = 1, TE_EPI_BIAS_GELU_AUX = 2 } te_epilogue;
+typedef enum {
+  TE_EPI_NONE = 0,
+  TE_EPI_BIAS = 1,
+  TE_EPI_BIAS_GELU_AUX = 2,
+  TE_EPI_DGELU = 3,      /* backward of BIAS_GELU_AUX: D = acc * gelu_tanh'(aux) */
+  TE_EPI_ACCUMULATE = 4  /* fp32 D += acc */
+} te_epilogue;
 
 typedef enum { TE_ROWWISE = 1, TE_COLWISE = 2, TE_BOTH = 3 } te_qdir;
 
@@ -171,8 +177,18 @@ te_status te_mxfp8_quantize_bgrad(const uint16_t* x, int64_t rows, int64_t cols,
  *            TE_EPI_BIAS:          D = acc + bias[n]
  *            TE_EPI_BIAS_GELU_AUX: pre = acc + bias[n]; aux = bf16(pre);
  *                                  D = gelu_tanh(pre)  ([TE-JAX] tanh GELU)
- *   bias     bf16 [N]; required iff epi != TE_EPI_NONE, NULL otherwise
- *   aux      bf16 [M, N]; required iff epi == TE_EPI_BIAS_GELU_AUX, NULL otherwise
+ *            TE_EPI_DGELU:         D = acc * gelu_tanh'(aux[m, n]): the
+ *                                  backward of BIAS_GELU_AUX, where aux is
+ *                                  the pre-activation the forward saved
+ *                                  (read here) and acc the gradient of the
+ *                                  GELU output
+ *            TE_EPI_ACCUMULATE:    D = D + acc with D fp32 (read and
+ *                                  written; the weight gradient added into
+ *                                  an fp32 main gradient, beta = 1)
+ *   bias     bf16 [N]; required iff epi is BIAS or BIAS_GELU_AUX, NULL otherwise
+ *   aux      bf16 [M, N]; required iff epi is BIAS_GELU_AUX (written) or
+ *            DGELU (read), NULL otherwise
+ *   TE_EPI_ACCUMULATE needs d_dtype == TE_FP32 (TE_ERR_DTYPE otherwise).
  *   Shapes: M, N, K >= 0; K % 128 == 0, M % 16 == 0, N % 16 == 0 (the
  *   [HK-PR] checks; M and N need not be multiples of the tile size).
  *   M == 0 or N == 0 enqueues nothing; K == 0 gives D = epi(0).

@@ -23,11 +23,12 @@ _lib = ctypes.CDLL(_LIB_PATH)
 # enum values of include/temx.h
 TE_OK, TE_ERR_NULL, TE_ERR_SHAPE, TE_ERR_ALIGN, TE_ERR_DTYPE, TE_ERR_WORKSPACE, TE_ERR_HIP, TE_ERR_VALUE = range(8)
 TE_BF16, TE_FP32, TE_E4M3, TE_E5M2, TE_E8M0 = range(5)
-TE_EPI_NONE, TE_EPI_BIAS, TE_EPI_BIAS_GELU_AUX = range(3)
+TE_EPI_NONE, TE_EPI_BIAS, TE_EPI_BIAS_GELU_AUX, TE_EPI_DGELU, TE_EPI_ACCUMULATE = range(5)
 TE_ROWWISE, TE_COLWISE, TE_BOTH = 1, 2, 3
 
 FORMATS = {"e4m3": TE_E4M3, "e5m2": TE_E5M2}
-EPILOGUES = {"none": TE_EPI_NONE, "bias": TE_EPI_BIAS, "bias_gelu_aux": TE_EPI_BIAS_GELU_AUX}
+EPILOGUES = {"none": TE_EPI_NONE, "bias": TE_EPI_BIAS, "bias_gelu_aux": TE_EPI_BIAS_GELU_AUX,
+             "dgelu": TE_EPI_DGELU, "accumulate": TE_EPI_ACCUMULATE}
 DIRECTIONS = {"row": TE_ROWWISE, "col": TE_COLWISE, "both": TE_BOTH}
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -202,19 +203,22 @@ def fp8_cast_current_scaling(x, fmt="e4m3", stream=None):
 
 
 def mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, epilogue="none", bias=None, out_dtype=torch.bfloat16,
-               stream=None):
-    """-> (D, aux) for D = epilogue(A . B^T); aux is None unless epilogue == "bias_gelu_aux"."""
+               aux=None, out=None, stream=None):
+    """-> (D, aux) for D = epilogue(A . B^T).  aux is written and returned for "bias_gelu_aux" and is
+    the saved pre-activation read by "dgelu"; "accumulate" adds into the given fp32 ``out``."""
     M, N = a.shape[0], b.shape[0]
-    d = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    aux = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if epilogue == "bias_gelu_aux" else None
+    d = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=a.device)
+    if epilogue == "bias_gelu_aux":
+        aux = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     te_mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, d, epilogue, bias, aux, None, stream)
-    return d, aux
+    return d, (aux if epilogue == "bias_gelu_aux" else None)
 
 
 def mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n, epilogue="none", bias=None,
-                       out_dtype=torch.bfloat16, stream=None):
+                       out_dtype=torch.bfloat16, aux=None, out=None, stream=None):
     total_m = a.shape[0]
-    d = torch.empty((total_m, n), dtype=out_dtype, device=a.device)
-    aux = torch.empty((total_m, n), dtype=torch.bfloat16, device=a.device) if epilogue == "bias_gelu_aux" else None
+    d = out if out is not None else torch.empty((total_m, n), dtype=out_dtype, device=a.device)
+    if epilogue == "bias_gelu_aux":
+        aux = torch.empty((total_m, n), dtype=torch.bfloat16, device=a.device)
     te_mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n, d, epilogue, bias, aux, None, stream)
-    return d, aux
+    return d, (aux if epilogue == "bias_gelu_aux" else None)

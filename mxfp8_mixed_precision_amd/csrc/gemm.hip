@@ -284,7 +284,7 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], voi
     const int64_t n = n0 + wn * LY::WTN + 16 * i + 4 * g;
     if (n >= N) continue;
     float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-    if constexpr (EPI != TE_EPI_NONE) {
+    if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
       const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
       b0 = bf16_bits_to_float(bb.x & 0xFFFFu);
       b1 = bf16_bits_to_float(bb.x >> 16);
@@ -296,7 +296,7 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], voi
       const int64_t m = m0 + wm * LY::WTM + 16 * j + r;
       if (m >= m_end) continue;
       float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
-      if constexpr (EPI != TE_EPI_NONE) {
+      if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
         v0 += b0;
         v1 += b1;
         v2 += b2;
@@ -308,6 +308,20 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], voi
         v1 = gelu_tanh(v1);
         v2 = gelu_tanh(v2);
         v3 = gelu_tanh(v3);
+      }
+      if constexpr (EPI == TE_EPI_DGELU) {  // aux holds the saved bf16 pre-activation
+        const uint2 pa = *reinterpret_cast<const uint2*>(aux + m * N + n);
+        v0 *= dgelu_tanh(bf16_bits_to_float(pa.x & 0xFFFFu));
+        v1 *= dgelu_tanh(bf16_bits_to_float(pa.x >> 16));
+        v2 *= dgelu_tanh(bf16_bits_to_float(pa.y & 0xFFFFu));
+        v3 *= dgelu_tanh(bf16_bits_to_float(pa.y >> 16));
+      }
+      if constexpr (EPI == TE_EPI_ACCUMULATE) {  // fp32 D is read and added to
+        const float4 c = *reinterpret_cast<const float4*>(static_cast<float*>(d) + m * N + n);
+        v0 = c.x + v0;
+        v1 = c.y + v1;
+        v2 = c.z + v2;
+        v3 = c.w + v3;
       }
       if constexpr (OUT == TE_BF16) {
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(d) + m * N + n) =
@@ -412,7 +426,8 @@ __global__ __launch_bounds__(LY::kThreads) void mx_grouped_gemm_kernel(GemmParam
     v4f acc[LY::FRN][LY::FRM];
     __syncthreads();  // the previous tile's last reads of stage 0/1 are done
     mainloop<LY, FA, FB>(lds, acc, A, B, p.K, wave, lane);
-    epilogue<LY, EPI, OUT>(acc, p.d, p.aux, EPI == TE_EPI_NONE ? nullptr : p.bias + (int64_t)e * p.N, m0, m_end,
+    const bool has_bias = EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX;
+    epilogue<LY, EPI, OUT>(acc, p.d, p.aux, has_bias ? p.bias + (int64_t)e * p.N : nullptr, m0, m_end,
                            n0, p.N, wave, lane);
   }
 }
@@ -437,7 +452,9 @@ te_status launch3(const GemmParams& p, te_epilogue epi, te_dtype out, dim3 grid,
   switch (epi) {
     case TE_EPI_NONE: return launch4<C, GROUPED, FA, FB, TE_EPI_NONE>(p, out, grid, stream);
     case TE_EPI_BIAS: return launch4<C, GROUPED, FA, FB, TE_EPI_BIAS>(p, out, grid, stream);
-    default: return launch4<C, GROUPED, FA, FB, TE_EPI_BIAS_GELU_AUX>(p, out, grid, stream);
+    case TE_EPI_BIAS_GELU_AUX: return launch4<C, GROUPED, FA, FB, TE_EPI_BIAS_GELU_AUX>(p, out, grid, stream);
+    case TE_EPI_DGELU: return launch4<C, GROUPED, FA, FB, TE_EPI_DGELU>(p, out, grid, stream);
+    default: return launch5<C, GROUPED, FA, FB, TE_EPI_ACCUMULATE, TE_FP32>(p, grid, stream);  // fp32 D only
   }
 }
 
@@ -464,12 +481,15 @@ inline bool use_small_tile(int64_t big_tiles, int64_t K) {
 te_status check_common(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,
                        const uint8_t* b_scale, te_dtype b_fmt, void* d, te_dtype d_dtype, te_epilogue epi,
                        const uint16_t* bias, uint16_t* aux, bool any_rows, bool any_k) {
-  TE_REQUIRE(epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX, TE_ERR_VALUE);
+  TE_REQUIRE(epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX || epi == TE_EPI_DGELU ||
+                 epi == TE_EPI_ACCUMULATE,
+             TE_ERR_VALUE);
   TE_REQUIRE(is_fp8(a_fmt) && is_fp8(b_fmt), TE_ERR_DTYPE);
   TE_REQUIRE(!(a_fmt == TE_E5M2 && b_fmt == TE_E5M2), TE_ERR_DTYPE);
   TE_REQUIRE(d_dtype == TE_BF16 || d_dtype == TE_FP32, TE_ERR_DTYPE);
-  TE_REQUIRE((epi != TE_EPI_NONE) == (bias != nullptr), TE_ERR_NULL);
-  TE_REQUIRE((epi == TE_EPI_BIAS_GELU_AUX) == (aux != nullptr), TE_ERR_NULL);
+  TE_REQUIRE(epi != TE_EPI_ACCUMULATE || d_dtype == TE_FP32, TE_ERR_DTYPE);
+  TE_REQUIRE((epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX) == (bias != nullptr), TE_ERR_NULL);
+  TE_REQUIRE((epi == TE_EPI_BIAS_GELU_AUX || epi == TE_EPI_DGELU) == (aux != nullptr), TE_ERR_NULL);
   if (!any_rows) return TE_OK;
   TE_REQUIRE(d != nullptr, TE_ERR_NULL);
   TE_REQUIRE(aligned16(d), TE_ERR_ALIGN);

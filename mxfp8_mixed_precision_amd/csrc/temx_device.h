@@ -136,4 +136,21 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// d/dx gelu_tanh(x) = s + 2 x s (1 - s) u' with s = 1 / (1 + e), e = 2^(-2 u log2 e)
+// and u' = sqrt(2/pi) (1 + 3 * 0.044715 x^2).  s (1 - s) is evaluated as
+// 1 / (2 + e + 1/e): no cancellation as s -> 0 or 1, and the right limit 0
+// when e overflows or underflows (the derivative then keeps its relative
+// accuracy down to where it leaves the fp32 range).  The product term is
+// taken as 0 once that factor is 0, so huge |x| (x^2 = inf) cannot give 0 * inf.
+__device__ __forceinline__ float dgelu_tanh(float x) {
+  constexpr float kC = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  constexpr float kK = 0.7978845608028654f;                                 // sqrt(2/pi)
+  const float x2 = x * x;
+  const float e = __builtin_amdgcn_exp2f(x * (kC + (kC * 0.044715f) * x2));
+  const float s = __builtin_amdgcn_rcpf(1.0f + e);
+  const float sd = __builtin_amdgcn_rcpf(2.0f + e + __builtin_amdgcn_rcpf(e));
+  const float t = 2.0f * x * sd * (kK + (kK * 3.0f * 0.044715f) * x2);
+  return s + (sd == 0.0f ? 0.0f : t);
+}
+
 }  // namespace temx

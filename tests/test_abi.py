@@ -122,7 +122,7 @@ def test_gemm_validation():
     assert gemm(fa=te.TE_E5M2, fb=te.TE_E5M2) == te.TE_ERR_DTYPE
     assert gemm(fa=te.TE_BF16) == te.TE_ERR_DTYPE
     assert gemm(dt=te.TE_E4M3) == te.TE_ERR_DTYPE
-    assert gemm(epi=5) == te.TE_ERR_VALUE
+    assert gemm(epi=6) == te.TE_ERR_VALUE
     assert gemm(epi=te.TE_EPI_BIAS) == te.TE_ERR_NULL                       # bias missing
     assert gemm(bias=P3) == te.TE_ERR_NULL                                  # bias without epilogue
     assert gemm(epi=te.TE_EPI_BIAS_GELU_AUX, bias=P3) == te.TE_ERR_NULL     # aux missing
@@ -133,6 +133,15 @@ def test_gemm_validation():
     assert gemm(sa=P + 2) == te.TE_ERR_ALIGN
     assert gemm(d=BAD) == te.TE_ERR_ALIGN
     assert gemm(M=0) == te.TE_OK and gemm(N=0, a=None, d=None) == te.TE_OK
+    # backward epilogues: dgelu reads aux and takes no bias; accumulate needs fp32 D
+    assert gemm(epi=te.TE_EPI_DGELU) == te.TE_ERR_NULL                      # aux missing
+    assert gemm(epi=te.TE_EPI_DGELU, aux=P3, bias=P3) == te.TE_ERR_NULL     # bias with dgelu
+    assert gemm(epi=te.TE_EPI_DGELU, aux=BAD) == te.TE_ERR_ALIGN
+    assert gemm(epi=te.TE_EPI_ACCUMULATE) == te.TE_ERR_DTYPE                 # bf16 D
+    assert gemm(epi=te.TE_EPI_ACCUMULATE, dt=te.TE_FP32, aux=P3) == te.TE_ERR_NULL
+    assert gemm(epi=te.TE_EPI_ACCUMULATE, dt=te.TE_FP32, bias=P3) == te.TE_ERR_NULL
+    assert gemm(epi=te.TE_EPI_ACCUMULATE, dt=te.TE_FP32, M=0) == te.TE_OK
+    assert gemm(epi=5) == te.TE_ERR_VALUE
 
 
 def grouped(G=4, splits=P3, T=1024, a=P, sa=P, fa=te.TE_E4M3, b=P, sb=P, fb=te.TE_E4M3, N=256, K=256, d=P2,

@@ -13,6 +13,8 @@ the CPU oracle.
   outputs that also meet the stated tolerance without H is printed.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -291,3 +293,116 @@ def test_moe_grouped_full_size_sampled():
     counts = workloads.moe_counts()
     assert counts.sum() == w.total_m
     check_grouped(counts.tolist(), N=w.N, K=w.K, epi=w.epilogue, seed=5, rows_per_expert=12)
+
+
+# ---------------------------------------------------------------- backward epilogues
+
+def backward_operands(M, N, K, seed):
+    a = workloads.normal_bf16(seed, 0, (M, K), 1e-2, 0.0)     # a gradient (E5M2)
+    b = workloads.normal_bf16(seed, 1, (N, K), 0.05, 0.0)     # weights (E4M3)
+    qa, sa, _, _ = te().mxfp8_quantize(dev(a), "e5m2", "row")
+    qb, sb, _, _ = te().mxfp8_quantize(dev(b), "e4m3", "row")
+    oqa, osa = oracle.quantize_rowwise(a, oracle.E5M2)
+    oqb, osb = oracle.quantize_rowwise(b, oracle.E4M3)
+    assert np.array_equal(host(qa), oqa) and np.array_equal(host(qb), oqb)
+    return qa, sa, qb, sb, oqa, osa, oqb, osb
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256)])
+def test_dgelu_epilogue(M, N, K):
+    qa, sa, qb, sb, oqa, osa, oqb, osb = backward_operands(M, N, K, 70 + K)
+    pre = workloads.normal_bf16(72, M + N, (M, N), 2.0, 0.0)   # the forward's saved pre-activation
+    d, _ = te().mxfp8_gemm(qa, sa, "e5m2", qb, sb, "e4m3", "dgelu", aux=dev(pre))
+    torch.cuda.synchronize()
+    rows = sample(M, seed=3) if M > 2048 else np.arange(M)
+    cols = sample(N, seed=4) if N > 2048 else np.arange(N)
+    Fa, Fb = oracle.E5M2, oracle.E4M3
+    p = pre[rows][:, cols]
+    ref, _, s = oracle.mx_gemm(oqa[rows], osa[rows], Fa, oqb[cols], osb[cols], Fb, epi="dgelu", aux_in=p)
+    got = bf16_to_f64(host(d)[rows][:, cols])
+    # against the instruction-sequence model's fp32 accumulators times gelu' of the saved pre-activation
+    acc = mfma_model.hw_gemm_fp32(oqa[rows], osa[rows], Fa, oqb[cols], osb[cols], Fb).astype(np.float64)
+    slope = oracle.dgelu_tanh(bf16_to_f64(p))
+    want = acc * slope
+    # bf16 rounding of the output (at most 2^-8 relative) plus the kernel's fp32
+    # evaluation of gelu' = s + t: a few ulps of each term (< 2^-17 relative to
+    # the result, and < 2^-20 of |s| + |t| <= 1 + |x u'| where the two nearly
+    # cancel, around gelu's minimum at x ~ -0.75)
+    x = bf16_to_f64(p)
+    terms = 1.0 + np.abs(x) * math.sqrt(2 / math.pi) * (1 + 3 * 0.044715 * x * x)
+    tol = (2.0 ** -8 + 2.0 ** -17) * np.abs(want) + 2.0 ** -20 * np.abs(acc) * terms + 1e-30
+    bad = np.abs(got - want) > tol
+    print(f"dgelu: {bad.sum()} of {bad.size} outside bf16 + fp32-gelu' precision; worst ratio "
+          f"{np.max(np.abs(got - want) / tol):.4f}")
+    assert not bad.any(), "dgelu epilogue differs from acc * gelu'(aux)"
+    # against the oracle: the GEMM bound (1e-5 S + H + K/16 fp32 additions) scaled by |gelu'|
+    err = np.abs(got - ref)
+    bound = (2.0 ** -8 * np.abs(ref) + np.abs(slope) * (1e-5 * s + (K / 16.0) * 2.0 ** -24 * s)
+             + 2.0 ** -20 * np.abs(acc) * terms)
+    r, cc = np.nonzero(err > bound)
+    if r.size:
+        h = mfma_model.truncation_bound_pairs(oqa[rows], osa[rows], Fa, oqb[cols], osb[cols], Fb, r, cc)
+        assert np.all(err[r, cc] <= bound[r, cc] + np.abs(slope[r, cc]) * h)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256)])
+def test_accumulate_epilogue(M, N, K):
+    qa, sa, qb, sb, oqa, osa, oqb, osb = backward_operands(M, N, K, 80 + K)
+    rng = np.random.default_rng(M + N + K)
+    c = (rng.standard_normal((M, N)) * 0.01).astype(np.float32)   # the fp32 main gradient
+    # D carved out of a larger buffer with canaries around it
+    buf = torch.full(((M + 64) * N,), 12345.0, dtype=torch.float32, device="cuda")
+    d = buf[32 * N:(32 + M) * N].view(M, N)
+    d.copy_(torch.from_numpy(c))
+    te().mxfp8_gemm(qa, sa, "e5m2", qb, sb, "e4m3", "accumulate", out=d)
+    torch.cuda.synchronize()
+    hb = host(buf)
+    assert np.all(hb[:32 * N] == 12345.0) and np.all(hb[(32 + M) * N:] == 12345.0)
+    rows = sample(M, seed=5) if M > 2048 else np.arange(M)
+    got = host(d)[rows]
+    Fa, Fb = oracle.E5M2, oracle.E4M3
+    # bit-exact: one fp32 add of the model's accumulators to C
+    acc = mfma_model.hw_gemm_fp32(oqa[rows], osa[rows], Fa, oqb, osb, Fb)
+    assert np.array_equal(got, (c[rows] + acc).astype(np.float32)), "accumulate differs from fl32(C + acc)"
+    ref, _, s = oracle.mx_gemm(oqa[rows], osa[rows], Fa, oqb, osb, Fb, epi="accumulate", c_in=c[rows])
+    bound = 2.0 ** -24 * np.abs(ref) + 2.0 ** -8 * np.abs(ref - c[rows]) + 1e-5 * s + (K / 16.0) * 2.0 ** -24 * s
+    err = np.abs(got - ref)
+    stated = err <= bound
+    if not stated.all():
+        r, cc = np.nonzero(~stated)
+        h = mfma_model.truncation_bound_pairs(oqa[rows], osa[rows], Fa, oqb, osb, Fb, r, cc)
+        assert np.all(err[r, cc] <= bound[r, cc] + h)
+
+
+@pytest.mark.parametrize("epi", ["dgelu", "accumulate"])
+def test_grouped_backward_epilogues_match_dense(epi):
+    # expert sizes are multiples of 16 (the dense GEMM's rule) but not of the tile sizes
+    counts = [304, 0, 528, 224]
+    G, N, K = len(counts), 400, 256
+    total = sum(counts)
+    a = workloads.normal_bf16(90, 0, (total, K), 1e-2, 0.0)
+    b = workloads.normal_bf16(90, 1, (G * N, K), 0.05, 0.0)
+    qa, sa, _, _ = te().mxfp8_quantize(dev(a), "e5m2", "row")
+    qb, sb, _, _ = te().mxfp8_quantize(dev(b), "e4m3", "row")
+    splits = torch.tensor(counts, dtype=torch.int32, device="cuda")
+    if epi == "dgelu":
+        aux = dev(workloads.normal_bf16(90, 2, (total, N), 2.0, 0.0))
+        d, _ = te().mxfp8_grouped_gemm(splits, qa, sa, "e5m2", qb, sb, "e4m3", N, "dgelu", aux=aux)
+    else:
+        c = torch.randn((total, N), dtype=torch.float32, device="cuda") * 0.01
+        d = c.clone()
+        te().mxfp8_grouped_gemm(splits, qa, sa, "e5m2", qb, sb, "e4m3", N, "accumulate", out=d)
+    off = 0
+    for e, me in enumerate(counts):
+        if me:
+            rows = slice(off, off + me)
+            if epi == "dgelu":
+                de, _ = te().mxfp8_gemm(qa[rows], sa[rows], "e5m2", qb[e * N:(e + 1) * N], sb[e * N:(e + 1) * N],
+                                        "e4m3", "dgelu", aux=aux[rows].contiguous())
+            else:
+                de = c[rows].clone()
+                te().mxfp8_gemm(qa[rows], sa[rows], "e5m2", qb[e * N:(e + 1) * N], sb[e * N:(e + 1) * N],
+                                "e4m3", "accumulate", out=de)
+            torch.cuda.synchronize()
+            assert torch.equal(d[rows], de), f"expert {e} differs from the dense GEMM"
+        off += me
