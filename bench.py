@@ -53,7 +53,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--workload", default="square_8192",
-                   choices=["square_8192", "decoder_fwd", "hybrid_bwd", "hybrid_bwd_fused", "moe_grouped", "tiny"])
+                   choices=["square_8192", "decoder_fwd", "decoder_fwd_mx", "hybrid_bwd", "hybrid_bwd_fused",
+                            "moe_grouped", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, copy a 512 MiB buffer 3 times (counter calibration)")
@@ -92,8 +93,8 @@ def q_bytes(rows, cols):
     return rows * cols * (2 + 1 + 1 / 32)
 
 
-def gemm_bytes(M, N, K, epi, grouped_experts=0):
-    b = M * K * (1 + 1 / 32) + N * K * (1 + 1 / 32) * max(1, grouped_experts) + M * N * 2
+def gemm_bytes(M, N, K, epi, grouped_experts=0, mx_out=False):
+    b = M * K * (1 + 1 / 32) + N * K * (1 + 1 / 32) * max(1, grouped_experts) + M * N * (1 + 1 / 32 if mx_out else 2)
     if epi == "bias_gelu_aux":
         b += M * N * 2
     if epi != "none":
@@ -163,12 +164,26 @@ def build_step(workload, torch, te, workloads):
         quantized[(spec, "row", fmt)] = rbufs
         quantized[(spec, "col", fmt)] = cbufs
 
+    mx_outputs = {}  # GEMM name -> rotating (codes, scales) of its MXFP8 output
     for g in w.gemms:
-        qa = add_quantize(g.a_src, g.fmt_a, g.a_dir, f"quantize_{g.a_dir}_{g.name}_A")
+        if g.a_from is not None:
+            qa = mx_outputs[g.a_from]
+        else:
+            qa = add_quantize(g.a_src, g.fmt_a, g.a_dir, f"quantize_{g.a_dir}_{g.name}_A")
         qb = add_quantize(g.b_src, g.fmt_b, g.b_dir, f"quantize_{g.b_dir}_{g.name}_B")
         bias = upload(g.bias.make()) if g.bias is not None else None
-        d = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev)
         aux = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev) if g.epilogue == "bias_gelu_aux" else None
+        if g.mx_out:
+            outs = qbufs(g.M, g.N, "row")
+            mx_outputs[g.name] = outs
+
+            def fn(r, g=g, qa=qa, qb=qb, bias=bias, outs=outs, aux=aux):
+                te.te_mxfp8_gemm_mxout(qa[r][0], qa[r][1], g.fmt_a, qb[r][0], qb[r][1], g.fmt_b, outs[r][0],
+                                       outs[r][1], "e4m3", g.epilogue, bias, aux)
+            step.add(f"gemm_{g.name}_mxout_{g.M}x{g.N}x{g.K}", "gemm", fn, g.flops,
+                     gemm_bytes(g.M, g.N, g.K, g.epilogue, mx_out=True))
+            continue
+        d = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev)
 
         def fn(r, g=g, qa=qa, qb=qb, bias=bias, d=d, aux=aux):
             te.te_mxfp8_gemm(qa[r][0], qa[r][1], g.fmt_a, qb[r][0], qb[r][1], g.fmt_b, d, g.epilogue, bias, aux)

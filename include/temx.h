@@ -204,6 +204,26 @@ te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * MXFP8 GEMM with an MXFP8 output: the GEMM and epilogue of te_mxfp8_gemm
+ * (NONE, BIAS or BIAS_GELU_AUX), whose D is written as the rowwise MXFP8
+ * operand of the next GEMM (the FC1 -> FC2 hand-over of LayerNormMLP: FC1's
+ * GELU output is FC2's input) instead of bf16.  The epilogue rounds its fp32
+ * results to bf16 exactly as te_mxfp8_gemm with d_dtype TE_BF16 does, then
+ * quantizes them in 32-column blocks as te_mxfp8_quantize (TE_ROWWISE) does,
+ * so d and d_scale are bit-identical to quantizing that bf16 D.
+ *   d        uint8 [M, N] codes, d_fmt TE_E4M3 or TE_E5M2
+ *   d_scale  uint8 [M, N/32] E8M0 scales
+ *   aux      as te_mxfp8_gemm (bf16 pre-activation, BIAS_GELU_AUX only)
+ *   Shapes as te_mxfp8_gemm, and N % 32 == 0.
+ */
+te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt,
+                              const uint8_t* b, const uint8_t* b_scale, te_dtype b_fmt,
+                              int64_t M, int64_t N, int64_t K,
+                              uint8_t* d, uint8_t* d_scale, te_dtype d_fmt, te_epilogue epi,
+                              const uint16_t* bias, uint16_t* aux,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Grouped MXFP8 GEMM in one launch ([ROCm-TE] single-launch grouped GEMM /
  * "Grouped GEMM using CK_Tile"; epilogues as te_mxfp8_gemm).  Expert g owns
  * rows [off_g, off_g + m_splits[g]) of A, D and aux, where off_g is the sum

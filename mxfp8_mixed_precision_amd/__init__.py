@@ -5,7 +5,7 @@ current HIP stream into the C entry point of the same name declared in
 ``include/temx.h``; all computation happens in the library's HIP kernels.
 The helpers without the prefix only allocate outputs with torch and call the
 ``te_*`` functions.  There is no fallback: importing this package fails if
-the library has not been built (``python -m mxfp8_mixed_precision_amd.build``).
+the library has not been built (``python mxfp8_mixed_precision_amd/build.py``).
 """
 
 from __future__ import annotations
@@ -17,7 +17,7 @@ import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtemx.so")
 if not os.path.exists(_LIB_PATH):
-    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m mxfp8_mixed_precision_amd.build`")
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python mxfp8_mixed_precision_amd/build.py`")
 _lib = ctypes.CDLL(_LIB_PATH)
 
 # enum values of include/temx.h
@@ -44,6 +44,8 @@ _SIGS = {
     "te_mxfp8_gemm_workspace_size": (_sz, [_i64, _i64, _i64]),
     "te_mxfp8_gemm": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _i64, _i64, _i64,
                                      _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
+    "te_mxfp8_gemm_mxout": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _i64, _i64, _i64,
+                                           _vp, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
     "te_mxfp8_grouped_gemm": (ctypes.c_int, [_i32, _vp, _i64, _vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int,
                                              _i64, _i64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
 }
@@ -139,6 +141,17 @@ def te_mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, d, epilogue="none", bias
         _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def te_mxfp8_gemm_mxout(a, a_scale, a_fmt, b, b_scale, b_fmt, d, d_scale, d_fmt, epilogue="none", bias=None,
+                        aux=None, workspace=None, stream=None) -> None:
+    M, K = a.shape
+    N = b.shape[0]
+    epi = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("te_mxfp8_gemm_mxout", _lib.te_mxfp8_gemm_mxout(
+        _ptr(a), _ptr(a_scale), _fmt(a_fmt), _ptr(b), _ptr(b_scale), _fmt(b_fmt), M, N, K,
+        _ptr(d), _ptr(d_scale), _fmt(d_fmt), epi, _ptr(bias), _ptr(aux), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def te_mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n: int, d, epilogue="none",
                           bias=None, aux=None, workspace=None, stream=None) -> None:
     total_m, K = a.shape
@@ -212,6 +225,18 @@ def mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, epilogue="none", bias=None,
         aux = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     te_mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, d, epilogue, bias, aux, None, stream)
     return d, (aux if epilogue == "bias_gelu_aux" else None)
+
+
+def mxfp8_gemm_mxout(a, a_scale, a_fmt, b, b_scale, b_fmt, epilogue="none", bias=None, out_fmt="e4m3",
+                     stream=None):
+    """-> (codes, scales, aux): D = epilogue(A . B^T) as a rowwise MXFP8 operand (codes [M, N], E8M0
+    scales [M, N/32]); aux as mxfp8_gemm."""
+    M, N = a.shape[0], b.shape[0]
+    d = torch.empty((M, N), dtype=torch.uint8, device=a.device)
+    ds = torch.empty((M, N // 32), dtype=torch.uint8, device=a.device)
+    aux = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if epilogue == "bias_gelu_aux" else None
+    te_mxfp8_gemm_mxout(a, a_scale, a_fmt, b, b_scale, b_fmt, d, ds, out_fmt, epilogue, bias, aux, None, stream)
+    return d, ds, aux
 
 
 def mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n, epilogue="none", bias=None,

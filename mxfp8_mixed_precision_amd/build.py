@@ -1,6 +1,7 @@
 """Build libtemx.so (the C-ABI library of HIP kernels for gfx950) in-tree.
 
-Usage: python -m mxfp8_mixed_precision_amd.build   (or call build()).
+Usage: python mxfp8_mixed_precision_amd/build.py   (or call build()).  Run it as a script, not
+as a package module: importing the package loads the library being rebuilt.
 """
 
 from __future__ import annotations

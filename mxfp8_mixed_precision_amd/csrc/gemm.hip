@@ -333,6 +333,71 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], voi
   }
 }
 
+// MXFP8 rowwise output.  The epilogue's fp32 results are rounded to bf16
+// exactly as for a bf16 D and then quantized in 32-column blocks (one E8M0
+// scale each, as the rowwise quantize kernel does), so the codes equal the
+// rowwise quantization of the bf16 D this GEMM writes otherwise: the next
+// GEMM sees the same operand without a bf16 round trip through memory.
+// Lane 16 g + r holds columns 16 i + 4 g .. +3 of row r, so the block
+// 32 b .. 32 b + 31 (i = 2b, 2b+1) sits in lanes r, r+16, r+32, r+48: the
+// block amax is a max over the lane's 8 values and then across those 4 lanes.
+template <class LY, int EPI, int FMT>
+__device__ __forceinline__ void epilogue_mx(const v4f (&acc)[LY::FRN][LY::FRM], uint8_t* d, uint8_t* d_scale,
+                                            uint16_t* aux, const uint16_t* bias, int64_t m0, int64_t m_end,
+                                            int64_t n0, int64_t N, int wave, int lane) {
+  static_assert(EPI == TE_EPI_NONE || EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX, "forward epilogues only");
+  const int wm = wave / LY::NWN, wn = wave % LY::NWN;
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int b = 0; b < LY::FRN / 2; ++b) {
+    const int64_t nb = n0 + wn * LY::WTN + 32 * b;  // wave-uniform; with N % 32 == 0 a block is all in or all out
+    if (nb >= N) continue;
+    float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if constexpr (EPI != TE_EPI_NONE) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(bias + nb + 16 * h + 4 * g);
+        bv[4 * h + 0] = bf16_bits_to_float(bb.x & 0xFFFFu);
+        bv[4 * h + 1] = bf16_bits_to_float(bb.x >> 16);
+        bv[4 * h + 2] = bf16_bits_to_float(bb.y & 0xFFFFu);
+        bv[4 * h + 3] = bf16_bits_to_float(bb.y >> 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < LY::FRM; ++j) {
+      const int64_t m = m0 + wm * LY::WTM + 16 * j + r;
+      const bool row_ok = m < m_end;
+      float v[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * h + e] = acc[2 * b + h][j][e] + bv[4 * h + e];
+      if constexpr (EPI == TE_EPI_BIAS_GELU_AUX) {
+        if (row_ok) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<uint2*>(aux + m * N + nb + 16 * h + 4 * g) =
+                make_uint2(pack_bf16x2(v[4 * h], v[4 * h + 1]), pack_bf16x2(v[4 * h + 2], v[4 * h + 3]));
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = gelu_tanh(v[k]);
+      }
+      const uint4 bits = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7])};
+      uint32_t amax = absmax_bits8(bits);  // every lane takes part in the exchanges
+      amax = max(amax, (uint32_t)__builtin_amdgcn_ds_swizzle((int)amax, 0x401F));               // lane ^ 16
+      amax = max(amax, (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, (int)amax));    // lane ^ 32
+      const uint32_t code = e8m0_code_from_amax_bits<FMT>(amax);
+      const uint2 q = cvt8_scaled<FMT>(bits, e8m0_to_float(code));
+      if (row_ok) {
+        *reinterpret_cast<uint32_t*>(d + m * N + nb + 4 * g) = q.x;
+        *reinterpret_cast<uint32_t*>(d + m * N + nb + 16 + 4 * g) = q.y;
+        if (g == 0) d_scale[m * (N / 32) + nb / 32] = (uint8_t)code;
+      }
+    }
+  }
+}
+
 struct GemmParams {
   const uint8_t* a;
   const uint8_t* a_scale;
@@ -344,6 +409,7 @@ struct GemmParams {
   int64_t M, N, K;
   const int32_t* m_splits;  // grouped only
   int32_t groups;           // grouped only
+  uint8_t* d_scale;         // MXFP8 output only: E8M0 scales [M, N/32]
 };
 
 // Dense: one workgroup per tile.
@@ -372,7 +438,11 @@ __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
   const Operand B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, BN);
   v4f acc[LY::FRN][LY::FRM];
   mainloop<LY, FA, FB>(lds, acc, A, B, p.K, wave, lane);
-  epilogue<LY, EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
+  if constexpr (OUT == TE_E4M3 || OUT == TE_E5M2)
+    epilogue_mx<LY, EPI, OUT>(acc, static_cast<uint8_t*>(p.d), p.d_scale, p.aux, p.bias, m0, p.M, n0, p.N, wave,
+                              lane);
+  else
+    epilogue<LY, EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
 }
 
 // Grouped: a persistent grid walks the flat list of (expert row-tile,
@@ -447,8 +517,25 @@ te_status launch4(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stre
                         : launch5<C, GROUPED, FA, FB, EPI, TE_FP32>(p, grid, stream);
 }
 
+template <class C, int FA, int FB, int EPI>
+te_status launch_mx4(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stream) {
+  return out == TE_E4M3 ? launch5<C, false, FA, FB, EPI, TE_E4M3>(p, grid, stream)
+                        : launch5<C, false, FA, FB, EPI, TE_E5M2>(p, grid, stream);
+}
+
 template <class C, bool GROUPED, int FA, int FB>
 te_status launch3(const GemmParams& p, te_epilogue epi, te_dtype out, dim3 grid, hipStream_t stream) {
+  if (out == TE_E4M3 || out == TE_E5M2) {  // MXFP8 output: dense, forward epilogues (validated)
+    if constexpr (GROUPED) {
+      return TE_ERR_DTYPE;
+    } else {
+      switch (epi) {
+        case TE_EPI_NONE: return launch_mx4<C, FA, FB, TE_EPI_NONE>(p, out, grid, stream);
+        case TE_EPI_BIAS: return launch_mx4<C, FA, FB, TE_EPI_BIAS>(p, out, grid, stream);
+        default: return launch_mx4<C, FA, FB, TE_EPI_BIAS_GELU_AUX>(p, out, grid, stream);
+      }
+    }
+  }
   switch (epi) {
     case TE_EPI_NONE: return launch4<C, GROUPED, FA, FB, TE_EPI_NONE>(p, out, grid, stream);
     case TE_EPI_BIAS: return launch4<C, GROUPED, FA, FB, TE_EPI_BIAS>(p, out, grid, stream);
@@ -544,6 +631,33 @@ extern "C" te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_
     return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_dtype,
                                  dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))), stream);
   return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)big_tiles), stream);
+}
+
+extern "C" te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,
+                                         const uint8_t* b_scale, te_dtype b_fmt, int64_t M, int64_t N, int64_t K,
+                                         uint8_t* d, uint8_t* d_scale, te_dtype d_fmt, te_epilogue epi,
+                                         const uint16_t* bias, uint16_t* aux, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  TE_REQUIRE(epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX, TE_ERR_VALUE);
+  TE_REQUIRE(d_fmt == TE_E4M3 || d_fmt == TE_E5M2, TE_ERR_DTYPE);
+  TE_REQUIRE(M >= 0 && N >= 0 && K >= 0, TE_ERR_SHAPE);
+  TE_REQUIRE(K % 128 == 0 && M % 16 == 0 && N % 32 == 0, TE_ERR_SHAPE);
+  TE_REQUIRE(M <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 31) - BK,
+             TE_ERR_SHAPE);
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  TE_REQUIRE(((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 31), TE_ERR_SHAPE);
+  // the common checks with the bf16 D this output stands for
+  te_status st = check_common(a, a_scale, a_fmt, b, b_scale, b_fmt, d, TE_BF16, epi, bias, aux, M > 0 && N > 0, K > 0);
+  if (st != TE_OK) return st;
+  if (M == 0 || N == 0) return TE_OK;
+  TE_REQUIRE(d_scale != nullptr, TE_ERR_NULL);
+  GemmParams p{a, a_scale, b, b_scale, d, bias, aux, M, N, K, nullptr, 0, d_scale};
+  if (use_small_tile(big_tiles, K))
+    return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_fmt,
+                                 dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))), stream);
+  return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_fmt, dim3((unsigned)big_tiles), stream);
 }
 
 extern "C" te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_splits, int64_t total_m,

@@ -144,6 +144,27 @@ def test_gemm_validation():
     assert gemm(epi=5) == te.TE_ERR_VALUE
 
 
+def mxout(a=P, sa=P, fa=te.TE_E4M3, b=P, sb=P, fb=te.TE_E4M3, M=256, N=256, K=256, d=P2, ds=P3,
+          df=te.TE_E4M3, epi=te.TE_EPI_NONE, bias=None, aux=None):
+    return L.te_mxfp8_gemm_mxout(a, sa, fa, b, sb, fb, M, N, K, d, ds, df, epi, bias, aux, None, 0, None)
+
+
+def test_gemm_mxout_validation():
+    assert mxout(N=48) == te.TE_ERR_SHAPE                 # blocks of 32 along N
+    assert mxout(K=192) == te.TE_ERR_SHAPE
+    assert mxout(df=te.TE_BF16) == te.TE_ERR_DTYPE
+    assert mxout(df=te.TE_E8M0) == te.TE_ERR_DTYPE
+    assert mxout(epi=te.TE_EPI_DGELU, aux=P3) == te.TE_ERR_VALUE      # forward epilogues only
+    assert mxout(epi=te.TE_EPI_ACCUMULATE) == te.TE_ERR_VALUE
+    assert mxout(epi=te.TE_EPI_BIAS) == te.TE_ERR_NULL
+    assert mxout(epi=te.TE_EPI_BIAS_GELU_AUX, bias=P3) == te.TE_ERR_NULL
+    assert mxout(ds=None) == te.TE_ERR_NULL
+    assert mxout(d=None) == te.TE_ERR_NULL
+    assert mxout(d=BAD) == te.TE_ERR_ALIGN
+    assert mxout(fa=te.TE_E5M2, fb=te.TE_E5M2) == te.TE_ERR_DTYPE
+    assert mxout(M=0, d=None, ds=None) == te.TE_OK
+
+
 def grouped(G=4, splits=P3, T=1024, a=P, sa=P, fa=te.TE_E4M3, b=P, sb=P, fb=te.TE_E4M3, N=256, K=256, d=P2,
             dt=te.TE_BF16, epi=te.TE_EPI_NONE, bias=None, aux=None):
     return L.te_mxfp8_grouped_gemm(G, splits, T, a, sa, fa, b, sb, fb, N, K, d, dt, epi, bias, aux, None, 0, None)

@@ -406,3 +406,41 @@ def test_grouped_backward_epilogues_match_dense(epi):
             torch.cuda.synchronize()
             assert torch.equal(d[rows], de), f"expert {e} differs from the dense GEMM"
         off += me
+
+
+# ---------------------------------------------------------------- MXFP8 output (FC1 -> FC2)
+
+@pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
+@pytest.mark.parametrize("M,N,K,out_fmt", [(16, 32, 128, "e4m3"), (272, 416, 256, "e4m3"), (1040, 800, 640, "e4m3"),
+                                           (4096 + 48, 4096 + 32, 256, "e4m3"), (272, 416, 256, "e5m2")])
+def test_mxfp8_output_equals_quantized_bf16_output(epi, M, N, K, out_fmt):
+    # the codes must be exactly the rowwise quantization of the bf16 D that
+    # te_mxfp8_gemm writes for the same inputs (itself checked against the
+    # oracle and the MFMA model by the tests above)
+    spec = workloads.GemmSpec("mxout", M, N, K, "e4m3", "e4m3", epi,
+                              workloads.TensorSpec(56, M, (M, K), 1.0, 0.01),
+                              workloads.TensorSpec(57, N, (N, K), 0.05),
+                              bias=None if epi == "none" else workloads.TensorSpec(58, N, (N,), 0.5))
+    bits_a, bits_b = spec.a_src.make(), spec.b_src.make()
+    qa, sa, qb, sb = quantize_pair(spec, bits_a, bits_b)
+    bias = None if spec.bias is None else dev(spec.bias.make())
+    d16, aux16 = te().mxfp8_gemm(qa, sa, "e4m3", qb, sb, "e4m3", epi, bias)
+    q, qs, aux = te().mxfp8_gemm_mxout(qa, sa, "e4m3", qb, sb, "e4m3", epi, bias, out_fmt=out_fmt)
+    torch.cuda.synchronize()
+    rows = sample(M, seed=6) if M > 2048 else np.arange(M)
+    oq, os_ = oracle.quantize_rowwise(host(d16)[rows], oracle.format_by_name(out_fmt))
+    assert np.array_equal(host(qs)[rows], os_), "scales differ from quantizing the bf16 output"
+    assert np.array_equal(host(q)[rows], oq), "codes differ from quantizing the bf16 output"
+    if epi == "bias_gelu_aux":
+        assert torch.equal(aux, aux16)
+    # D itself (through the codes): within the GEMM bound plus the quantization step, on sampled outputs
+    cols = sample(N, seed=7) if N > 2048 else np.arange(N)
+    oqa, osa = oracle_operand_rows(bits_a, "row", "e4m3", rows)
+    oqb, osb = oracle_operand_rows(bits_b, "row", "e4m3", cols)
+    ref, _, s = oracle.mx_gemm(oqa, osa, oracle.E4M3, oqb, osb, oracle.E4M3,
+                               None if spec.bias is None else spec.bias.make()[cols], epi)
+    deq = oracle.dequantize(host(q)[rows], host(qs)[rows], oracle.format_by_name(out_fmt))[:, cols]
+    step = 2.0 ** -3 if out_fmt == "e4m3" else 2.0 ** -2   # relative spacing of the element grid
+    scale = oracle.e8m0_decode(host(qs)[rows]).repeat(32, axis=1)[:, cols]
+    sub = (2.0 ** -9 if out_fmt == "e4m3" else 2.0 ** -16) * scale   # subnormal spacing
+    assert np.all(np.abs(deq - ref) <= step * np.abs(ref) + sub + 2.0 ** -7 * np.abs(ref) + 2e-5 * s + 1e-30)

@@ -82,6 +82,8 @@ class GemmSpec:
     a_dir: str = "row"
     b_dir: str = "row"
     bias: TensorSpec | None = None
+    mx_out: bool = False        # D written as a rowwise MXFP8 operand (fmt_a of the consumer) instead of bf16
+    a_from: str | None = None   # A is the MXFP8 output of this earlier GEMM (a_src is then unused)
 
     @property
     def flops(self) -> float:
@@ -138,6 +140,20 @@ def decoder_forward() -> Workload:
     ])
 
 
+def decoder_forward_mx() -> Workload:
+    """The decoder forward with FC1 -> FC2 chained: FC1's GELU output is written
+    as FC2's rowwise MXFP8 operand by FC1's epilogue (no bf16 D, no separate
+    quantize of FC2's input)."""
+    T, H, F = 4096, 1024, 4096
+    base = {g.name: g for g in decoder_forward().gemms}
+    fc1, fc2 = base["fc1"], base["fc2"]
+    return Workload("decoder_fwd_mx_4096x1024", gemms=[
+        base["qkv"],
+        GemmSpec("fc1", T, F, H, "e4m3", "e4m3", "bias_gelu_aux", fc1.a_src, fc1.b_src, bias=fc1.bias, mx_out=True),
+        GemmSpec("fc2", T, H, F, "e4m3", "e4m3", "bias", fc2.a_src, fc2.b_src, bias=fc2.bias, a_from="fc1"),
+    ])
+
+
 def large_square() -> Workload:
     """M = N = K = 8192 fprop, 1% outlier K-columns on both operands, plus
     standalone rowwise and columnwise quantization of both inputs."""
@@ -185,5 +201,5 @@ def moe_grouped() -> Workload:
         TensorSpec(5, 1, (T, K), 1.0), TensorSpec(5, 2, (E * N, K), 0.02), TensorSpec(5, 3, (E, N), 0.02))])
 
 
-ALL = {"tiny": tiny, "decoder_fwd": decoder_forward, "square_8192": large_square,
+ALL = {"tiny": tiny, "decoder_fwd": decoder_forward, "decoder_fwd_mx": decoder_forward_mx, "square_8192": large_square,
        "hybrid_bwd": hybrid_backward, "hybrid_bwd_fused": hybrid_backward_fused, "moe_grouped": moe_grouped}
