@@ -40,6 +40,7 @@ from .formats import E4M3, E5M2, FP8Format, decode, encode, e8m0_decode, format_
 from .mx import block_scale_code, quantize_rowwise, quantize_colwise, dequantize
 from .current_scaling import amax, current_scale, cast_current_scaling
 from .bgrad import column_sums, column_abs_sums
+from .delayed_scaling import delayed_scaling_step, next_scale, fp8_gemm_per_tensor
 from .gemm import mx_gemm, gelu_tanh, dgelu_tanh, epilogue, grouped_mx_gemm, within_tolerance, tolerance_bound
 
 __all__ = [
