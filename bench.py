@@ -43,7 +43,8 @@ ROTATE = 4                     # copies of each bandwidth-bound input / output
 KERNELS = {"quantize_row": ["quantize_rowwise_kernel"], "quantize_col": ["quantize_colwise_kernel"],
            "gemm": ["mx_gemm_kernel"], "grouped": ["mx_grouped_gemm_kernel"],
            "cast": ["amax_partial_kernel", "amax_final_kernel", "cast_kernel"],
-           "quantize_bgrad": ["quantize_colwise_kernel", "bgrad_final_kernel"]}
+           "quantize_bgrad": ["quantize_colwise_kernel", "bgrad_final_kernel"],
+           "cast_delayed": ["cast_amax_kernel", "delayed_update_kernel"]}
 CALIBRATION_BYTES = 512 << 20  # one device-to-device copy of this many bytes reads and writes it once
 
 
@@ -53,8 +54,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--workload", default="square_8192",
-                   choices=["square_8192", "decoder_fwd", "decoder_fwd_mx", "hybrid_bwd", "hybrid_bwd_fused",
-                            "moe_grouped", "tiny"])
+                   choices=["square_8192", "decoder_fwd", "decoder_fwd_mx", "decoder_fwd_delayed", "hybrid_bwd",
+                            "hybrid_bwd_fused", "moe_grouped", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, copy a 512 MiB buffer 3 times (counter calibration)")
@@ -164,8 +165,36 @@ def build_step(workload, torch, te, workloads):
         quantized[(spec, "row", fmt)] = rbufs
         quantized[(spec, "col", fmt)] = cbufs
 
+    def add_delayed_cast(spec, fmt, label):
+        # one tensor's delayed-scaling state (scale, amax history) and its rotating casts
+        src = rotated(spec.make())
+        n = spec.shape[0] * spec.shape[1]
+        scale = torch.ones(1, dtype=torch.float32, device=dev)
+        hist = torch.zeros(16, dtype=torch.float32, device=dev)
+        ws = torch.empty(te.te_amax_workspace_size(n), dtype=torch.uint8, device=dev)
+        outs = [(torch.empty(spec.shape, dtype=torch.uint8, device=dev), torch.empty(1, dtype=torch.float32, device=dev))
+                for _ in range(ROTATE)]
+
+        def fn(r, src=src, outs=outs, scale=scale, hist=hist, ws=ws, fmt=fmt):
+            te.te_fp8_cast_delayed_scaling(src[r], fmt, outs[r][0], outs[r][1], scale, hist, ws, "max", 0)
+        step.add(label, "cast", fn, 0.0, n * (2 + 1), KERNELS["cast_delayed"])
+        return outs
+
     mx_outputs = {}  # GEMM name -> rotating (codes, scales) of its MXFP8 output
     for g in w.gemms:
+        if g.scaling == "delayed":
+            ca = add_delayed_cast(g.a_src, g.fmt_a, f"cast_delayed_{g.name}_A")
+            cb = add_delayed_cast(g.b_src, g.fmt_b, f"cast_delayed_{g.name}_B")
+            bias = upload(g.bias.make()) if g.bias is not None else None
+            d = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev)
+            aux = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev) if g.epilogue == "bias_gelu_aux" else None
+
+            def fn(r, g=g, ca=ca, cb=cb, bias=bias, d=d, aux=aux):
+                te.te_fp8_gemm(ca[r][0], ca[r][1], g.fmt_a, cb[r][0], cb[r][1], g.fmt_b, d, g.epilogue, bias, aux)
+            # per-tensor operands: 1 B per element, no block scales
+            nbytes = gemm_bytes(g.M, g.N, g.K, g.epilogue) - (g.M + g.N) * g.K / 32
+            step.add(f"gemm_fp8_{g.name}_{g.M}x{g.N}x{g.K}", "gemm", fn, g.flops, nbytes)
+            continue
         if g.a_from is not None:
             qa = mx_outputs[g.a_from]
         else:
@@ -252,15 +281,24 @@ def cpu_baseline(workload, workloads):
             else:
                 sn //= 2
         fa, fb = oracle.format_by_name(g.fmt_a), oracle.format_by_name(g.fmt_b)
-        t0 = time.perf_counter()
-        qa, sa = (oracle.quantize_rowwise(a[:sm], fa) if g.a_dir == "row"
-                  else oracle.quantize_colwise(np.ascontiguousarray(a[:, :sm]), fa))
-        qb, sb = (oracle.quantize_rowwise(b[:sn], fb) if g.b_dir == "row"
-                  else oracle.quantize_colwise(np.ascontiguousarray(b[:, :sn]), fb))
-        t1 = time.perf_counter()
         bias = g.bias.make()[:sn] if g.bias is not None else None
-        oracle.mx_gemm(qa, sa, fa, qb, sb, fb, bias, g.epilogue)
-        t2 = time.perf_counter()
+        if g.scaling == "delayed":
+            t0 = time.perf_counter()
+            h0 = np.zeros(16, np.float32)
+            qa, ia, _, _, _ = oracle.delayed_scaling_step(a[:sm], fa, h0, np.float32(1.0))
+            qb, ib, _, _, _ = oracle.delayed_scaling_step(b[:sn], fb, h0, np.float32(1.0))
+            t1 = time.perf_counter()
+            oracle.fp8_gemm_per_tensor(qa, ia, fa, qb, ib, fb, bias, g.epilogue)
+            t2 = time.perf_counter()
+        else:
+            t0 = time.perf_counter()
+            qa, sa = (oracle.quantize_rowwise(a[:sm], fa) if g.a_dir == "row"
+                      else oracle.quantize_colwise(np.ascontiguousarray(a[:, :sm]), fa))
+            qb, sb = (oracle.quantize_rowwise(b[:sn], fb) if g.b_dir == "row"
+                      else oracle.quantize_colwise(np.ascontiguousarray(b[:, :sn]), fb))
+            t1 = time.perf_counter()
+            oracle.mx_gemm(qa, sa, fa, qb, sb, fb, bias, g.epilogue)
+            t2 = time.perf_counter()
         q_time += t1 - t0
         q_elems_s += (sm + sn) * g.K
         q_elems_full += (g.M + g.N) * g.K

@@ -87,6 +87,8 @@ typedef enum {
 
 typedef enum { TE_ROWWISE = 1, TE_COLWISE = 2, TE_BOTH = 3 } te_qdir;
 
+typedef enum { TE_AMAX_MAX = 0, TE_AMAX_MOST_RECENT = 1 } te_amax_algo;
+
 /* Human-readable name of a status code (static storage). */
 const char* te_status_str(te_status status);
 
@@ -118,6 +120,34 @@ te_status te_amax_reduce(const uint16_t* x, int64_t n, float* amax_out,
  */
 te_status te_fp8_cast_current_scaling(const uint16_t* x, int64_t n, te_dtype fmt, uint8_t* q_out,
                                       float* amax_out, float* scale_out, float* scale_inv_out,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Delayed-scaling FP8 cast ([TE-JAX] README example and "Enabling
+ * Quantization": DelayedScaling with margin, interval, an amax history of
+ * length 16 and the "max" algorithm; [FP8-WF] Step 4: a history window of
+ * amax values).  One call is one step on a tensor:
+ *   1. q_i = saturating RNE encode of fl32(x_i * scale), with the scale as it
+ *      stands on entry; q_scale_inv_out = fl32(1 / that scale) (what a GEMM
+ *      on q takes as its alpha factor);
+ *   2. the tensor's amax enters amax_history, newest first (the oldest drops);
+ *   3. r = max(amax_history) (TE_AMAX_MAX) or amax_history[0]
+ *      (TE_AMAX_MOST_RECENT); if r is positive and finite,
+ *      scale = fl32(fl32(fmt_max / r) / 2^margin) (a quotient beyond float
+ *      gives the largest finite float), else scale is kept.
+ *   x            bf16 [n]
+ *   fmt          TE_E4M3 or TE_E5M2
+ *   q_out        uint8 [n]
+ *   q_scale_inv_out, scale (in/out)   float [1] each, device
+ *   amax_history float [history_len], device, in/out; 1 <= history_len <= 1024
+ *   margin       0 .. 64
+ *   workspace    at least te_amax_workspace_size(n) bytes
+ * Initial state: scale = 1, history all zeros.  How often the scale is
+ * updated (the recipe's interval) is the caller's choice of when to call.
+ */
+te_status te_fp8_cast_delayed_scaling(const uint16_t* x, int64_t n, te_dtype fmt, uint8_t* q_out,
+                                      float* q_scale_inv_out, float* scale, float* amax_history,
+                                      int history_len, te_amax_algo algo, int margin,
                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -202,6 +232,25 @@ te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt
                         void* d, te_dtype d_dtype, te_epilogue epi,
                         const uint16_t* bias, uint16_t* aux,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Per-tensor FP8 GEMM (the GEMM of the delayed and current scaling recipes):
+ *   D = epi( a_scale_inv * b_scale_inv * sum_k val(a[m, k]) * val(b[n, k]) )
+ * with fp32 accumulation; the product of the two scale inverses is formed in
+ * fp32 and multiplies the accumulators before the epilogue.
+ *   a, b             uint8 [M, K] / [N, K] FP8 codes (no block scales)
+ *   a_scale_inv, b_scale_inv   float [1] each, device (e.g. q_scale_inv_out
+ *                    of te_fp8_cast_delayed_scaling or scale_inv_out of
+ *                    te_fp8_cast_current_scaling)
+ *   d, d_dtype, bias, aux, shapes, workspace: as te_mxfp8_gemm; epi is
+ *   TE_EPI_NONE, TE_EPI_BIAS or TE_EPI_BIAS_GELU_AUX.
+ */
+te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_dtype a_fmt,
+                      const uint8_t* b, const float* b_scale_inv, te_dtype b_fmt,
+                      int64_t M, int64_t N, int64_t K,
+                      void* d, te_dtype d_dtype, te_epilogue epi,
+                      const uint16_t* bias, uint16_t* aux,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * MXFP8 GEMM with an MXFP8 output: the GEMM and epilogue of te_mxfp8_gemm

@@ -25,6 +25,8 @@ TE_OK, TE_ERR_NULL, TE_ERR_SHAPE, TE_ERR_ALIGN, TE_ERR_DTYPE, TE_ERR_WORKSPACE, 
 TE_BF16, TE_FP32, TE_E4M3, TE_E5M2, TE_E8M0 = range(5)
 TE_EPI_NONE, TE_EPI_BIAS, TE_EPI_BIAS_GELU_AUX, TE_EPI_DGELU, TE_EPI_ACCUMULATE = range(5)
 TE_ROWWISE, TE_COLWISE, TE_BOTH = 1, 2, 3
+TE_AMAX_MAX, TE_AMAX_MOST_RECENT = 0, 1
+AMAX_ALGOS = {"max": TE_AMAX_MAX, "most_recent": TE_AMAX_MOST_RECENT}
 
 FORMATS = {"e4m3": TE_E4M3, "e5m2": TE_E5M2}
 EPILOGUES = {"none": TE_EPI_NONE, "bias": TE_EPI_BIAS, "bias_gelu_aux": TE_EPI_BIAS_GELU_AUX,
@@ -37,6 +39,10 @@ _SIGS = {
     "te_amax_workspace_size": (_sz, [_i64]),
     "te_amax_reduce": (ctypes.c_int, [_vp, _i64, _vp, _vp, _sz, _vp]),
     "te_fp8_cast_current_scaling": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "te_fp8_cast_delayed_scaling": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int,
+                                                   ctypes.c_int, ctypes.c_int, _vp, _sz, _vp]),
+    "te_fp8_gemm": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _i64, _i64, _i64,
+                                   _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
     "te_mxfp8_quantize": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]),
     "te_mxfp8_quantize_bgrad_workspace_size": (_sz, [_i64, _i64]),
     "te_mxfp8_quantize_bgrad": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, ctypes.c_int,
@@ -103,6 +109,27 @@ def te_fp8_cast_current_scaling(x, fmt, q_out, amax_out, scale_out, scale_inv_ou
     _check("te_fp8_cast_current_scaling", _lib.te_fp8_cast_current_scaling(
         _ptr(x), x.numel(), _fmt(fmt), _ptr(q_out), _ptr(amax_out), _ptr(scale_out), _ptr(scale_inv_out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def te_fp8_cast_delayed_scaling(x, fmt, q_out, q_scale_inv_out, scale, amax_history, workspace, algo="max",
+                                margin=0, stream=None) -> None:
+    a = AMAX_ALGOS[algo] if isinstance(algo, str) else int(algo)
+    _check("te_fp8_cast_delayed_scaling", _lib.te_fp8_cast_delayed_scaling(
+        _ptr(x), x.numel(), _fmt(fmt), _ptr(q_out), _ptr(q_scale_inv_out), _ptr(scale), _ptr(amax_history),
+        amax_history.numel(), a, int(margin), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def te_fp8_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, d, epilogue="none", bias=None, aux=None,
+                workspace=None, stream=None) -> None:
+    M, K = a.shape
+    N = b.shape[0]
+    d_dtype = TE_BF16 if d.dtype == torch.bfloat16 else TE_FP32
+    epi = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("te_fp8_gemm", _lib.te_fp8_gemm(
+        _ptr(a), _ptr(a_scale_inv), _fmt(a_fmt), _ptr(b), _ptr(b_scale_inv), _fmt(b_fmt), M, N, K,
+        _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def te_mxfp8_quantize(x, fmt, direction, q_row=None, s_row=None, q_col=None, s_col=None, stream=None) -> None:
@@ -196,6 +223,36 @@ def mxfp8_quantize_bgrad(x, fmt="e5m2", bgrad_dtype=torch.float32, stream=None):
     ws = torch.empty(max(te_mxfp8_quantize_bgrad_workspace_size(rows, cols), 16), dtype=torch.uint8, device=dev)
     te_mxfp8_quantize_bgrad(x, fmt, q_row, s_row, q_col, s_col, bgrad, ws, stream)
     return q_row, s_row, q_col, s_col, bgrad
+
+
+class DelayedScaling:
+    """Device state of one tensor under delayed scaling: scale (starts at 1) and the amax history
+    (zeros, newest first).  step(x) casts x with the current scale and updates the state."""
+
+    def __init__(self, fmt="e4m3", history_len=16, algo="max", margin=0, device="cuda"):
+        self.fmt, self.algo, self.margin = fmt, algo, margin
+        self.scale = torch.ones(1, dtype=torch.float32, device=device)
+        self.history = torch.zeros(history_len, dtype=torch.float32, device=device)
+
+    def step(self, x, stream=None):
+        """-> (q, q_scale_inv): x cast with the scale as it stood, and that scale's inverse."""
+        dev = x.device
+        q = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+        q_inv = torch.empty(1, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(te_amax_workspace_size(x.numel()), 4), dtype=torch.uint8, device=dev)
+        te_fp8_cast_delayed_scaling(x, self.fmt, q, q_inv, self.scale, self.history, ws, self.algo, self.margin,
+                                    stream)
+        return q, q_inv
+
+
+def fp8_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, epilogue="none", bias=None, out_dtype=torch.bfloat16,
+             stream=None):
+    """Per-tensor FP8 GEMM -> (D, aux)."""
+    M, N = a.shape[0], b.shape[0]
+    d = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    aux = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if epilogue == "bias_gelu_aux" else None
+    te_fp8_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, d, epilogue, bias, aux, None, stream)
+    return d, aux
 
 
 def amax(x, stream=None):

@@ -142,6 +142,98 @@ __global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// Delayed scaling ("Getting Started" recipes: DelayedScaling with an amax
+// history; "Workflow: ... Quickstart" Step 4).  One pass casts x with the
+// scale the history has given so far and records per-workgroup maxima of
+// |x| (x is read once); then one workgroup shifts the history (newest first),
+// reduces it (max, or the most recent), and replaces the scale with
+// fl32(fl32(fmt_max / r) / 2^margin) when r is positive and finite.
+template <int FMT>
+__global__ __launch_bounds__(kAmaxThreads) void cast_amax_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                 const float* __restrict__ scale_ptr,
+                                                                 uint8_t* __restrict__ q,
+                                                                 uint32_t* __restrict__ partial) {
+  const float scale = *scale_ptr;
+  const int64_t nchunks = n / 8;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads * kAmaxUnroll;
+  for (int64_t c0 = (int64_t)blockIdx.x * kAmaxThreads * kAmaxUnroll + threadIdx.x; c0 < nchunks; c0 += stride) {
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int64_t c = c0 + (int64_t)u * kAmaxThreads;
+      v[u] = c < nchunks ? load_nt16(xv + c) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const int64_t c = c0 + (int64_t)u * kAmaxThreads;
+      if (c < nchunks) {
+        m = max(m, absmax_bits8(v[u]));
+        uint2 r;
+        r.x = cast4<FMT>(v[u].x, v[u].y, scale);
+        r.y = cast4<FMT>(v[u].z, v[u].w, scale);
+        reinterpret_cast<uint2*>(q)[c] = r;
+      }
+    }
+  }
+  if (blockIdx.x == 0) {  // the n % 8 tail
+    const int64_t i = nchunks * 8 + threadIdx.x;
+    if (i < n) {
+      const uint32_t h = x[i];
+      m = max(m, h & 0x7FFFu);
+      q[i] = (uint8_t)(cast4<FMT>(h, 0, scale) & 0xFFu);
+    }
+  }
+  m = block_max(m);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+constexpr int kMaxHistory = 1024;
+
+template <int FMT>
+__global__ __launch_bounds__(kAmaxThreads) void delayed_update_kernel(const uint32_t* __restrict__ partial,
+                                                                      int nparts, float* __restrict__ history,
+                                                                      int len, int most_recent, int margin,
+                                                                      float* __restrict__ scale,
+                                                                      float* __restrict__ q_scale_inv) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += kAmaxThreads) m = max(m, partial[i]);
+  m = block_max(m);
+  const float amax = bf16_bits_to_float(m);
+  // shift: read every entry, wait, then write one place further
+  float held[kMaxHistory / kAmaxThreads];
+#pragma unroll
+  for (int k = 0; k < kMaxHistory / kAmaxThreads; ++k) {
+    const int i = threadIdx.x + k * kAmaxThreads;
+    held[k] = i < len ? history[i] : 0.0f;
+  }
+  __syncthreads();
+  uint32_t r = 0;  // max of the new history, over non-negative float bit patterns
+#pragma unroll
+  for (int k = 0; k < kMaxHistory / kAmaxThreads; ++k) {
+    const int i = threadIdx.x + k * kAmaxThreads;
+    if (i + 1 < len) {
+      history[i + 1] = held[k];
+      r = max(r, __float_as_uint(held[k]));
+    }
+  }
+  r = block_max(r);
+  if (threadIdx.x != 0) return;
+  history[0] = amax;
+  // over bit patterns (all entries are >= 0): a NaN sorts above inf and, like the
+  // plain maximum, makes the result non-finite, so the scale is kept
+  const float red = most_recent ? amax : __uint_as_float(max(__float_as_uint(amax), r));
+  const float s_old = *scale;
+  *q_scale_inv = (float)(1.0 / (double)s_old);  // the inverse of the scale the cast used
+  if (red > 0.0f && red <= FLT_MAX) {
+    // correctly rounded fp32 quotient (see amax_final_kernel), then an exact power-of-two division
+    float s = (float)((double)FmtTraits<FMT>::max_value / (double)red);
+    if (!(s <= FLT_MAX)) s = FLT_MAX;
+    *scale = ldexpf(s, -margin);
+  }
+}
+
 te_status launch_amax(const uint16_t* x, int64_t n, uint32_t* partial, int64_t blocks, hipStream_t stream) {
   hipLaunchKernelGGL(amax_partial_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream, x, n, partial);
   return launch_status();
@@ -201,5 +293,41 @@ extern "C" te_status te_fp8_cast_current_scaling(const uint16_t* x, int64_t n, t
     hipLaunchKernelGGL(cast_kernel<TE_E4M3>, dim3((unsigned)grid), dim3(256), 0, stream, x, n, scale_out, q_out);
   else
     hipLaunchKernelGGL(cast_kernel<TE_E5M2>, dim3((unsigned)grid), dim3(256), 0, stream, x, n, scale_out, q_out);
+  return launch_status();
+}
+
+extern "C" te_status te_fp8_cast_delayed_scaling(const uint16_t* x, int64_t n, te_dtype fmt, uint8_t* q_out,
+                                                 float* q_scale_inv_out, float* scale, float* amax_history,
+                                                 int history_len, te_amax_algo algo, int margin, void* workspace,
+                                                 size_t workspace_bytes, hipStream_t stream) {
+  TE_REQUIRE(is_fp8(fmt), TE_ERR_DTYPE);
+  TE_REQUIRE(algo == TE_AMAX_MAX || algo == TE_AMAX_MOST_RECENT, TE_ERR_VALUE);
+  TE_REQUIRE(n >= 0 && history_len >= 1 && history_len <= kMaxHistory, TE_ERR_SHAPE);
+  TE_REQUIRE(margin >= 0 && margin <= 64, TE_ERR_VALUE);
+  TE_REQUIRE(q_scale_inv_out != nullptr && scale != nullptr && amax_history != nullptr && workspace != nullptr,
+             TE_ERR_NULL);
+  TE_REQUIRE(n == 0 || (x != nullptr && q_out != nullptr), TE_ERR_NULL);
+  TE_REQUIRE(n == 0 || (aligned16(x) && aligned16(q_out)), TE_ERR_ALIGN);
+  TE_REQUIRE(((uintptr_t)workspace & 3u) == 0, TE_ERR_ALIGN);
+  TE_REQUIRE(((uintptr_t)scale & 3u) == 0 && ((uintptr_t)amax_history & 3u) == 0 &&
+                 ((uintptr_t)q_scale_inv_out & 3u) == 0,
+             TE_ERR_ALIGN);
+  const int64_t blocks = amax_blocks(n);
+  TE_REQUIRE(workspace_bytes >= (size_t)blocks * sizeof(uint32_t), TE_ERR_WORKSPACE);
+  uint32_t* partial = static_cast<uint32_t*>(workspace);
+  const int mr = algo == TE_AMAX_MOST_RECENT ? 1 : 0;
+  if (fmt == TE_E4M3) {
+    hipLaunchKernelGGL(cast_amax_kernel<TE_E4M3>, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream, x, n, scale,
+                       q_out, partial);
+    if (launch_status() != TE_OK) return TE_ERR_HIP;
+    hipLaunchKernelGGL(delayed_update_kernel<TE_E4M3>, dim3(1), dim3(kAmaxThreads), 0, stream, partial, (int)blocks,
+                       amax_history, history_len, mr, margin, scale, q_scale_inv_out);
+  } else {
+    hipLaunchKernelGGL(cast_amax_kernel<TE_E5M2>, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream, x, n, scale,
+                       q_out, partial);
+    if (launch_status() != TE_OK) return TE_ERR_HIP;
+    hipLaunchKernelGGL(delayed_update_kernel<TE_E5M2>, dim3(1), dim3(kAmaxThreads), 0, stream, partial, (int)blocks,
+                       amax_history, history_len, mr, margin, scale, q_scale_inv_out);
+  }
   return launch_status();
 }

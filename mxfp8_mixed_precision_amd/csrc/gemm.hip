@@ -158,7 +158,7 @@ __device__ __forceinline__ CopyOffsets copy_offsets(int64_t K, int c, int lane) 
   return o;
 }
 
-template <class C>
+template <class C, bool PT = false>
 __device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, const Operand& B,
                                            const CopyOffsets& off, int64_t K, int kt, int c) {
 #pragma unroll
@@ -168,7 +168,7 @@ __device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, con
     lds_dma16(A.data, stage + q * 1024, off.data, so);
     lds_dma16(B.data, stage + C::kOffBData + q * 1024, off.data, so);
   }
-  if (c < C::BM / 64) {
+  if (!PT && c < C::BM / 64) {
     lds_dma4(A.scale, stage + C::kOffAScale + c * 256, off.scale, kt * 4);
     lds_dma4(B.scale, stage + C::kOffBScale + c * 256, off.scale, kt * 4);
   }
@@ -211,23 +211,24 @@ __device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) { 
 // MFMA that uses it (measured: 2-12% faster across the GEMM shapes than
 // shifting the byte out of the row's scale word).  Rows 16 j further are 2 KB
 // further (an immediate offset).
+template <bool PT = false>
 __device__ __forceinline__ Frag read_frag(const uint8_t* stage, int data_off, int data_off2, int scale_off, int j) {
   const uint4 lo = *reinterpret_cast<const uint4*>(stage + data_off + j * 16 * BK);
   const uint4 hi = *reinterpret_cast<const uint4*>(stage + data_off2 + j * 16 * BK);
   Frag f;
   f.v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  f.s = (int)stage[scale_off + j * 64];
+  f.s = PT ? 127 : (int)stage[scale_off + j * 64];  // per-tensor: every block scale is 2^0
   return f;
 }
 
-template <class LY, int FA, int FB>
+template <class LY, int FA, int FB, bool PT = false>
 __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN][LY::FRM], const ReadOffsets& ro) {
   Frag bop[LY::FRM];
 #pragma unroll
-  for (int j = 0; j < LY::FRM; ++j) bop[j] = read_frag(stage, ro.a_data, ro.a_data2, ro.a_scale, j);
+  for (int j = 0; j < LY::FRM; ++j) bop[j] = read_frag<PT>(stage, ro.a_data, ro.a_data2, ro.a_scale, j);
 #pragma unroll
   for (int i = 0; i < LY::FRN; ++i) {
-    const Frag aop = read_frag(stage, ro.b_data, ro.b_data2, ro.b_scale, i);
+    const Frag aop = read_frag<PT>(stage, ro.b_data, ro.b_data2, ro.b_scale, i);
 #pragma unroll
     for (int j = 0; j < LY::FRM; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop.v, bop[j].v, acc[i][j], MfmaFmt<FB>::v,
@@ -246,7 +247,7 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN
 // for much of a step.  In the big tile the copiers are waves 4-7, one per
 // SIMD, and the other wave of each SIMD keeps the MFMA pipe busy meanwhile
 // (measured: 8192^3 GEMM ~10% faster than with all 8 waves copying).
-template <class LY, int FA, int FB>
+template <class LY, int FA, int FB, bool PT = false>
 __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::FRM], const Operand& A,
                                          const Operand& B, int64_t K, int wave, int lane) {
   const int wm = wave / LY::NWN, wn = wave % LY::NWN;
@@ -261,13 +262,13 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
   const CopyOffsets off = copy_offsets(K, copier ? c : 0, lane);
   const ReadOffsets ro = read_offsets<LY>(wm, wn, lane);
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-  if (copier) load_stage<LY>(lds_addr, A, B, off, K, 0, c);
+  if (copier) load_stage<LY, PT>(lds_addr, A, B, off, K, 0, c);
   for (int kt = 0; kt < kt_n; ++kt) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (copier && kt + 1 < kt_n) load_stage<LY>(lds_addr + ((kt + 1) & 1) * LY::kStage, A, B, off, K, kt + 1, c);
+    if (copier && kt + 1 < kt_n) load_stage<LY, PT>(lds_addr + ((kt + 1) & 1) * LY::kStage, A, B, off, K, kt + 1, c);
 
-    compute<LY, FA, FB>(lds + (kt & 1) * LY::kStage, acc, ro);
+    compute<LY, FA, FB, PT>(lds + (kt & 1) * LY::kStage, acc, ro);
   }
 }
 
@@ -410,10 +411,15 @@ struct GemmParams {
   const int32_t* m_splits;  // grouped only
   int32_t groups;           // grouped only
   uint8_t* d_scale;         // MXFP8 output only: E8M0 scales [M, N/32]
+  const float* alpha_a;     // per-tensor FP8 only: a_scale_inv and b_scale_inv (device scalars)
+  const float* alpha_b;
 };
 
 // Dense: one workgroup per tile.
-template <class LY, int FA, int FB, int EPI, int OUT>
+// PT: per-tensor FP8 operands (no block scales): every MFMA block scale is
+// 2^0 and the accumulators are multiplied by alpha = a_scale_inv * b_scale_inv
+// before the epilogue.
+template <class LY, int FA, int FB, int EPI, int OUT, bool PT = false>
 __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
   constexpr int BM = LY::BM, BN = LY::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
@@ -437,7 +443,17 @@ __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
   const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, BM);
   const Operand B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, BN);
   v4f acc[LY::FRN][LY::FRM];
-  mainloop<LY, FA, FB>(lds, acc, A, B, p.K, wave, lane);
+  mainloop<LY, FA, FB, PT>(lds, acc, A, B, p.K, wave, lane);
+  if constexpr (PT) {
+    // these products are rounded on their own: with contraction off here the
+    // epilogue's bias add stays a second rounding instead of becoming an FMA
+#pragma clang fp contract(off)
+    const float alpha = *p.alpha_a * *p.alpha_b;
+#pragma unroll
+    for (int i = 0; i < LY::FRN; ++i)
+#pragma unroll
+      for (int j = 0; j < LY::FRM; ++j) acc[i][j] *= alpha;
+  }
   if constexpr (OUT == TE_E4M3 || OUT == TE_E5M2)
     epilogue_mx<LY, EPI, OUT>(acc, static_cast<uint8_t*>(p.d), p.d_scale, p.aux, p.bias, m0, p.M, n0, p.N, wave,
                               lane);
@@ -515,6 +531,32 @@ template <class C, bool GROUPED, int FA, int FB, int EPI>
 te_status launch4(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stream) {
   return out == TE_BF16 ? launch5<C, GROUPED, FA, FB, EPI, TE_BF16>(p, grid, stream)
                         : launch5<C, GROUPED, FA, FB, EPI, TE_FP32>(p, grid, stream);
+}
+
+template <class C, int FA, int FB, int EPI>
+te_status launch_pt4(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stream) {
+  if (out == TE_BF16)
+    hipLaunchKernelGGL((mx_gemm_kernel<C, FA, FB, EPI, TE_BF16, true>), grid, dim3(C::kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<C, FA, FB, EPI, TE_FP32, true>), grid, dim3(C::kThreads), 0, stream, p);
+  return launch_status();
+}
+
+template <class C, int FA, int FB>
+te_status launch_pt3(const GemmParams& p, te_epilogue epi, te_dtype out, dim3 grid, hipStream_t stream) {
+  switch (epi) {
+    case TE_EPI_NONE: return launch_pt4<C, FA, FB, TE_EPI_NONE>(p, out, grid, stream);
+    case TE_EPI_BIAS: return launch_pt4<C, FA, FB, TE_EPI_BIAS>(p, out, grid, stream);
+    default: return launch_pt4<C, FA, FB, TE_EPI_BIAS_GELU_AUX>(p, out, grid, stream);
+  }
+}
+
+template <class C>
+te_status launch_pt(const GemmParams& p, te_dtype fa, te_dtype fb, te_epilogue epi, te_dtype out, dim3 grid,
+                    hipStream_t stream) {
+  if (fa == TE_E4M3 && fb == TE_E4M3) return launch_pt3<C, TE_E4M3, TE_E4M3>(p, epi, out, grid, stream);
+  if (fa == TE_E5M2 && fb == TE_E4M3) return launch_pt3<C, TE_E5M2, TE_E4M3>(p, epi, out, grid, stream);
+  return launch_pt3<C, TE_E4M3, TE_E5M2>(p, epi, out, grid, stream);
 }
 
 template <class C, int FA, int FB, int EPI>
@@ -658,6 +700,34 @@ extern "C" te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scal
     return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_fmt,
                                  dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))), stream);
   return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_fmt, dim3((unsigned)big_tiles), stream);
+}
+
+extern "C" te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_dtype a_fmt, const uint8_t* b,
+                                 const float* b_scale_inv, te_dtype b_fmt, int64_t M, int64_t N, int64_t K, void* d,
+                                 te_dtype d_dtype, te_epilogue epi, const uint16_t* bias, uint16_t* aux,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  TE_REQUIRE(epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX, TE_ERR_VALUE);
+  TE_REQUIRE(M >= 0 && N >= 0 && K >= 0, TE_ERR_SHAPE);
+  TE_REQUIRE(K % 128 == 0 && M % 16 == 0 && N % 16 == 0, TE_ERR_SHAPE);
+  TE_REQUIRE(M <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 31) - BK,
+             TE_ERR_SHAPE);
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  TE_REQUIRE(((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 31), TE_ERR_SHAPE);
+  // the scale pointers stand in for the block-scale arrays in the common checks
+  te_status st = check_common(a, reinterpret_cast<const uint8_t*>(a_scale_inv), a_fmt, b,
+                              reinterpret_cast<const uint8_t*>(b_scale_inv), b_fmt, d, d_dtype, epi, bias, aux,
+                              M > 0 && N > 0, K > 0);
+  if (st != TE_OK) return st;
+  if (M == 0 || N == 0) return TE_OK;
+  TE_REQUIRE(a_scale_inv != nullptr && b_scale_inv != nullptr, TE_ERR_NULL);
+  // the block-scale descriptors are never read in per-tensor mode; they point at the data
+  GemmParams p{a, a, b, b, d, bias, aux, M, N, K, nullptr, 0, nullptr, a_scale_inv, b_scale_inv};
+  if (use_small_tile(big_tiles, K))
+    return launch_pt<Small>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))),
+                            stream);
+  return launch_pt<Big>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)big_tiles), stream);
 }
 
 extern "C" te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_splits, int64_t total_m,

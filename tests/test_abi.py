@@ -165,6 +165,46 @@ def test_gemm_mxout_validation():
     assert mxout(M=0, d=None, ds=None) == te.TE_OK
 
 
+def delayed(x=P, n=64, fmt=te.TE_E4M3, q=P2, qinv=P3, scale=P3, hist=P3, L=16, algo=te.TE_AMAX_MAX, margin=0,
+            ws=P, ws_bytes=4096):
+    return L_.te_fp8_cast_delayed_scaling(x, n, fmt, q, qinv, scale, hist, L, algo, margin, ws, ws_bytes, None)
+
+
+L_ = L
+
+
+def test_delayed_scaling_validation():
+    assert delayed(fmt=te.TE_BF16) == te.TE_ERR_DTYPE
+    assert delayed(algo=2) == te.TE_ERR_VALUE
+    assert delayed(margin=-1) == te.TE_ERR_VALUE
+    assert delayed(L=0) == te.TE_ERR_SHAPE and delayed(L=1025) == te.TE_ERR_SHAPE
+    assert delayed(n=-8) == te.TE_ERR_SHAPE
+    assert delayed(scale=None) == te.TE_ERR_NULL
+    assert delayed(hist=None) == te.TE_ERR_NULL
+    assert delayed(qinv=None) == te.TE_ERR_NULL
+    assert delayed(ws=None) == te.TE_ERR_NULL
+    assert delayed(q=None) == te.TE_ERR_NULL
+    assert delayed(x=BAD) == te.TE_ERR_ALIGN
+    assert delayed(scale=P3 + 2) == te.TE_ERR_ALIGN
+    assert delayed(ws_bytes=0) == te.TE_ERR_WORKSPACE
+
+
+def fp8gemm(a=P, sa=P3, fa=te.TE_E4M3, b=P, sb=P3, fb=te.TE_E4M3, M=256, N=256, K=256, d=P2, dt=te.TE_BF16,
+            epi=te.TE_EPI_NONE, bias=None, aux=None):
+    return L.te_fp8_gemm(a, sa, fa, b, sb, fb, M, N, K, d, dt, epi, bias, aux, None, 0, None)
+
+
+def test_fp8_gemm_validation():
+    assert fp8gemm(K=192) == te.TE_ERR_SHAPE
+    assert fp8gemm(epi=te.TE_EPI_DGELU, aux=P3) == te.TE_ERR_VALUE
+    assert fp8gemm(fa=te.TE_E5M2, fb=te.TE_E5M2) == te.TE_ERR_DTYPE
+    assert fp8gemm(dt=te.TE_E4M3) == te.TE_ERR_DTYPE
+    assert fp8gemm(sa=None) == te.TE_ERR_NULL
+    assert fp8gemm(sb=P3 + 2) == te.TE_ERR_ALIGN
+    assert fp8gemm(epi=te.TE_EPI_BIAS) == te.TE_ERR_NULL
+    assert fp8gemm(M=0, d=None) == te.TE_OK
+
+
 def grouped(G=4, splits=P3, T=1024, a=P, sa=P, fa=te.TE_E4M3, b=P, sb=P, fb=te.TE_E4M3, N=256, K=256, d=P2,
             dt=te.TE_BF16, epi=te.TE_EPI_NONE, bias=None, aux=None):
     return L.te_mxfp8_grouped_gemm(G, splits, T, a, sa, fa, b, sb, fb, N, K, d, dt, epi, bias, aux, None, 0, None)

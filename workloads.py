@@ -83,6 +83,7 @@ class GemmSpec:
     b_dir: str = "row"
     bias: TensorSpec | None = None
     mx_out: bool = False        # D written as a rowwise MXFP8 operand (fmt_a of the consumer) instead of bf16
+    scaling: str = "mx"         # "mx": MXFP8 operands; "delayed": per-tensor FP8 cast with delayed scaling
     a_from: str | None = None   # A is the MXFP8 output of this earlier GEMM (a_src is then unused)
 
     @property
@@ -154,6 +155,15 @@ def decoder_forward_mx() -> Workload:
     ])
 
 
+def decoder_forward_delayed() -> Workload:
+    """The decoder forward with the other recipe: per-tensor FP8 operands cast
+    with delayed scaling (amax history 16, "max", margin 0) and per-tensor
+    FP8 GEMMs."""
+    from dataclasses import replace
+    return Workload("decoder_fwd_delayed_4096x1024",
+                    gemms=[replace(g, scaling="delayed") for g in decoder_forward().gemms])
+
+
 def large_square() -> Workload:
     """M = N = K = 8192 fprop, 1% outlier K-columns on both operands, plus
     standalone rowwise and columnwise quantization of both inputs."""
@@ -201,5 +211,6 @@ def moe_grouped() -> Workload:
         TensorSpec(5, 1, (T, K), 1.0), TensorSpec(5, 2, (E * N, K), 0.02), TensorSpec(5, 3, (E, N), 0.02))])
 
 
-ALL = {"tiny": tiny, "decoder_fwd": decoder_forward, "decoder_fwd_mx": decoder_forward_mx, "square_8192": large_square,
+ALL = {"tiny": tiny, "decoder_fwd": decoder_forward, "decoder_fwd_mx": decoder_forward_mx,
+       "decoder_fwd_delayed": decoder_forward_delayed, "square_8192": large_square,
        "hybrid_bwd": hybrid_backward, "hybrid_bwd_fused": hybrid_backward_fused, "moe_grouped": moe_grouped}
