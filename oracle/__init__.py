@@ -41,6 +41,7 @@ from .mx import block_scale_code, quantize_rowwise, quantize_colwise, dequantize
 from .current_scaling import amax, current_scale, cast_current_scaling
 from .bgrad import column_sums, column_abs_sums
 from .delayed_scaling import delayed_scaling_step, next_scale, fp8_gemm_per_tensor
+from .blockwise import quantize_1d, quantize_2d, block_gemm, pow2_at_least, e8m0_of
 from .gemm import mx_gemm, gelu_tanh, dgelu_tanh, epilogue, grouped_mx_gemm, within_tolerance, tolerance_bound
 
 __all__ = [
