@@ -89,6 +89,12 @@ typedef enum { TE_ROWWISE = 1, TE_COLWISE = 2, TE_BOTH = 3 } te_qdir;
 
 typedef enum { TE_AMAX_MAX = 0, TE_AMAX_MOST_RECENT = 1 } te_amax_algo;
 
+/* How the blockwise FP8 GEMM applies its FP32 block scales. */
+typedef enum {
+  TE_BLOCK_SCALES_E8M0 = 0, /* cast to E8M0 (smallest power of two >= s) first: the gfx950 default */
+  TE_BLOCK_SCALES_FP32 = 1  /* the FP32 scales themselves */
+} te_block_scaling;
+
 /* Human-readable name of a status code (static storage). */
 const char* te_status_str(te_status status);
 
@@ -297,6 +303,60 @@ te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_splits, int
                                 void* d, te_dtype d_dtype, te_epilogue epi,
                                 const uint16_t* bias, uint16_t* aux,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Blockwise FP8 scales cast to MXFP8 scales ([ROCm-TE] "Blockwise FP8 GEMM
+ * support on ROCm": on gfx950 the blockwise GEMM computes with the FP32
+ * scales cast to E8M0).  A blockwise operand [rows, cols] carries one FP32
+ * scale inverse per 1 x 128 block (1-D) or per 128 x 128 block (2-D); its
+ * value is code * scale_inv.  Each scale s becomes the E8M0 code of the
+ * smallest power of two >= s, saturating at 2^127 (+inf included); +-0 and
+ * values up to 2^-127 give 2^-127 (code 0); NaN and negative values give
+ * the E8M0 NaN code 255.  Every 32-block inherits its 128-block's code, so
+ * the codes with these scales form an MXFP8 operand (exact when every s is
+ * a power of two, as the recipe's own scales are).
+ *   scale_inv  float [rows, cols/128] (block_2d = 0) or
+ *              [ceil(rows/128), cols/128] (block_2d = 1); 4-byte aligned
+ *   mx_scale   uint8 [rows, cols/32] E8M0, 4-byte aligned (written)
+ *   Shapes: rows >= 0, cols >= 0, cols % 128 == 0; empty enqueues nothing.
+ */
+te_status te_fp8_block_scales_to_mx(const float* scale_inv, int64_t rows, int64_t cols, int block_2d,
+                                    uint8_t* mx_scale, hipStream_t stream);
+
+/*
+ * Blockwise FP8 GEMM, "TN" ([ROCm-TE] "Blockwise FP8 GEMM support on ROCm
+ * (gfx942 and gfx950)": 1-D x 2-D or 1-D x 1-D block scaling, E4M3 / E5M2
+ * inputs except E5M2 x E5M2, bias and DGELU epilogues; an E8M0-cast kernel
+ * by default and a kernel taking the FP32 scales):
+ *   D[m, n] = epi( sum_kb sa[m, kb] * sb[n, kb] * sum_{k in kb} val(a[m, k]) * val(b[n, k]) )
+ * with fp32 accumulation, K blocks kb of 128, and sb read at row n / 128
+ * when b_block_2d.
+ *   a            uint8 [M, K] codes, a_scale_inv float [M, K/128] (1-D blocks)
+ *   b            uint8 [N, K] codes, b_scale_inv float [N, K/128]
+ *                (b_block_2d = 0) or [ceil(N/128), K/128] (b_block_2d = 1)
+ *   mode         TE_BLOCK_SCALES_E8M0: sa and sb are first cast as
+ *                te_fp8_block_scales_to_mx casts them (into the workspace),
+ *                then the MXFP8 GEMM runs: the result is te_mxfp8_gemm's on
+ *                those operands.
+ *                TE_BLOCK_SCALES_FP32: each K block's product is computed
+ *                with unit scales and added to the fp32 accumulator times
+ *                fl32(sa * sb) with one fused multiply-add; no workspace.
+ *   d, d_dtype, epi, bias, aux: as te_mxfp8_gemm (every epilogue).
+ *   Shapes as te_mxfp8_gemm: K % 128 == 0, M % 16 == 0, N % 16 == 0.
+ *   Scale pointers are 4-byte aligned and may be NULL when M, N or K is 0.
+ *   workspace    te_fp8_block_gemm_workspace_size(M, N, K, mode) bytes
+ *                (0 for TE_BLOCK_SCALES_FP32), 16-byte aligned; holds the
+ *                E8M0 scales of A, then (at the next 256-byte boundary)
+ *                those of B.  It must not be in use by other work on the
+ *                device while the call's kernels run.
+ */
+size_t te_fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K, te_block_scaling mode);
+te_status te_fp8_block_gemm(const uint8_t* a, const float* a_scale_inv, te_dtype a_fmt,
+                            const uint8_t* b, const float* b_scale_inv, te_dtype b_fmt, int b_block_2d,
+                            int64_t M, int64_t N, int64_t K,
+                            void* d, te_dtype d_dtype, te_epilogue epi,
+                            const uint16_t* bias, uint16_t* aux, te_block_scaling mode,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,8 @@ TE_EPI_NONE, TE_EPI_BIAS, TE_EPI_BIAS_GELU_AUX, TE_EPI_DGELU, TE_EPI_ACCUMULATE 
 TE_ROWWISE, TE_COLWISE, TE_BOTH = 1, 2, 3
 TE_AMAX_MAX, TE_AMAX_MOST_RECENT = 0, 1
 AMAX_ALGOS = {"max": TE_AMAX_MAX, "most_recent": TE_AMAX_MOST_RECENT}
+TE_BLOCK_SCALES_E8M0, TE_BLOCK_SCALES_FP32 = 0, 1
+BLOCK_SCALINGS = {"e8m0": TE_BLOCK_SCALES_E8M0, "fp32": TE_BLOCK_SCALES_FP32}
 
 FORMATS = {"e4m3": TE_E4M3, "e5m2": TE_E5M2}
 EPILOGUES = {"none": TE_EPI_NONE, "bias": TE_EPI_BIAS, "bias_gelu_aux": TE_EPI_BIAS_GELU_AUX,
@@ -54,6 +56,11 @@ _SIGS = {
                                            _vp, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
     "te_mxfp8_grouped_gemm": (ctypes.c_int, [_i32, _vp, _i64, _vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int,
                                              _i64, _i64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
+    "te_fp8_block_scales_to_mx": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
+    "te_fp8_block_gemm_workspace_size": (_sz, [_i64, _i64, _i64, ctypes.c_int]),
+    "te_fp8_block_gemm": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64, _i64,
+                                         _i64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _sz,
+                                         _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -191,6 +198,32 @@ def te_mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n: int
         _stream(stream)))
 
 
+def _block_scaling(mode) -> int:
+    return BLOCK_SCALINGS[mode] if isinstance(mode, str) else int(mode)
+
+
+def te_fp8_block_scales_to_mx(scale_inv, rows: int, cols: int, block_2d: bool, mx_scale, stream=None) -> None:
+    _check("te_fp8_block_scales_to_mx", _lib.te_fp8_block_scales_to_mx(
+        _ptr(scale_inv), int(rows), int(cols), int(bool(block_2d)), _ptr(mx_scale), _stream(stream)))
+
+
+def te_fp8_block_gemm_workspace_size(M: int, N: int, K: int, mode="e8m0") -> int:
+    return int(_lib.te_fp8_block_gemm_workspace_size(M, N, K, _block_scaling(mode)))
+
+
+def te_fp8_block_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, b_block_2d, d, epilogue="none", bias=None,
+                      aux=None, mode="e8m0", workspace=None, stream=None) -> None:
+    M, K = a.shape
+    N = b.shape[0]
+    d_dtype = TE_BF16 if d.dtype == torch.bfloat16 else TE_FP32
+    epi = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("te_fp8_block_gemm", _lib.te_fp8_block_gemm(
+        _ptr(a), _ptr(a_scale_inv), _fmt(a_fmt), _ptr(b), _ptr(b_scale_inv), _fmt(b_fmt), int(bool(b_block_2d)),
+        M, N, K, _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _block_scaling(mode), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
 # ------------------------------------------------------- allocating helpers
 
 def mxfp8_quantize(x, fmt="e4m3", direction="row", stream=None):
@@ -303,4 +336,28 @@ def mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n, epilog
     if epilogue == "bias_gelu_aux":
         aux = torch.empty((total_m, n), dtype=torch.bfloat16, device=a.device)
     te_mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n, d, epilogue, bias, aux, None, stream)
+    return d, (aux if epilogue == "bias_gelu_aux" else None)
+
+
+def fp8_block_scales_to_mx(scale_inv, rows: int, cols: int, block_2d: bool, stream=None):
+    """FP32 block scale inverses -> E8M0 MXFP8 scales uint8 [rows, cols/32]."""
+    out = torch.empty((rows, cols // 32), dtype=torch.uint8, device=scale_inv.device)
+    te_fp8_block_scales_to_mx(scale_inv, rows, cols, block_2d, out, stream)
+    return out
+
+
+def fp8_block_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, b_block_2d=True, epilogue="none", bias=None,
+                   out_dtype=torch.bfloat16, aux=None, out=None, mode="e8m0", workspace=None, stream=None):
+    """Blockwise FP8 GEMM -> (D, aux); scale inverses float [M, K/128] for A and [N, K/128] (1-D) or
+    [ceil(N/128), K/128] (2-D) for B; mode "e8m0" (scales cast to powers of two) or "fp32"."""
+    M, K = a.shape
+    N = b.shape[0]
+    d = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=a.device)
+    if epilogue == "bias_gelu_aux":
+        aux = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    if workspace is None:
+        ws_bytes = te_fp8_block_gemm_workspace_size(M, N, K, mode)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device) if ws_bytes else None
+    te_fp8_block_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, b_block_2d, d, epilogue, bias, aux, mode,
+                      workspace, stream)
     return d, (aux if epilogue == "bias_gelu_aux" else None)

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtemx.so")
-SOURCES = ["quantize.hip", "amax_cast.hip", "gemm.hip", "status.hip"]
+SOURCES = ["quantize.hip", "amax_cast.hip", "gemm.hip", "block_gemm.hip", "block_scale.hip", "status.hip"]
 ARCH = "gfx950"
 
 
@@ -38,17 +38,20 @@ def compile_flags() -> list[str]:
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libtemx.so; returns its path."""
-    objs = []
     obj_dir = os.path.join(PKG, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     cc = hipcc()
-    for src in SOURCES:
+    objs, procs = [], []
+    for src in SOURCES:  # compiled in parallel (the GEMM sources take the longest)
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
         cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        procs.append((src, subprocess.Popen(cmd)))
         objs.append(obj)
+    failed = [src for src, proc in procs if proc.wait() != 0]
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -1,0 +1,634 @@
+// MXFP8 GEMM ("TN": A [M, K], B [N, K], D = A . B^T) with bias / GELU(tanh) /
+// GELU-aux epilogues, dense and grouped, for gfx950.
+//
+// Method: "HipKittens MXFP8 GEMM Support" (ROCm/TransformerEngine PR #566):
+// an MXFP8 GEMM with BIAS and GELU AUX epilogues; review threads: 1-D MXFP8
+// scaling, K % 128 == 0, M % 16 == 0, N % 16 == 0, "TN" operands.  GELU is
+// the tanh approximation ("Getting Started", TE JAX quickstart).  The grouped
+// form is the single-launch grouped GEMM of "Transformer Engine On ROCm and
+// AMDGPU" ("Grouped GEMM using CK_Tile").
+//
+// Design for CDNA4:
+// * v_mfma_scale_f32_16x16x128_f8f6f4 consumes the fp8 codes and the E8M0
+//   block scales directly.  Its operand layout (lane l = 16 g + r holds row r,
+//   bytes 0-15 = K 16g..16g+15 and bytes 16-31 = K 64+16g..; the scale byte
+//   of K-block kb comes from lane r + 16 kb) means a lane loads two 16-byte
+//   chunks of one row and supplies the scale of block g of that row.
+// * The MFMA's A operand is a B-tile row (n) and its B operand an A-tile row
+//   (m), so each lane ends with 4 consecutive output columns of one row: the
+//   epilogue stores 8 bytes (bf16) per lane straight from registers.
+// * 256 x 256 workgroup tile, 8 waves in 4 x 2 (two per SIMD), 64 x 128 per
+//   wave (4 x 8 MFMA tiles = 128 fp32 accumulators per lane), K step 128;
+//   a 128 x 128 tile (4 waves of 64 x 64) for grids the big tile cannot fill.
+// * A, B and their scale tiles are copied global -> LDS with direct-to-LDS
+//   buffer loads (buffer_load_dwordx4 / _dword ... lds), double-buffered
+//   (2 x 66 KB), issued by one wave per SIMD.
+// * Workgroup -> tile mapping is XCD-aware: workgroups are dealt round-robin
+//   to the 8 XCDs, so each XCD is given a contiguous run of tiles (grouped in
+//   bands of 4 row-tiles) and its L2 sees the reuse.
+// * Ragged M / N tails: each tile's copies go through buffer resources that
+//   cover only its valid rows, so rows past the end read as zeros; stores are
+//   masked.  The workspace is 0 bytes.
+#pragma once
+
+#include "temx_device.h"
+
+namespace temx {
+namespace {
+
+constexpr int BK = 128;
+
+// How the operands are scaled (a template parameter of the kernels):
+//   SM_MX   MXFP8: E8M0 scale bytes [rows, K/32], applied by the MFMA itself.
+//   SM_PT   per-tensor: no block scales; the MFMA scales are 2^0 and the
+//           accumulators are multiplied by a_scale_inv * b_scale_inv at the end.
+//   SM_FS1  blockwise FP8 with FP32 scale inverses, one per 1 x 128 block
+//           ([rows, K/128] floats) for both operands: each 128-deep MFMA is
+//           one K block, computed with unit scales and added to the
+//           accumulators times sa[m, kb] * sb[n, kb].
+//   SM_FS2  as SM_FS1, but B has one scale per 128 x 128 block
+//           ([ceil(N/128), K/128] floats).
+// A [rows, K/128] float array has the row stride of a [rows, K/32] byte
+// array and holds block kt of a row at byte 4 kt, where the E8M0 bytes of
+// step kt sit: the stage copies move either kind of scale unchanged, and in
+// LDS each tile row has 4 scale bytes per stage (four E8M0 codes, or one float).
+constexpr int SM_MX = 0, SM_PT = 1, SM_FS1 = 2, SM_FS2 = 3;
+constexpr bool fp32_scales(int sm) { return sm == SM_FS1 || sm == SM_FS2; }
+
+// Workgroup tile configurations.  A BM x BN tile is computed by NWM x NWN
+// waves, each a (BM / NWM) x (BN / NWN) block of FRM x FRN MFMA tiles of
+// 16 x 16; the last NCOPY waves issue the stage copies.  One stage in LDS is
+// A data [BM][128], B data [BN][128], A scales [BM][4], B scales [BN][4];
+// two stages.
+//   Big:   256 x 256, 8 waves of 64 x 128 (two per SIMD, 128 accumulators),
+//          waves 4-7 copy; 132 KB of LDS, one workgroup per CU.
+//   Small: 128 x 128, 4 waves of 64 x 64 (64 accumulators), all four copy;
+//          66 KB of LDS, two workgroups per CU.  For grids the big tile
+//          cannot fill (few or ragged row tiles).
+template <int BM_, int BN_, int NWM_, int NWN_, int NCOPY_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_, NW = NWM * NWN, kThreads = 64 * NW;
+  static constexpr int NCOPY = NCOPY_;
+  static constexpr int WTM = BM / NWM, WTN = BN / NWN;
+  static constexpr int FRM = WTM / 16, FRN = WTN / 16;
+  static constexpr int kAData = BM * BK, kBData = BN * BK, kAScale = BM * 4, kBScale = BN * 4;
+  static constexpr int kOffBData = kAData;
+  static constexpr int kOffAScale = kAData + kBData;
+  static constexpr int kOffBScale = kOffAScale + kAScale;
+  static constexpr int kStage = kOffBScale + kBScale;
+  static constexpr int kLds = 2 * kStage;
+  static_assert(BM == BN, "one row clamp and one copy scheme serve both operands");
+  static_assert(NCOPY % 2 == 0 && (BM / 8) % NCOPY == 0 && (BM / 64) <= NCOPY, "copy slices per copier wave");
+};
+using Big = Cfg<256, 256, 4, 2, 4>;
+using Small = Cfg<128, 128, 2, 2, 4>;
+constexpr int kGroupM = 4;      // row-tile band of the raster order
+constexpr int kMaxGroups = 1024;
+
+// LDS data tile of one operand and stage: [BM rows][128 bytes] (the step's
+// 128 K bytes of each row).  The eight 16-byte chunks of row r are permuted
+// by chunk ^ swz(r).  A fragment read has lane 16 g + r fetch logical chunks
+// g and g + 4 of row r; with swz(r) = (r >> 1) & 7 these ds_read_b128 run
+// without bank conflicts on gfx950 (measured: 4.2 clocks per wave
+// instruction, the same as a linear 1-KB read; unswizzled 128-byte rows take
+// 14.5).  Chunk g + 4 is at chunk g's address XOR 64.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+template <int F> struct MfmaFmt;  // cbsz / blgp operand format codes
+template <> struct MfmaFmt<TE_E4M3> { static constexpr int v = 0; };
+template <> struct MfmaFmt<TE_E5M2> { static constexpr int v = 1; };
+
+// An operand tile as two buffer resources: rows [row0, row0 + rows) of the
+// data [*, K] and of the scales [*, K/32].  Reads past the valid rows (ragged
+// M / N / expert tails) return zeros from the buffer range check.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+struct Operand {
+  i32x4 data;
+  i32x4 scale;
+};
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw byte buffer, 32-bit data format (gfx9 descriptor word 3)
+
+// The descriptor must live in SGPRs; its inputs are uniform over the wave
+// (tile coordinates), which readfirstlane states for the compiler.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane((int)bytes), kRsrcWord3};
+}
+
+__device__ __forceinline__ Operand make_operand(const uint8_t* data, const uint8_t* scale, int64_t row0,
+                                                int64_t rows, int64_t K, int64_t tile_rows) {
+  rows = rows < 0 ? 0 : (rows > tile_rows ? tile_rows : rows);
+  return Operand{make_rsrc(data + row0 * K, rows * K), make_rsrc(scale + row0 * (K / 32), rows * (K / 32))};
+}
+
+// B of SM_FS2: one scale row (K/128 floats = K/32 bytes) per 128 data rows;
+// row0 is a multiple of 128.
+__device__ __forceinline__ Operand make_operand_2d(const uint8_t* data, const uint8_t* scale, int64_t row0,
+                                                   int64_t rows, int64_t K, int64_t tile_rows) {
+  rows = rows < 0 ? 0 : (rows > tile_rows ? tile_rows : rows);
+  return Operand{make_rsrc(data + row0 * K, rows * K),
+                 make_rsrc(scale + (row0 / 128) * (K / 32), ((rows + 127) / 128) * (K / 32))};
+}
+
+// Direct-to-LDS buffer loads (buffer_load_dword{,x4} ... lds): lane l's
+// bytes land at LDS address m0 + size * l.  They are issued from inline asm
+// so that the compiler, which cannot tell the stage being filled from the
+// stage being read, does not wait for them before every LDS read; the K loop
+// orders them itself (s_waitcnt vmcnt(0) + barrier before a stage is read).
+// m0 is saved and restored around the copy (the LDS base is read at issue).
+__device__ __forceinline__ void lds_dma16(const i32x4& rsrc, uint32_t lds_addr, int voff, int soff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_dma4(const i32x4& rsrc, uint32_t lds_addr, int voff, int soff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+// Per-lane byte offsets of the tile copies.  A copy instruction fills one
+// 1-KB slice: rows 8 q .. 8 q + 7, lane l landing at LDS byte 16 l, i.e. row
+// 8 q + l/8, physical chunk l % 8, which holds logical chunk
+// (l % 8) ^ swz(8 q + l/8) = (l % 8) ^ (l / 16) ^ (4 if q is odd).  Each
+// instruction reads 8 whole 128-byte lines.  The BM/8 slices of an operand
+// tile are dealt to the NCOPY copier waves as q = c + NCOPY i; with NCOPY
+// even, q has copier c's parity, so one per-lane offset plus the uniform
+// 8 NCOPY i K + 128 kt serves every copy.  Scale slices are rows
+// 64 s .. 64 s + 63 of the BM x 4-byte scale tile; copier c < BM/64 copies
+// scale slice c of both operands.
+struct CopyOffsets {
+  int data;
+  int scale;
+  int scale_2d;  // SM_FS2 B scales: rows 64 c .. 64 c + 63 all lie in 128-row block c / 2
+};
+
+__device__ __forceinline__ CopyOffsets copy_offsets(int64_t K, int c, int lane) {
+  const int chunk = (lane & 7) ^ (lane >> 4) ^ ((c & 1) << 2);
+  CopyOffsets o;
+  o.data = (int)((8 * c + (lane >> 3)) * K) + chunk * 16;
+  o.scale = (int)((64 * c + lane) * (K / 32));
+  o.scale_2d = (int)((c >> 1) * (K / 32));
+  return o;
+}
+
+template <class C, int SM = SM_MX>
+__device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, const Operand& B,
+                                           const CopyOffsets& off, int64_t K, int kt, int c) {
+#pragma unroll
+  for (int i = 0; i < C::BM / 8 / C::NCOPY; ++i) {
+    const int q = c + C::NCOPY * i;
+    const int so = (int)(8 * C::NCOPY * i * K) + kt * BK;
+    lds_dma16(A.data, stage + q * 1024, off.data, so);
+    lds_dma16(B.data, stage + C::kOffBData + q * 1024, off.data, so);
+  }
+  if (SM != SM_PT && c < C::BM / 64) {
+    lds_dma4(A.scale, stage + C::kOffAScale + c * 256, off.scale, kt * 4);
+    lds_dma4(B.scale, stage + C::kOffBScale + c * 256, SM == SM_FS2 ? off.scale_2d : off.scale, kt * 4);
+  }
+}
+
+struct Frag {
+  v8i v;
+  int s;
+};
+
+// Per-lane LDS read offsets of a wave, computed once.  Fragment j of a
+// wave's 128 rows is 16 j rows further (1 KB of data, 64 B of scales), which
+// the reads take as immediate offsets.  The empty asm statement keeps each
+// offset a single opaque VGPR so that the compiler does not re-associate it
+// into per-fragment address registers.
+struct ReadOffsets {
+  int a_data, a_data2, b_data, b_data2, a_scale, b_scale;
+};
+
+// With FP32 scales, a_scale is the float of row r (fragment j: + 64 bytes)
+// and b_scale the four floats of columns 4 g .. 4 g + 3 (SM_FS1; fragment i:
+// + 64 bytes) or the one float of the wave's 128-row block of B (SM_FS2:
+// a wave's columns never straddle a 128 boundary).
+template <class LY, int SM = SM_MX>
+__device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) {  // LY: a Cfg
+  const int g = lane >> 4, r = lane & 15;
+  const int lane_off = r * BK + ((g ^ swz(r)) << 4);
+  ReadOffsets o;
+  o.a_data = wm * LY::WTM * BK + lane_off;
+  o.a_data2 = o.a_data ^ 64;
+  o.b_data = LY::kOffBData + wn * LY::WTN * BK + lane_off;
+  o.b_data2 = o.b_data ^ 64;
+  if constexpr (fp32_scales(SM)) {
+    static_assert(128 % LY::WTN == 0, "a wave's columns stay inside one 128-row block of B");
+    o.a_scale = LY::kOffAScale + (wm * LY::WTM + r) * 4;
+    o.b_scale = LY::kOffBScale + (wn * LY::WTN + (SM == SM_FS1 ? 4 * g : 0)) * 4;
+  } else {
+    o.a_scale = LY::kOffAScale + (wm * LY::WTM + r) * 4 + g;
+    o.b_scale = LY::kOffBScale + (wn * LY::WTN + r) * 4 + g;
+  }
+  asm volatile("" : "+v"(o.a_data), "+v"(o.a_data2), "+v"(o.b_data), "+v"(o.b_data2), "+v"(o.a_scale),
+               "+v"(o.b_scale));
+  return o;
+}
+
+// Fragment j: two 16-byte chunks (K 16g.. and 64 + 16g.. of the step) of row
+// 16 j + r of the wave's rows, and the E8M0 byte of block g of that row,
+// read on its own (ds_read_u8; the four lanes of a row share one dword, a
+// broadcast).  No ALU work depends on the scale read, so its wait lands at the
+// MFMA that uses it (measured: 2-12% faster across the GEMM shapes than
+// shifting the byte out of the row's scale word).  Rows 16 j further are 2 KB
+// further (an immediate offset).
+template <bool UNIT = false>
+__device__ __forceinline__ Frag read_frag(const uint8_t* stage, int data_off, int data_off2, int scale_off, int j) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(stage + data_off + j * 16 * BK);
+  const uint4 hi = *reinterpret_cast<const uint4*>(stage + data_off2 + j * 16 * BK);
+  Frag f;
+  f.v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  f.s = UNIT ? 127 : (int)stage[scale_off + j * 64];  // unit: every MFMA block scale is 2^0
+  return f;
+}
+
+template <class LY, int FA, int FB, int SM = SM_MX>
+__device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN][LY::FRM], const ReadOffsets& ro) {
+  constexpr bool UNIT = SM != SM_MX;
+  Frag bop[LY::FRM];
+#pragma unroll
+  for (int j = 0; j < LY::FRM; ++j) bop[j] = read_frag<UNIT>(stage, ro.a_data, ro.a_data2, ro.a_scale, j);
+  if constexpr (fp32_scales(SM)) {
+    // one K block per step: P = the block's unit-scale product, then
+    // acc += (sa[m] * sb[n]) * P with one rounding (fma)
+    float sa[LY::FRM];
+#pragma unroll
+    for (int j = 0; j < LY::FRM; ++j) sa[j] = *reinterpret_cast<const float*>(stage + ro.a_scale + j * 64);
+    float sab[LY::FRM];
+    if constexpr (SM == SM_FS2) {
+      const float sb = *reinterpret_cast<const float*>(stage + ro.b_scale);
+#pragma unroll
+      for (int j = 0; j < LY::FRM; ++j) sab[j] = sa[j] * sb;
+    }
+#pragma unroll
+    for (int i = 0; i < LY::FRN; ++i) {
+      const Frag aop = read_frag<true>(stage, ro.b_data, ro.b_data2, 0, i);
+      float4 sb4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (SM == SM_FS1) sb4 = *reinterpret_cast<const float4*>(stage + ro.b_scale + i * 64);
+#pragma unroll
+      for (int j = 0; j < LY::FRM; ++j) {
+        const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop.v, bop[j].v, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                       MfmaFmt<FB>::v, MfmaFmt<FA>::v, 0, 127, 0, 127);
+        if constexpr (SM == SM_FS2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sab[j], t[e], acc[i][j][e]);
+        } else {
+          acc[i][j][0] = __builtin_fmaf(sa[j] * sb4.x, t[0], acc[i][j][0]);
+          acc[i][j][1] = __builtin_fmaf(sa[j] * sb4.y, t[1], acc[i][j][1]);
+          acc[i][j][2] = __builtin_fmaf(sa[j] * sb4.z, t[2], acc[i][j][2]);
+          acc[i][j][3] = __builtin_fmaf(sa[j] * sb4.w, t[3], acc[i][j][3]);
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < LY::FRN; ++i) {
+    const Frag aop = read_frag<UNIT>(stage, ro.b_data, ro.b_data2, ro.b_scale, i);
+#pragma unroll
+    for (int j = 0; j < LY::FRM; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop.v, bop[j].v, acc[i][j], MfmaFmt<FB>::v,
+                                                                   MfmaFmt<FA>::v, 0, aop.s, 0, bop[j].s);
+  }
+}
+
+// Double-buffered K loop: the copies of step kt+1 are in flight while step
+// kt computes; each stage is read only after s_waitcnt vmcnt(0) and a barrier
+// (all copies landed), and refilled only after the next barrier (all waves
+// finished reading it).
+//
+// Only the last NCOPY waves issue the copies.  A direct-to-LDS buffer load
+// holds up the wave that issues it for ~70-90 clocks (measured on gfx950,
+// whether the data is in L2 or not), so a wave issuing many of them stalls
+// for much of a step.  In the big tile the copiers are waves 4-7, one per
+// SIMD, and the other wave of each SIMD keeps the MFMA pipe busy meanwhile
+// (measured: 8192^3 GEMM ~10% faster than with all 8 waves copying).
+template <class LY, int FA, int FB, int SM = SM_MX>
+__device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::FRM], const Operand& A,
+                                         const Operand& B, int64_t K, int wave, int lane) {
+  const int wm = wave / LY::NWN, wn = wave % LY::NWN;
+#pragma unroll
+  for (int i = 0; i < LY::FRN; ++i)
+#pragma unroll
+    for (int j = 0; j < LY::FRM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int kt_n = (int)(K / BK);
+  if (kt_n == 0) return;
+  const int c = wave - (LY::NW - LY::NCOPY);
+  const bool copier = c >= 0;
+  const CopyOffsets off = copy_offsets(K, copier ? c : 0, lane);
+  const ReadOffsets ro = read_offsets<LY, SM>(wm, wn, lane);
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  if (copier) load_stage<LY, SM>(lds_addr, A, B, off, K, 0, c);
+  for (int kt = 0; kt < kt_n; ++kt) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (copier && kt + 1 < kt_n) load_stage<LY, SM>(lds_addr + ((kt + 1) & 1) * LY::kStage, A, B, off, K, kt + 1, c);
+
+    compute<LY, FA, FB, SM>(lds + (kt & 1) * LY::kStage, acc, ro);
+  }
+}
+
+// Epilogue from registers.  acc[i][j][e] is D[m][n] with
+// m = m0 + WTM wm + 16 j + (lane & 15), n = n0 + WTN wn + 16 i + 4 (lane >> 4) + e.
+template <class LY, int EPI, int OUT>
+__device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], void* d, uint16_t* aux,
+                                         const uint16_t* bias, int64_t m0, int64_t m_end, int64_t n0, int64_t N,
+                                         int wave, int lane) {
+  const int wm = wave / LY::NWN, wn = wave % LY::NWN;
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int i = 0; i < LY::FRN; ++i) {
+    const int64_t n = n0 + wn * LY::WTN + 16 * i + 4 * g;
+    if (n >= N) continue;
+    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+    if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
+      const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+      b0 = bf16_bits_to_float(bb.x & 0xFFFFu);
+      b1 = bf16_bits_to_float(bb.x >> 16);
+      b2 = bf16_bits_to_float(bb.y & 0xFFFFu);
+      b3 = bf16_bits_to_float(bb.y >> 16);
+    }
+#pragma unroll
+    for (int j = 0; j < LY::FRM; ++j) {
+      const int64_t m = m0 + wm * LY::WTM + 16 * j + r;
+      if (m >= m_end) continue;
+      float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
+      if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
+        v0 += b0;
+        v1 += b1;
+        v2 += b2;
+        v3 += b3;
+      }
+      if constexpr (EPI == TE_EPI_BIAS_GELU_AUX) {
+        *reinterpret_cast<uint2*>(aux + m * N + n) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        v0 = gelu_tanh(v0);
+        v1 = gelu_tanh(v1);
+        v2 = gelu_tanh(v2);
+        v3 = gelu_tanh(v3);
+      }
+      if constexpr (EPI == TE_EPI_DGELU) {  // aux holds the saved bf16 pre-activation
+        const uint2 pa = *reinterpret_cast<const uint2*>(aux + m * N + n);
+        v0 *= dgelu_tanh(bf16_bits_to_float(pa.x & 0xFFFFu));
+        v1 *= dgelu_tanh(bf16_bits_to_float(pa.x >> 16));
+        v2 *= dgelu_tanh(bf16_bits_to_float(pa.y & 0xFFFFu));
+        v3 *= dgelu_tanh(bf16_bits_to_float(pa.y >> 16));
+      }
+      if constexpr (EPI == TE_EPI_ACCUMULATE) {  // fp32 D is read and added to
+        const float4 c = *reinterpret_cast<const float4*>(static_cast<float*>(d) + m * N + n);
+        v0 = c.x + v0;
+        v1 = c.y + v1;
+        v2 = c.z + v2;
+        v3 = c.w + v3;
+      }
+      if constexpr (OUT == TE_BF16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(d) + m * N + n) =
+            make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(d) + m * N + n) = make_float4(v0, v1, v2, v3);
+      }
+    }
+  }
+}
+
+// MXFP8 rowwise output.  The epilogue's fp32 results are rounded to bf16
+// exactly as for a bf16 D and then quantized in 32-column blocks (one E8M0
+// scale each, as the rowwise quantize kernel does), so the codes equal the
+// rowwise quantization of the bf16 D this GEMM writes otherwise: the next
+// GEMM sees the same operand without a bf16 round trip through memory.
+// Lane 16 g + r holds columns 16 i + 4 g .. +3 of row r, so the block
+// 32 b .. 32 b + 31 (i = 2b, 2b+1) sits in lanes r, r+16, r+32, r+48: the
+// block amax is a max over the lane's 8 values and then across those 4 lanes.
+template <class LY, int EPI, int FMT>
+__device__ __forceinline__ void epilogue_mx(const v4f (&acc)[LY::FRN][LY::FRM], uint8_t* d, uint8_t* d_scale,
+                                            uint16_t* aux, const uint16_t* bias, int64_t m0, int64_t m_end,
+                                            int64_t n0, int64_t N, int wave, int lane) {
+  static_assert(EPI == TE_EPI_NONE || EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX, "forward epilogues only");
+  const int wm = wave / LY::NWN, wn = wave % LY::NWN;
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int b = 0; b < LY::FRN / 2; ++b) {
+    const int64_t nb = n0 + wn * LY::WTN + 32 * b;  // wave-uniform; with N % 32 == 0 a block is all in or all out
+    if (nb >= N) continue;
+    float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if constexpr (EPI != TE_EPI_NONE) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(bias + nb + 16 * h + 4 * g);
+        bv[4 * h + 0] = bf16_bits_to_float(bb.x & 0xFFFFu);
+        bv[4 * h + 1] = bf16_bits_to_float(bb.x >> 16);
+        bv[4 * h + 2] = bf16_bits_to_float(bb.y & 0xFFFFu);
+        bv[4 * h + 3] = bf16_bits_to_float(bb.y >> 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < LY::FRM; ++j) {
+      const int64_t m = m0 + wm * LY::WTM + 16 * j + r;
+      const bool row_ok = m < m_end;
+      float v[8];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * h + e] = acc[2 * b + h][j][e] + bv[4 * h + e];
+      if constexpr (EPI == TE_EPI_BIAS_GELU_AUX) {
+        if (row_ok) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<uint2*>(aux + m * N + nb + 16 * h + 4 * g) =
+                make_uint2(pack_bf16x2(v[4 * h], v[4 * h + 1]), pack_bf16x2(v[4 * h + 2], v[4 * h + 3]));
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = gelu_tanh(v[k]);
+      }
+      const uint4 bits = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                          pack_bf16x2(v[6], v[7])};
+      uint32_t amax = absmax_bits8(bits);  // every lane takes part in the exchanges
+      amax = max(amax, (uint32_t)__builtin_amdgcn_ds_swizzle((int)amax, 0x401F));               // lane ^ 16
+      amax = max(amax, (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, (int)amax));    // lane ^ 32
+      const uint32_t code = e8m0_code_from_amax_bits<FMT>(amax);
+      const uint2 q = cvt8_scaled<FMT>(bits, e8m0_to_float(code));
+      if (row_ok) {
+        *reinterpret_cast<uint32_t*>(d + m * N + nb + 4 * g) = q.x;
+        *reinterpret_cast<uint32_t*>(d + m * N + nb + 16 + 4 * g) = q.y;
+        if (g == 0) d_scale[m * (N / 32) + nb / 32] = (uint8_t)code;
+      }
+    }
+  }
+}
+
+struct GemmParams {
+  const uint8_t* a;
+  const uint8_t* a_scale;
+  const uint8_t* b;
+  const uint8_t* b_scale;
+  void* d;
+  const uint16_t* bias;
+  uint16_t* aux;
+  int64_t M, N, K;
+  const int32_t* m_splits;  // grouped only
+  int32_t groups;           // grouped only
+  uint8_t* d_scale;         // MXFP8 output only: E8M0 scales [M, N/32]
+  const float* alpha_a;     // per-tensor FP8 only: a_scale_inv and b_scale_inv (device scalars)
+  const float* alpha_b;
+};
+
+// Dense: one workgroup per tile, operands scaled as SM says (SM_PT: the
+// accumulators are multiplied by alpha = a_scale_inv * b_scale_inv before the
+// epilogue).
+template <class LY, int FA, int FB, int EPI, int OUT, int SM = SM_MX>
+__global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
+  constexpr int BM = LY::BM, BN = LY::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntm = (int)((p.M + BM - 1) / BM), ntn = (int)((p.N + BN - 1) / BN);
+  const int ntiles = ntm * ntn;
+  // XCD-aware remap: workgroup b runs on XCD b % 8; give each XCD a
+  // contiguous run of tiles.
+  const int bid = blockIdx.x;
+  const int per = ntiles / 8;
+  const int t = bid < 8 * per ? (bid % 8) * per + bid / 8 : bid;
+  // raster in bands of kGroupM row-tiles
+  const int band = t / (kGroupM * ntn);
+  const int first_tm = band * kGroupM;
+  const int band_rows = min(ntm - first_tm, kGroupM);
+  const int in_band = t % (kGroupM * ntn);
+  const int tm = first_tm + in_band % band_rows;
+  const int tn = in_band / band_rows;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, BM);
+  const Operand B = SM == SM_FS2 ? make_operand_2d(p.b, p.b_scale, n0, p.N - n0, p.K, BN)
+                                 : make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, BN);
+  v4f acc[LY::FRN][LY::FRM];
+  mainloop<LY, FA, FB, SM>(lds, acc, A, B, p.K, wave, lane);
+  if constexpr (SM == SM_PT) {
+    // these products are rounded on their own: with contraction off here the
+    // epilogue's bias add stays a second rounding instead of becoming an FMA
+#pragma clang fp contract(off)
+    const float alpha = *p.alpha_a * *p.alpha_b;
+#pragma unroll
+    for (int i = 0; i < LY::FRN; ++i)
+#pragma unroll
+      for (int j = 0; j < LY::FRM; ++j) acc[i][j] *= alpha;
+  }
+  if constexpr (OUT == TE_E4M3 || OUT == TE_E5M2)
+    epilogue_mx<LY, EPI, OUT>(acc, static_cast<uint8_t*>(p.d), p.d_scale, p.aux, p.bias, m0, p.M, n0, p.N, wave,
+                              lane);
+  else
+    epilogue<LY, EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
+}
+
+// Grouped: a persistent grid walks the flat list of (expert row-tile,
+// n-tile) pairs, built in LDS from the device-resident splits.
+template <class LY, int FA, int FB, int EPI, int OUT>
+__global__ __launch_bounds__(LY::kThreads) void mx_grouped_gemm_kernel(GemmParams p) {
+  constexpr int BM = LY::BM, BN = LY::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
+  __shared__ int tile_prefix[kMaxGroups + 1];
+  __shared__ int64_t row_off[kMaxGroups + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = p.groups;
+  const int64_t total_m = p.M;
+  if (threadIdx.x == 0) {
+    int tiles = 0;
+    int64_t off = 0;
+    tile_prefix[0] = 0;
+    row_off[0] = 0;
+    for (int e = 0; e < G; ++e) {
+      int64_t me = p.m_splits[e];
+      me = me < 0 ? 0 : me;
+      int64_t end = off + me;
+      end = end > total_m ? total_m : end;
+      tiles += (int)((end - off + BM - 1) / BM);
+      off = end;
+      tile_prefix[e + 1] = tiles;
+      row_off[e + 1] = off;
+    }
+  }
+  __syncthreads();
+  const int ntn = (int)((p.N + BN - 1) / BN);
+  const int total = tile_prefix[G] * ntn;
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8, nslots = gridDim.x / 8;
+  const int chunk = (total + 7) / 8;
+  const int t_end = min((xcd + 1) * chunk, total);
+  for (int t = xcd * chunk + slot; t < t_end; t += nslots) {
+    const int rt = t / ntn, tn = t % ntn;
+    int lo = 0, hi = G;  // find e with tile_prefix[e] <= rt < tile_prefix[e + 1]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_prefix[mid] <= rt) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int64_t m0 = row_off[e] + (int64_t)(rt - tile_prefix[e]) * BM;
+    const int64_t m_end = row_off[e + 1];
+    const int64_t n0 = (int64_t)tn * BN;
+    const Operand A = make_operand(p.a, p.a_scale, m0, m_end - m0, p.K, BM);
+    const Operand B = make_operand(p.b + (int64_t)e * p.N * p.K, p.b_scale + (int64_t)e * p.N * (p.K / 32), n0,
+                                   p.N - n0, p.K, BN);
+    v4f acc[LY::FRN][LY::FRM];
+    __syncthreads();  // the previous tile's last reads of stage 0/1 are done
+    mainloop<LY, FA, FB>(lds, acc, A, B, p.K, wave, lane);
+    const bool has_bias = EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX;
+    epilogue<LY, EPI, OUT>(acc, p.d, p.aux, has_bias ? p.bias + (int64_t)e * p.N : nullptr, m0, m_end,
+                           n0, p.N, wave, lane);
+  }
+}
+
+// The big tile unless its grid leaves CUs idle.  Measured on MI355X (256 CUs):
+// the small tile (4x the tiles, two workgroups per CU) is faster with fewer
+// 256 x 256 tiles than CUs (4096 x 1024 x 4096: 33 vs 56 us; 4096 x 3072 x
+// 1024: 24 vs 26 us), and with up to two tiles per CU when K is short
+// (4096 x 4096 x 1024 + GELU aux: 42 vs 48 us, where the small tiles overlap
+// one round's output stores with the next round's MFMAs); the big tile wins
+// with long K (4096 x 4096 x 14336: 215 vs 299 us) and on larger grids.
+inline bool use_small_tile(int64_t big_tiles, int64_t K) {
+  const int64_t cus = device_cu_count();
+  return big_tiles < cus || (big_tiles < 2 * cus && K <= 4096);
+}
+
+inline te_status check_common(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,
+                       const uint8_t* b_scale, te_dtype b_fmt, void* d, te_dtype d_dtype, te_epilogue epi,
+                       const uint16_t* bias, uint16_t* aux, bool any_rows, bool any_k) {
+  TE_REQUIRE(epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX || epi == TE_EPI_DGELU ||
+                 epi == TE_EPI_ACCUMULATE,
+             TE_ERR_VALUE);
+  TE_REQUIRE(is_fp8(a_fmt) && is_fp8(b_fmt), TE_ERR_DTYPE);
+  TE_REQUIRE(!(a_fmt == TE_E5M2 && b_fmt == TE_E5M2), TE_ERR_DTYPE);
+  TE_REQUIRE(d_dtype == TE_BF16 || d_dtype == TE_FP32, TE_ERR_DTYPE);
+  TE_REQUIRE(epi != TE_EPI_ACCUMULATE || d_dtype == TE_FP32, TE_ERR_DTYPE);
+  TE_REQUIRE((epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX) == (bias != nullptr), TE_ERR_NULL);
+  TE_REQUIRE((epi == TE_EPI_BIAS_GELU_AUX || epi == TE_EPI_DGELU) == (aux != nullptr), TE_ERR_NULL);
+  if (!any_rows) return TE_OK;
+  TE_REQUIRE(d != nullptr, TE_ERR_NULL);
+  TE_REQUIRE(aligned16(d), TE_ERR_ALIGN);
+  if (any_k) {  // with K == 0 the operands are never read
+    TE_REQUIRE(a && a_scale && b && b_scale, TE_ERR_NULL);
+    TE_REQUIRE(aligned16(a) && aligned16(b), TE_ERR_ALIGN);
+    TE_REQUIRE(((uintptr_t)a_scale & 3u) == 0 && ((uintptr_t)b_scale & 3u) == 0, TE_ERR_ALIGN);
+  }
+  TE_REQUIRE(bias == nullptr || ((uintptr_t)bias & 7u) == 0, TE_ERR_ALIGN);
+  TE_REQUIRE(aux == nullptr || aligned16(aux), TE_ERR_ALIGN);
+  return TE_OK;
+}
+
+}  // namespace
+}  // namespace temx

@@ -21,7 +21,9 @@ Readings where the pages are silent:
   (no block saturates); a zero block gets scale_inv = 1.  Codes are the
   saturating round-to-nearest-even encodes of x / scale_inv (exact division).
 * The E8M0 cast of an FP32 scale_inv s > 0 is the smallest power of two >= s
-  (exact for the recipe's own power-of-two scales).
+  (exact for the recipe's own power-of-two scales), kept within E8M0's range
+  2^-127 .. 2^127; NaN and negative s have no E8M0 value and map to its NaN
+  code.
 * GEMM: D = epilogue(sum_kb sa[m, kb] * sb[n, kb] * sum_{k in kb} A_q[m, k] B_q[n, k]),
   with sb[n, kb] read at n // 128 for 2-D B.
 """
@@ -104,9 +106,14 @@ def block_gemm(qa, sa_inv, fmt_a: FP8Format, qb, sb_inv, fmt_b: FP8Format, b_2d:
 
 
 def e8m0_of(scale_inv) -> np.ndarray:
-    """The E8M0 codes (biased exponents) of the E8M0 cast of FP32 scale inverses."""
-    p = pow2_at_least(scale_inv)
-    return (np.log2(p).round().astype(np.int64) + 127).astype(np.uint8)
+    """The E8M0 codes (biased exponents) of the E8M0 cast of FP32 scale inverses: the smallest
+    E8M0 value (2^-127 .. 2^127) >= s, or 2^127 above that range (+inf included); s = +-0 gives
+    2^-127; NaN and negative s give the E8M0 NaN code 255 (there is no negative scale)."""
+    v = np.asarray(scale_inv, dtype=np.float64)
+    bad = np.isnan(v) | (v < 0)
+    w = np.clip(np.where(bad, 1.0, v), 2.0 ** -127, 2.0 ** 127)
+    code = np.log2(pow2_at_least(w)).round().astype(np.int64) + 127
+    return np.where(bad, 255, code).astype(np.uint8)
 
 
 def dequantize_1d(q, scale_inv, fmt: FP8Format) -> np.ndarray:

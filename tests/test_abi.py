@@ -205,6 +205,48 @@ def test_fp8_gemm_validation():
     assert fp8gemm(M=0, d=None) == te.TE_OK
 
 
+def blockgemm(a=P, sa=P3, fa=te.TE_E4M3, b=P, sb=P3, fb=te.TE_E4M3, b2d=1, M=256, N=256, K=256, d=P2,
+              dt=te.TE_BF16, epi=te.TE_EPI_NONE, bias=None, aux=None, mode=te.TE_BLOCK_SCALES_E8M0, ws=P,
+              ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = te.te_fp8_block_gemm_workspace_size(M, N, K, mode)
+    return L.te_fp8_block_gemm(a, sa, fa, b, sb, fb, b2d, M, N, K, d, dt, epi, bias, aux, mode, ws, ws_bytes, None)
+
+
+def test_block_gemm_workspace_and_validation():
+    # E8M0 scales of A (M * K/32 bytes, padded to 256), then of B
+    assert te.te_fp8_block_gemm_workspace_size(4096, 1024, 4096, "e8m0") == 4096 * 128 + 1024 * 128
+    assert te.te_fp8_block_gemm_workspace_size(16, 16, 128, "e8m0") == 256 + 64
+    assert te.te_fp8_block_gemm_workspace_size(8192, 8192, 8192, "fp32") == 0
+    for mode in (te.TE_BLOCK_SCALES_E8M0, te.TE_BLOCK_SCALES_FP32):
+        assert blockgemm(mode=mode, K=192) == te.TE_ERR_SHAPE
+        assert blockgemm(mode=mode, N=40) == te.TE_ERR_SHAPE
+        assert blockgemm(mode=mode, b2d=2) == te.TE_ERR_VALUE
+        assert blockgemm(mode=mode, fa=te.TE_E5M2, fb=te.TE_E5M2) == te.TE_ERR_DTYPE
+        assert blockgemm(mode=mode, dt=te.TE_E4M3) == te.TE_ERR_DTYPE
+        assert blockgemm(mode=mode, epi=te.TE_EPI_ACCUMULATE) == te.TE_ERR_DTYPE
+        assert blockgemm(mode=mode, epi=te.TE_EPI_BIAS) == te.TE_ERR_NULL
+        assert blockgemm(mode=mode, epi=te.TE_EPI_DGELU) == te.TE_ERR_NULL
+        assert blockgemm(mode=mode, sa=None) == te.TE_ERR_NULL
+        assert blockgemm(mode=mode, sb=P3 + 2) == te.TE_ERR_ALIGN
+        assert blockgemm(mode=mode, a=BAD) == te.TE_ERR_ALIGN
+        assert blockgemm(mode=mode, M=0, d=None) == te.TE_OK
+    assert blockgemm(mode=2) == te.TE_ERR_VALUE
+    assert blockgemm(ws=None) == te.TE_ERR_NULL
+    assert blockgemm(ws_bytes=1024) == te.TE_ERR_WORKSPACE
+    assert blockgemm(ws=P + 8) == te.TE_ERR_ALIGN
+    assert blockgemm(mode=te.TE_BLOCK_SCALES_FP32, ws=None, ws_bytes=0, sa=None) == te.TE_ERR_NULL
+    conv = L.te_fp8_block_scales_to_mx
+    assert conv(P, 64, 192, 0, P2, None) == te.TE_ERR_SHAPE
+    assert conv(P, -1, 128, 0, P2, None) == te.TE_ERR_SHAPE
+    assert conv(P, 64, 128, 2, P2, None) == te.TE_ERR_VALUE
+    assert conv(None, 64, 128, 1, P2, None) == te.TE_ERR_NULL
+    assert conv(P, 64, 128, 1, None, None) == te.TE_ERR_NULL
+    assert conv(P + 2, 64, 128, 0, P2, None) == te.TE_ERR_ALIGN
+    assert conv(P, 64, 128, 0, P2 + 1, None) == te.TE_ERR_ALIGN
+    assert conv(None, 0, 128, 0, None, None) == te.TE_OK
+
+
 def grouped(G=4, splits=P3, T=1024, a=P, sa=P, fa=te.TE_E4M3, b=P, sb=P, fb=te.TE_E4M3, N=256, K=256, d=P2,
             dt=te.TE_BF16, epi=te.TE_EPI_NONE, bias=None, aux=None):
     return L.te_mxfp8_grouped_gemm(G, splits, T, a, sa, fa, b, sb, fb, N, K, d, dt, epi, bias, aux, None, 0, None)

@@ -38,6 +38,13 @@ def test_pow2_at_least():
     want = np.array([1.0, 0.5, 2.0 ** -130, 4.0, 0.5, 2.0, 1.0, 512.0, 0.25])
     assert np.array_equal(pow2_at_least(v), want)
     assert np.array_equal(e8m0_of(np.array([1.0, 0.25, 3.0], np.float32)), np.array([127, 125, 129], np.uint8))
+    # E8M0's range ends at 2^-127: smaller scales round up to it
+    tiny = np.array([2.0 ** -127, 2.0 ** -130, 2.0 ** -126 * 0.75, 2.0 ** 127], np.float32)
+    assert np.array_equal(e8m0_of(tiny), np.array([0, 0, 1, 254], np.uint8))
+    # beyond 2^127 it saturates; zeros take the smallest value; NaN / negative have none
+    special = np.array([np.finfo(np.float32).max, np.inf, 0.0, -0.0, np.nan, -1.0, -np.inf, 2.0 ** 126 * 1.5],
+                       np.float32)
+    assert np.array_equal(e8m0_of(special), np.array([254, 254, 0, 0, 255, 255, 255, 254], np.uint8))
 
 
 def test_quantize_1d_hand_block_and_invariants():
