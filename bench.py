@@ -44,7 +44,9 @@ KERNELS = {"quantize_row": ["quantize_rowwise_kernel"], "quantize_col": ["quanti
            "gemm": ["mx_gemm_kernel"], "grouped": ["mx_grouped_gemm_kernel"],
            "cast": ["amax_partial_kernel", "amax_final_kernel", "cast_kernel"],
            "quantize_bgrad": ["quantize_colwise_kernel", "bgrad_final_kernel"],
-           "cast_delayed": ["cast_amax_kernel", "delayed_update_kernel"]}
+           "cast_delayed": ["cast_amax_kernel", "delayed_update_kernel"],
+           "quantize_block1d": ["block_quantize_1d_kernel"], "quantize_block2d": ["block_quantize_2d_kernel"],
+           "gemm_block_e8m0": ["block_scale_expand_kernel", "mx_gemm_kernel"], "gemm_block_fp32": ["mx_gemm_kernel"]}
 CALIBRATION_BYTES = 512 << 20  # one device-to-device copy of this many bytes reads and writes it once
 
 
@@ -55,7 +57,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--workload", default="square_8192",
                    choices=["square_8192", "decoder_fwd", "decoder_fwd_mx", "decoder_fwd_delayed", "hybrid_bwd",
-                            "hybrid_bwd_fused", "moe_grouped", "tiny"])
+                            "hybrid_bwd_fused", "moe_grouped", "block_e8m0_square_8192", "block_fp32_square_8192",
+                            "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, copy a 512 MiB buffer 3 times (counter calibration)")
@@ -180,8 +183,41 @@ def build_step(workload, torch, te, workloads):
         step.add(label, "cast", fn, 0.0, n * (2 + 1), KERNELS["cast_delayed"])
         return outs
 
+    def add_block_quantize(spec, fmt, block_2d, label):
+        src = rotated(spec.make())
+        rows, cols = spec.shape
+        srows = (rows + 127) // 128 if block_2d else rows
+        outs = [(torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+                 torch.empty((srows, cols // 128), dtype=torch.float32, device=dev)) for _ in range(ROTATE)]
+
+        def fn(r, src=src, outs=outs, fmt=fmt, block_2d=block_2d):
+            te.te_fp8_block_quantize(src[r], fmt, block_2d, outs[r][0], outs[r][1])
+        step.add(label, "quantize", fn, 0.0, rows * cols * 3 + srows * (cols // 128) * 4,
+                 KERNELS["quantize_block2d" if block_2d else "quantize_block1d"])
+        return outs
+
     mx_outputs = {}  # GEMM name -> rotating (codes, scales) of its MXFP8 output
     for g in w.gemms:
+        if g.scaling.startswith("block_"):
+            mode = g.scaling[len("block_"):]
+            qa = add_block_quantize(g.a_src, g.fmt_a, False, f"quantize_block1d_{g.name}_A")
+            qb = add_block_quantize(g.b_src, g.fmt_b, True, f"quantize_block2d_{g.name}_B")
+            bias = upload(g.bias.make()) if g.bias is not None else None
+            d = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev)
+            aux = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev) if g.epilogue == "bias_gelu_aux" else None
+            wsb = te.te_fp8_block_gemm_workspace_size(g.M, g.N, g.K, mode)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+
+            def fn(r, g=g, qa=qa, qb=qb, bias=bias, d=d, aux=aux, ws=ws, mode=mode):
+                te.te_fp8_block_gemm(qa[r][0], qa[r][1], g.fmt_a, qb[r][0], qb[r][1], g.fmt_b, True, d, g.epilogue,
+                                     bias, aux, mode, ws)
+            # algorithmic bytes: 1 B per operand element, the fp32 scales (one per 128 elements of A, per
+            # 128 x 128 of B) and the output
+            nbytes = gemm_bytes(g.M, g.N, g.K, g.epilogue) - (g.M + g.N) * g.K / 32 + g.M * g.K / 32 + \
+                ((g.N + 127) // 128) * g.K / 32
+            step.add(f"gemm_block_{mode}_{g.name}_{g.M}x{g.N}x{g.K}", "gemm", fn, g.flops, nbytes,
+                     KERNELS["gemm_block_" + mode])
+            continue
         if g.scaling == "delayed":
             ca = add_delayed_cast(g.a_src, g.fmt_a, f"cast_delayed_{g.name}_A")
             cb = add_delayed_cast(g.b_src, g.fmt_b, f"cast_delayed_{g.name}_B")
@@ -282,7 +318,17 @@ def cpu_baseline(workload, workloads):
                 sn //= 2
         fa, fb = oracle.format_by_name(g.fmt_a), oracle.format_by_name(g.fmt_b)
         bias = g.bias.make()[:sn] if g.bias is not None else None
-        if g.scaling == "delayed":
+        if g.scaling.startswith("block_"):
+            sn = max(128, sn // 128 * 128)  # whole 128-row blocks of B
+            t0 = time.perf_counter()
+            qa, sa = oracle.quantize_1d(a[:sm], fa)
+            qb, sb = oracle.quantize_2d(b[:sn], fb)
+            t1 = time.perf_counter()
+            if g.scaling == "block_e8m0":
+                sa, sb = oracle.pow2_at_least(sa), oracle.pow2_at_least(sb)
+            oracle.block_gemm(qa, sa, fa, qb, sb, fb, True, bias, g.epilogue)
+            t2 = time.perf_counter()
+        elif g.scaling == "delayed":
             t0 = time.perf_counter()
             h0 = np.zeros(16, np.float32)
             qa, ia, _, _, _ = oracle.delayed_scaling_step(a[:sm], fa, h0, np.float32(1.0))
@@ -508,6 +554,15 @@ def stats_from(stats_dir, command):
 
 # --------------------------------------------------------------------- main
 
+def arithmetic(w):
+    kinds = {g.scaling for g in w.gemms} or {"mx"}
+    text = {"mx": "MXFP8 (E4M3/E5M2 codes, E8M0 scales per 32 elements)",
+            "delayed": "per-tensor FP8 (E4M3/E5M2 codes, one FP32 scale per tensor, delayed scaling)",
+            "block_e8m0": "blockwise FP8 (E4M3/E5M2 codes, FP32 scales per 1x128 / 128x128 block, cast to E8M0)",
+            "block_fp32": "blockwise FP8 (E4M3/E5M2 codes, FP32 scales per 1x128 / 128x128 block, applied in fp32)"}
+    return "; ".join(text[k] for k in sorted(kinds)) + " products, fp32 accumulate"
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -656,7 +711,7 @@ def main():
         "data": "synthetic (seeded N(0, sigma) bf16, outlier columns per config)",
         "config": {"workload": w.name, "gemm_flops_per_step": step.flops, "parallelism": "single GPU",
                    "launch": "eager" if graphs is None else "HIP graph replay (a graph per cycle of the 4 buffer rotations)",
-                   "arithmetic": "MXFP8 (E4M3/E5M2 codes, E8M0 block scales) products, fp32 accumulate",
+                   "arithmetic": arithmetic(w),
                    "rotating_buffers": ROTATE},
         "roofline": roof,
         "quantize_gbs_min": min((k["gbs"] for k in qk), default=None),

@@ -7,6 +7,9 @@
  *   - MXFP8 1-D block quantization of bf16 tensors, rowwise and transposed
  *     columnwise (32-element blocks, one E8M0 power-of-two scale per block),
  *     and the fused cast-transpose with bias gradient;
+ *   - delayed scaling (amax history) and the per-tensor FP8 GEMM;
+ *   - blockwise FP8 (1 x 128 / 128 x 128 blocks with FP32 scale inverses):
+ *     quantization and the GEMM, with the scales cast to E8M0 or as FP32;
  *   - the MXFP8 x MXFP8 -> fp32-accumulate GEMM with bias, GELU(tanh) and
  *     GELU-aux (pre-activation) epilogues;
  *   - a single-launch grouped (MoE) variant over ragged expert row counts.
@@ -303,6 +306,26 @@ te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_splits, int
                                 void* d, te_dtype d_dtype, te_epilogue epi,
                                 const uint16_t* bias, uint16_t* aux,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Blockwise FP8 quantization ([ROCm-TE] "Blockwise FP8 GEMM support on
+ * ROCm": 1-D (1 x 128) blocks for activations and gradients, 2-D
+ * (128 x 128) blocks for weights; on gfx950 the recipe's scales are powers
+ * of two).  Each block gets scale_inv = the smallest power of two p with
+ * amax / p <= the format's largest finite value (448 E4M3, 57344 E5M2), or
+ * 1 for an all-zero block; codes are the saturating round-to-nearest-even
+ * encodes of x / p (exact division), so no element saturates.
+ *   x          bf16 [rows, cols]; cols % 128 == 0, rows >= 0 (any)
+ *   fmt        TE_E4M3 or TE_E5M2
+ *   block_2d   0: blocks of 128 along each row; scale_inv float [rows, cols/128]
+ *              1: 128 x 128 blocks (the last block row may be short);
+ *                 scale_inv float [ceil(rows/128), cols/128]
+ *   q          uint8 [rows, cols] codes
+ *   Inputs holding NaN or Inf give unspecified codes and scales for their
+ *   block.  An empty tensor enqueues nothing.
+ */
+te_status te_fp8_block_quantize(const uint16_t* x, int64_t rows, int64_t cols, te_dtype fmt, int block_2d,
+                                uint8_t* q, float* scale_inv, hipStream_t stream);
 
 /*
  * Blockwise FP8 scales cast to MXFP8 scales ([ROCm-TE] "Blockwise FP8 GEMM

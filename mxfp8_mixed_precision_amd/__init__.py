@@ -56,6 +56,7 @@ _SIGS = {
                                            _vp, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
     "te_mxfp8_grouped_gemm": (ctypes.c_int, [_i32, _vp, _i64, _vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int,
                                              _i64, _i64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, _sz, _vp]),
+    "te_fp8_block_quantize": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]),
     "te_fp8_block_scales_to_mx": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
     "te_fp8_block_gemm_workspace_size": (_sz, [_i64, _i64, _i64, ctypes.c_int]),
     "te_fp8_block_gemm": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64, _i64,
@@ -202,6 +203,12 @@ def _block_scaling(mode) -> int:
     return BLOCK_SCALINGS[mode] if isinstance(mode, str) else int(mode)
 
 
+def te_fp8_block_quantize(x, fmt, block_2d, q, scale_inv, stream=None) -> None:
+    rows, cols = x.shape
+    _check("te_fp8_block_quantize", _lib.te_fp8_block_quantize(
+        _ptr(x), rows, cols, _fmt(fmt), int(bool(block_2d)), _ptr(q), _ptr(scale_inv), _stream(stream)))
+
+
 def te_fp8_block_scales_to_mx(scale_inv, rows: int, cols: int, block_2d: bool, mx_scale, stream=None) -> None:
     _check("te_fp8_block_scales_to_mx", _lib.te_fp8_block_scales_to_mx(
         _ptr(scale_inv), int(rows), int(cols), int(bool(block_2d)), _ptr(mx_scale), _stream(stream)))
@@ -337,6 +344,16 @@ def mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n, epilog
         aux = torch.empty((total_m, n), dtype=torch.bfloat16, device=a.device)
     te_mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n, d, epilogue, bias, aux, None, stream)
     return d, (aux if epilogue == "bias_gelu_aux" else None)
+
+
+def fp8_block_quantize(x, fmt="e4m3", block_2d=False, stream=None):
+    """bf16 [rows, cols] -> (codes uint8 [rows, cols], scale_inv float [rows or ceil(rows/128), cols/128])."""
+    rows, cols = x.shape
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    srows = (rows + 127) // 128 if block_2d else rows
+    s = torch.empty((srows, cols // 128), dtype=torch.float32, device=x.device)
+    te_fp8_block_quantize(x, fmt, block_2d, q, s, stream)
+    return q, s
 
 
 def fp8_block_scales_to_mx(scale_inv, rows: int, cols: int, block_2d: bool, stream=None):

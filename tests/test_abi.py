@@ -236,6 +236,17 @@ def test_block_gemm_workspace_and_validation():
     assert blockgemm(ws_bytes=1024) == te.TE_ERR_WORKSPACE
     assert blockgemm(ws=P + 8) == te.TE_ERR_ALIGN
     assert blockgemm(mode=te.TE_BLOCK_SCALES_FP32, ws=None, ws_bytes=0, sa=None) == te.TE_ERR_NULL
+    bq = L.te_fp8_block_quantize
+    assert bq(P, 64, 192, te.TE_E4M3, 0, P2, P3, None) == te.TE_ERR_SHAPE
+    assert bq(P, -1, 128, te.TE_E4M3, 0, P2, P3, None) == te.TE_ERR_SHAPE
+    assert bq(P, 64, 128, te.TE_BF16, 0, P2, P3, None) == te.TE_ERR_DTYPE
+    assert bq(P, 64, 128, te.TE_E5M2, 3, P2, P3, None) == te.TE_ERR_VALUE
+    assert bq(P, 64, 128, te.TE_E4M3, 1, None, P3, None) == te.TE_ERR_NULL
+    assert bq(P, 64, 128, te.TE_E4M3, 1, P2, None, None) == te.TE_ERR_NULL
+    assert bq(BAD, 64, 128, te.TE_E4M3, 0, P2, P3, None) == te.TE_ERR_ALIGN
+    assert bq(P, 64, 128, te.TE_E4M3, 0, P2 + 8, P3, None) == te.TE_ERR_ALIGN
+    assert bq(P, 64, 128, te.TE_E4M3, 0, P2, P3 + 2, None) == te.TE_ERR_ALIGN
+    assert bq(None, 0, 128, te.TE_E4M3, 1, None, None, None) == te.TE_OK
     conv = L.te_fp8_block_scales_to_mx
     assert conv(P, 64, 192, 0, P2, None) == te.TE_ERR_SHAPE
     assert conv(P, -1, 128, 0, P2, None) == te.TE_ERR_SHAPE

@@ -218,3 +218,44 @@ def test_fp32_mode_epilogues_equal_e8m0_mode(b_2d, epi):
         ref, _, _ = oracle.block_gemm(qa, sa, oracle.E4M3, qb, sb, oracle.E5M2, b_2d)
         assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)
         assert np.array_equal(outs["fp32"][0], bf16_rne(ref))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_block_square_full_size_sampled(mode):
+    """The bench workload (8192^3, A in 1 x 128 blocks, B in 128 x 128 blocks) through the device quantizer
+    and the GEMM as bench.py launches them; sampled rows of A and columns in six 128-row blocks of B
+    (first, last, across a 256-column tile boundary, random) against the oracle."""
+    g = workloads.block_square(mode).gemms[0]
+    a_bits, b_bits = g.a_src.make(), g.b_src.make()
+    m = te()
+    qa, sa = m.fp8_block_quantize(dev(a_bits), g.fmt_a, block_2d=False)
+    qb, sb = m.fp8_block_quantize(dev(b_bits), g.fmt_b, block_2d=True)
+    ws_bytes = m.te_fp8_block_gemm_workspace_size(g.M, g.N, g.K, mode)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
+    d = torch.empty((g.M, g.N), dtype=torch.bfloat16, device="cuda")
+    m.te_fp8_block_gemm(qa, sa, g.fmt_a, qb, sb, g.fmt_b, True, d, g.epilogue, None, None, mode, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(81)
+    rows = np.array(sorted({0, 255, 256, g.M - 1} | set(rng.choice(g.M, 60, replace=False).tolist())))
+    slabs = sorted({0, 1, 2, g.N // 128 - 1} | set(rng.choice(g.N // 128, 2, replace=False).tolist()))
+    Fa, Fb = oracle.format_by_name(g.fmt_a), oracle.format_by_name(g.fmt_b)
+    oqa, osa = oracle.quantize_1d(a_bits[rows], Fa)
+    assert np.array_equal(host(qa[rows]), oqa) and np.array_equal(host(sa[rows]), osa)
+    cols, oqb, osb = [], [], []
+    for sl in slabs:
+        q2, s2 = oracle.quantize_2d(b_bits[128 * sl:128 * (sl + 1)], Fb)
+        assert np.array_equal(host(qb[128 * sl:128 * (sl + 1)]), q2) and np.array_equal(host(sb[sl:sl + 1]), s2)
+        pick = sorted({0, 127} | set(rng.choice(128, 14, replace=False).tolist()))
+        cols += [128 * sl + p for p in pick]
+        oqb.append(q2[pick])
+        osb.append(np.repeat(s2, len(pick), axis=0))
+    cols = np.array(cols)
+    # B rows sampled as 1-D rows carrying their block's scale row
+    sub_qb, sub_sb = np.concatenate(oqb), np.concatenate(osb)
+    full_qb = np.zeros((g.N, g.K), np.uint8)
+    full_sb = np.ones((g.N, g.K // 128), np.float32)
+    full_qb[cols], full_sb[cols] = sub_qb, sub_sb
+    full_qa = np.zeros((g.M, g.K), np.uint8)
+    full_sa = np.ones((g.M, g.K // 128), np.float32)
+    full_qa[rows], full_sa[rows] = oqa, osa
+    check_recipe(mode, full_qa, full_sa, g.fmt_a, full_qb, full_sb, g.fmt_b, False, rows, cols, d)

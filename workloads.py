@@ -83,7 +83,10 @@ class GemmSpec:
     b_dir: str = "row"
     bias: TensorSpec | None = None
     mx_out: bool = False        # D written as a rowwise MXFP8 operand (fmt_a of the consumer) instead of bf16
-    scaling: str = "mx"         # "mx": MXFP8 operands; "delayed": per-tensor FP8 cast with delayed scaling
+    # "mx": MXFP8 operands; "delayed": per-tensor FP8 cast with delayed scaling;
+    # "block_e8m0" / "block_fp32": blockwise FP8 (A in 1 x 128 blocks, B in
+    # 128 x 128 blocks), the GEMM taking the scales cast to E8M0 or as FP32
+    scaling: str = "mx"
     a_from: str | None = None   # A is the MXFP8 output of this earlier GEMM (a_src is then unused)
 
     @property
@@ -174,6 +177,17 @@ def large_square() -> Workload:
                     quantize=[(a, "e4m3", "row"), (a, "e4m3", "col"), (b, "e4m3", "row"), (b, "e4m3", "col")])
 
 
+def block_square(mode: str = "e8m0") -> Workload:
+    """M = N = K = 8192 with the blockwise FP8 recipe on the operands of
+    square_8192: A quantized in 1 x 128 blocks, B in 128 x 128 blocks
+    (power-of-two FP32 scales), then the 1-D x 2-D blockwise GEMM with the
+    scales cast to E8M0 (mode "e8m0") or applied as FP32 ("fp32")."""
+    n = 8192
+    g = large_square().gemms[0]
+    return Workload(f"block_{mode}_square_8192", gemms=[GemmSpec("fprop", n, n, n, "e4m3", "e4m3", "none",
+                                                                 g.a_src, g.b_src, scaling=f"block_{mode}")])
+
+
 def hybrid_backward() -> Workload:
     """FFN backward, 4096 tokens, hidden 4096, ffn 14336, HYBRID formats.
 
@@ -213,4 +227,5 @@ def moe_grouped() -> Workload:
 
 ALL = {"tiny": tiny, "decoder_fwd": decoder_forward, "decoder_fwd_mx": decoder_forward_mx,
        "decoder_fwd_delayed": decoder_forward_delayed, "square_8192": large_square,
+       "block_e8m0_square_8192": lambda: block_square("e8m0"), "block_fp32_square_8192": lambda: block_square("fp32"),
        "hybrid_bwd": hybrid_backward, "hybrid_bwd_fused": hybrid_backward_fused, "moe_grouped": moe_grouped}
