@@ -68,7 +68,9 @@ def parse():
                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/")
     p.add_argument("--stats-from", metavar="DIR",
                    help="no GPU: turn a rocprofv3 --kernel-trace --stats run into profiles/")
-    p.add_argument("--command", default="", help="the profiling command, recorded with --stats-from")
+    p.add_argument("--mfma-from", metavar="DIR",
+                   help="no GPU: turn a rocprofv3 --pmc run of the MFMA and clock counters into profiles/")
+    p.add_argument("--command", default="", help="the profiling command, recorded with --stats-from / --mfma-from")
     p.add_argument("--no-graph", action="store_true",
                    help="launch every op from Python instead of replaying captured HIP graphs")
     return p.parse_args()
@@ -552,6 +554,62 @@ def stats_from(stats_dir, command):
     print(f"wrote {path}")
 
 
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE GRBM_COUNT"
+
+
+def mfma_from(pmc_dir, command):
+    """Summarise a rocprofv3 --pmc run of MFMA_COUNTERS: per MFMA kernel, the FP8 MFMA work the counters
+    saw against the op's algorithmic flops, and the MFMA-busy share of the SIMDs' active cycles."""
+    import csv
+    import statistics
+    csvs = [os.path.join(r, f) for r, _, fs in os.walk(pmc_dir) for f in fs if f.endswith("counter_collection.csv")]
+    with open(csvs[0]) as fh:
+        rows = list(csv.DictReader(fh))
+    with open(os.path.join(pmc_dir, "ops.json")) as fh:
+        record = json.load(fh)
+    by, name, dur = {}, {}, {}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        by.setdefault(d, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        name[d] = r["Kernel_Name"].replace("void ", "").replace("temx::(anonymous namespace)::", "").split("(")[0]
+        dur[d] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    xcc, simds = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+    gemm_flops = sorted({o["flops"] for o in record["ops"] if o.get("flops")})
+    wl = record["workload"]
+    md = [f"# MFMA utilisation, workload {wl}", "", "Command (from the repository root, GPU box):", "",
+          "    " + command, "",
+          "Per dispatch of each kernel that issues FP8 MFMAs (medians over the run's dispatches):", "",
+          "- MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_F8 x 512 (the counter counts multiply and add operations / 512);",
+          "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs): the share of the",
+          "  SIMDs' active cycles in which the matrix unit is busy;",
+          "- GRBM cycles per ns = GRBM_GUI_ACTIVE / 8 over the dispatch's counter-run duration (a relative clock:",
+          "  compare it with the HBM-bound kernels of the same run, which run at the full clock).", "",
+          "| kernel | dispatches | MFMA flops | algorithmic flops | ratio | MFMA busy | GRBM cycles per ns |",
+          "|---|---:|---:|---:|---:|---:|---:|"]
+    kernels = sorted({name[d] for d in by})
+    other = []
+    for k in kernels:
+        ds = [d for d in by if name[d] == k]
+        f = statistics.median([by[d].get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) * 512 for d in ds])
+        clk = statistics.median([by[d]["GRBM_GUI_ACTIVE"] / xcc / max(dur[d], 1) for d in ds])
+        if f <= 0:
+            other.append((k, len(ds), clk))
+            continue
+        busy = statistics.median([by[d]["SQ_VALU_MFMA_BUSY_CYCLES"] / (by[d]["GRBM_GUI_ACTIVE"] / xcc * simds)
+                                  for d in ds])
+        alg = min(gemm_flops, key=lambda x: abs(x - f)) if gemm_flops else 0.0
+        md.append(f"| `{k[:80]}` | {len(ds)} | {f:.4g} | {alg:.4g} | {f / alg if alg else 0:.4f} | "
+                  f"{100 * busy:.1f}% | {clk:.3f} |")
+    md += ["", "Kernels without MFMA work in the same run:", "", "| kernel | dispatches | GRBM cycles per ns |",
+           "|---|---:|---:|"]
+    md += [f"| `{k[:80]}` | {n} | {c:.3f} |" for k, n, c in other]
+    md += ["", f"Kernel sources hash: {kernel_sources_hash()}", ""]
+    path = os.path.join(ROOT, "profiles", f"{wl}_mfma_util.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(md))
+    print(f"wrote {path}")
+
+
 # --------------------------------------------------------------------- main
 
 def arithmetic(w):
@@ -570,6 +628,9 @@ def main():
         return
     if args.stats_from:
         stats_from(args.stats_from, args.command)
+        return
+    if args.mfma_from:
+        mfma_from(args.mfma_from, args.command)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -736,7 +797,7 @@ def main():
                           f"python bench.py --workload {args.workload} --steps {args.steps} "
                           f"--warmup {args.warmup} --no-cpu-baseline --copy-calibration "
                           f"--record-ops {os.path.relpath(os.path.abspath(args.record_ops), ROOT)}",
-               "ops": [{"label": o[0], "kind": o[1], "bytes": o[4], "kernels": k}
+               "ops": [{"label": o[0], "kind": o[1], "bytes": o[4], "flops": o[3], "kernels": k}
                        for o, k in zip(step.ops, step.kernels)],
                "bench_line": {"kernels": kernels, "summary": summary}}
         os.makedirs(os.path.dirname(os.path.abspath(args.record_ops)), exist_ok=True)
