@@ -46,7 +46,7 @@ KERNELS = {"quantize_row": ["quantize_rowwise_kernel"], "quantize_col": ["quanti
            "quantize_bgrad": ["quantize_colwise_kernel", "bgrad_final_kernel"],
            "cast_delayed": ["cast_amax_kernel", "delayed_update_kernel"],
            "quantize_block1d": ["block_quantize_1d_kernel"], "quantize_block2d": ["block_quantize_2d_kernel"],
-           "gemm_block_e8m0": ["block_scale_expand_kernel", "mx_gemm_kernel"], "gemm_block_fp32": ["mx_gemm_kernel"]}
+           "gemm_block_e8m0": ["mx_gemm_kernel"], "gemm_block_fp32": ["mx_gemm_kernel"]}
 CALIBRATION_BYTES = 512 << 20  # one device-to-device copy of this many bytes reads and writes it once
 
 

@@ -357,21 +357,18 @@ te_status te_fp8_block_scales_to_mx(const float* scale_inv, int64_t rows, int64_
  *   a            uint8 [M, K] codes, a_scale_inv float [M, K/128] (1-D blocks)
  *   b            uint8 [N, K] codes, b_scale_inv float [N, K/128]
  *                (b_block_2d = 0) or [ceil(N/128), K/128] (b_block_2d = 1)
- *   mode         TE_BLOCK_SCALES_E8M0: sa and sb are first cast as
- *                te_fp8_block_scales_to_mx casts them (into the workspace),
- *                then the MXFP8 GEMM runs: the result is te_mxfp8_gemm's on
- *                those operands.
+ *   mode         TE_BLOCK_SCALES_E8M0: every scale is cast to E8M0 as
+ *                te_fp8_block_scales_to_mx casts it (inside the GEMM kernel):
+ *                the result is te_mxfp8_gemm's on the operands with those
+ *                scales.
  *                TE_BLOCK_SCALES_FP32: each K block's product is computed
  *                with unit scales and added to the fp32 accumulator times
  *                fl32(sa * sb) with one fused multiply-add; no workspace.
  *   d, d_dtype, epi, bias, aux: as te_mxfp8_gemm (every epilogue).
  *   Shapes as te_mxfp8_gemm: K % 128 == 0, M % 16 == 0, N % 16 == 0.
  *   Scale pointers are 4-byte aligned and may be NULL when M, N or K is 0.
- *   workspace    te_fp8_block_gemm_workspace_size(M, N, K, mode) bytes
- *                (0 for TE_BLOCK_SCALES_FP32), 16-byte aligned; holds the
- *                E8M0 scales of A, then (at the next 256-byte boundary)
- *                those of B.  It must not be in use by other work on the
- *                device while the call's kernels run.
+ *   workspace    none is needed (te_fp8_block_gemm_workspace_size returns
+ *                0); pass NULL / 0.
  */
 size_t te_fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K, te_block_scaling mode);
 te_status te_fp8_block_gemm(const uint8_t* a, const float* a_scale_inv, te_dtype a_fmt,

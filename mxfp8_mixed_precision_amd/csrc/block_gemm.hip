@@ -7,13 +7,16 @@
 // scaling, E4M3 / E5M2 inputs (not E5M2 x E5M2), bias and DGELU epilogues;
 // on gfx950 the default kernel computes with the scales cast to E8M0, and a
 // second kernel uses the FP32 scales themselves.  Both are here:
-// * TE_BLOCK_SCALES_E8M0: one small kernel casts the scales to E8M0 and
-//   lays them out as MXFP8 scales in the caller's workspace (block_scale.hip);
-//   the MXFP8 GEMM then runs unchanged (a 128-block is four 32-blocks with
-//   one scale).
-// * TE_BLOCK_SCALES_FP32: the GEMM kernel of gemm_core.h in mode SM_FS1 /
-//   SM_FS2; each 128-deep MFMA covers one K block, whose unit-scale product
-//   is added to the accumulators times sa * sb.  No workspace.
+// Both run the GEMM kernel of gemm_core.h; the FP32 scale rows ride the
+// stage copies into LDS like E8M0 scale bytes, and each 128-deep MFMA covers
+// one K block.
+// * TE_BLOCK_SCALES_E8M0 (modes SM_BE1 / SM_BE2): each lane casts its row's
+//   FP32 scale to E8M0 as it reads it and hands the code to the MFMA, which
+//   applies it to all four 32-blocks of the 128-block: the MXFP8 arithmetic
+//   on the cast scales.
+// * TE_BLOCK_SCALES_FP32 (SM_FS1 / SM_FS2): each block's product is computed
+//   with unit scales and added to the accumulators times sa * sb.
+// No workspace either way.
 #include "gemm_core.h"
 
 namespace temx {
@@ -51,23 +54,21 @@ te_status launch_fs2(const GemmParams& p, te_dtype fa, te_dtype fb, te_epilogue 
 }
 
 template <class C>
-te_status launch_fs(const GemmParams& p, int b_2d, te_dtype fa, te_dtype fb, te_epilogue epi, te_dtype out,
+te_status launch_fs(const GemmParams& p, bool e8m0, int b2d, te_dtype fa, te_dtype fb, te_epilogue epi, te_dtype out,
                     dim3 grid, hipStream_t stream) {
-  return b_2d ? launch_fs2<C, SM_FS2>(p, fa, fb, epi, out, grid, stream)
-              : launch_fs2<C, SM_FS1>(p, fa, fb, epi, out, grid, stream);
+  if (e8m0)
+    return b2d ? launch_fs2<C, SM_BE2>(p, fa, fb, epi, out, grid, stream)
+               : launch_fs2<C, SM_BE1>(p, fa, fb, epi, out, grid, stream);
+  return b2d ? launch_fs2<C, SM_FS2>(p, fa, fb, epi, out, grid, stream)
+             : launch_fs2<C, SM_FS1>(p, fa, fb, epi, out, grid, stream);
 }
-
-inline int64_t align256(int64_t n) { return (n + 255) & ~(int64_t)255; }
 
 }  // namespace
 }  // namespace temx
 
 using namespace temx;
 
-extern "C" size_t te_fp8_block_gemm_workspace_size(int64_t M, int64_t N, int64_t K, te_block_scaling mode) {
-  if (mode != TE_BLOCK_SCALES_E8M0 || M < 0 || N < 0 || K < 0) return 0;
-  return (size_t)(align256(M * (K / 32)) + N * (K / 32));
-}
+extern "C" size_t te_fp8_block_gemm_workspace_size(int64_t, int64_t, int64_t, te_block_scaling) { return 0; }
 
 extern "C" te_status te_fp8_block_gemm(const uint8_t* a, const float* a_scale_inv, te_dtype a_fmt,
                                        const uint8_t* b, const float* b_scale_inv, te_dtype b_fmt, int b_block_2d,
@@ -83,34 +84,18 @@ extern "C" te_status te_fp8_block_gemm(const uint8_t* a, const float* a_scale_in
              TE_ERR_SHAPE);
   const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
   TE_REQUIRE(((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 31), TE_ERR_SHAPE);
-  const bool e8m0 = mode == TE_BLOCK_SCALES_E8M0;
-  const bool work = M > 0 && N > 0 && K > 0;  // scales are read (and, for E8M0, cast)
-  if (e8m0 && work) {
-    TE_REQUIRE(workspace != nullptr, TE_ERR_NULL);
-    TE_REQUIRE(workspace_bytes >= te_fp8_block_gemm_workspace_size(M, N, K, mode), TE_ERR_WORKSPACE);
-    TE_REQUIRE(((uintptr_t)workspace & 15u) == 0, TE_ERR_ALIGN);
-  }
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const uint8_t* sa = e8m0 ? ws : reinterpret_cast<const uint8_t*>(a_scale_inv);
-  const uint8_t* sb = e8m0 ? (ws ? ws + align256(M * (K / 32)) : nullptr) : reinterpret_cast<const uint8_t*>(b_scale_inv);
+  (void)workspace;
+  (void)workspace_bytes;
+  const uint8_t* sa = reinterpret_cast<const uint8_t*>(a_scale_inv);
+  const uint8_t* sb = reinterpret_cast<const uint8_t*>(b_scale_inv);
+  // the scale arrays stand in for the E8M0 ones in the common checks (non-NULL, 4-byte aligned when read)
   te_status st = check_common(a, sa, a_fmt, b, sb, b_fmt, d, d_dtype, epi, bias, aux, M > 0 && N > 0, K > 0);
   if (st != TE_OK) return st;
   if (M == 0 || N == 0) return TE_OK;
-  if (work) {
-    TE_REQUIRE(a_scale_inv != nullptr && b_scale_inv != nullptr, TE_ERR_NULL);
-    TE_REQUIRE(((uintptr_t)a_scale_inv & 3u) == 0 && ((uintptr_t)b_scale_inv & 3u) == 0, TE_ERR_ALIGN);
-  }
-  if (e8m0) {
-    if (work) {
-      st = launch_block_scale_expand(a_scale_inv, M, 0, ws, b_scale_inv, N, b_block_2d, const_cast<uint8_t*>(sb),
-                                     K / 128, stream);
-      if (st != TE_OK) return st;
-    }
-    return te_mxfp8_gemm(a, sa, a_fmt, b, sb, b_fmt, M, N, K, d, d_dtype, epi, bias, aux, nullptr, 0, stream);
-  }
   GemmParams p{a, sa, b, sb, d, bias, aux, M, N, K, nullptr, 0};
+  const bool e8m0 = mode == TE_BLOCK_SCALES_E8M0;
   if (use_small_tile(big_tiles, K))
-    return launch_fs<Small>(p, b_block_2d, a_fmt, b_fmt, epi, d_dtype,
+    return launch_fs<Small>(p, e8m0, b_block_2d, a_fmt, b_fmt, epi, d_dtype,
                             dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))), stream);
-  return launch_fs<Big>(p, b_block_2d, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)big_tiles), stream);
+  return launch_fs<Big>(p, e8m0, b_block_2d, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)big_tiles), stream);
 }

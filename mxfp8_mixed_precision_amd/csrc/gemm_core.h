@@ -48,12 +48,18 @@ constexpr int BK = 128;
 //           accumulators times sa[m, kb] * sb[n, kb].
 //   SM_FS2  as SM_FS1, but B has one scale per 128 x 128 block
 //           ([ceil(N/128), K/128] floats).
+//   SM_BE1, SM_BE2  blockwise FP8 as SM_FS1 / SM_FS2, with each FP32 scale
+//           cast to E8M0 (the smallest power of two >= s) as it is read from
+//           LDS and handed to the MFMA as the scale of all four 32-blocks of
+//           its 128-block: the MXFP8 arithmetic on the cast scales.
 // A [rows, K/128] float array has the row stride of a [rows, K/32] byte
 // array and holds block kt of a row at byte 4 kt, where the E8M0 bytes of
 // step kt sit: the stage copies move either kind of scale unchanged, and in
 // LDS each tile row has 4 scale bytes per stage (four E8M0 codes, or one float).
-constexpr int SM_MX = 0, SM_PT = 1, SM_FS1 = 2, SM_FS2 = 3;
+constexpr int SM_MX = 0, SM_PT = 1, SM_FS1 = 2, SM_FS2 = 3, SM_BE1 = 4, SM_BE2 = 5;
 constexpr bool fp32_scales(int sm) { return sm == SM_FS1 || sm == SM_FS2; }
+constexpr bool block_scales(int sm) { return sm == SM_FS1 || sm == SM_FS2 || sm == SM_BE1 || sm == SM_BE2; }
+constexpr bool b_2d(int sm) { return sm == SM_FS2 || sm == SM_BE2; }
 
 // Workgroup tile configurations.  A BM x BN tile is computed by NWM x NWN
 // waves, each a (BM / NWM) x (BN / NWN) block of FRM x FRN MFMA tiles of
@@ -200,7 +206,7 @@ __device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, con
   }
   if (SM != SM_PT && c < C::BM / 64) {
     lds_dma4(A.scale, stage + C::kOffAScale + c * 256, off.scale, kt * 4);
-    lds_dma4(B.scale, stage + C::kOffBScale + c * 256, SM == SM_FS2 ? off.scale_2d : off.scale, kt * 4);
+    lds_dma4(B.scale, stage + C::kOffBScale + c * 256, b_2d(SM) ? off.scale_2d : off.scale, kt * 4);
   }
 }
 
@@ -221,7 +227,9 @@ struct ReadOffsets {
 // With FP32 scales, a_scale is the float of row r (fragment j: + 64 bytes)
 // and b_scale the four floats of columns 4 g .. 4 g + 3 (SM_FS1; fragment i:
 // + 64 bytes) or the one float of the wave's 128-row block of B (SM_FS2:
-// a wave's columns never straddle a 128 boundary).
+// a wave's columns never straddle a 128 boundary).  With E8M0-cast blockwise
+// scales a_scale is the float of row r, whose code serves every lane g, and
+// b_scale likewise (SM_BE1) or the wave's one block-row float (SM_BE2).
 template <class LY, int SM = SM_MX>
 __device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) {  // LY: a Cfg
   const int g = lane >> 4, r = lane & 15;
@@ -235,6 +243,10 @@ __device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) { 
     static_assert(128 % LY::WTN == 0, "a wave's columns stay inside one 128-row block of B");
     o.a_scale = LY::kOffAScale + (wm * LY::WTM + r) * 4;
     o.b_scale = LY::kOffBScale + (wn * LY::WTN + (SM == SM_FS1 ? 4 * g : 0)) * 4;
+  } else if constexpr (block_scales(SM)) {
+    static_assert(128 % LY::WTN == 0, "a wave's columns stay inside one 128-row block of B");
+    o.a_scale = LY::kOffAScale + (wm * LY::WTM + r) * 4;
+    o.b_scale = LY::kOffBScale + (wn * LY::WTN + (SM == SM_BE1 ? r : 0)) * 4;
   } else {
     o.a_scale = LY::kOffAScale + (wm * LY::WTM + r) * 4 + g;
     o.b_scale = LY::kOffBScale + (wn * LY::WTN + r) * 4 + g;
@@ -251,22 +263,28 @@ __device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) { 
 // MFMA that uses it (measured: 2-12% faster across the GEMM shapes than
 // shifting the byte out of the row's scale word).  Rows 16 j further are 2 KB
 // further (an immediate offset).
-template <bool UNIT = false>
+// Scale kinds of a fragment read: the E8M0 byte of block g, 2^0, or the
+// E8M0 cast of the row's FP32 block scale.
+constexpr int kScaleByte = 0, kScaleUnit = 1, kScaleCast = 2;
+
+template <int SK = kScaleByte>
 __device__ __forceinline__ Frag read_frag(const uint8_t* stage, int data_off, int data_off2, int scale_off, int j) {
   const uint4 lo = *reinterpret_cast<const uint4*>(stage + data_off + j * 16 * BK);
   const uint4 hi = *reinterpret_cast<const uint4*>(stage + data_off2 + j * 16 * BK);
   Frag f;
   f.v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-  f.s = UNIT ? 127 : (int)stage[scale_off + j * 64];  // unit: every MFMA block scale is 2^0
+  if constexpr (SK == kScaleUnit) f.s = 127;
+  else if constexpr (SK == kScaleCast) f.s = (int)e8m0_at_least(*reinterpret_cast<const float*>(stage + scale_off + j * 64));
+  else f.s = (int)stage[scale_off + j * 64];
   return f;
 }
 
 template <class LY, int FA, int FB, int SM = SM_MX>
 __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN][LY::FRM], const ReadOffsets& ro) {
-  constexpr bool UNIT = SM != SM_MX;
+  constexpr int SK = SM == SM_MX ? kScaleByte : (SM == SM_BE1 || SM == SM_BE2) ? kScaleCast : kScaleUnit;
   Frag bop[LY::FRM];
 #pragma unroll
-  for (int j = 0; j < LY::FRM; ++j) bop[j] = read_frag<UNIT>(stage, ro.a_data, ro.a_data2, ro.a_scale, j);
+  for (int j = 0; j < LY::FRM; ++j) bop[j] = read_frag<SK>(stage, ro.a_data, ro.a_data2, ro.a_scale, j);
   if constexpr (fp32_scales(SM)) {
     // one K block per step: P = the block's unit-scale product, then
     // acc += (sa[m] * sb[n]) * P with one rounding (fma)
@@ -281,7 +299,7 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN
     }
 #pragma unroll
     for (int i = 0; i < LY::FRN; ++i) {
-      const Frag aop = read_frag<true>(stage, ro.b_data, ro.b_data2, 0, i);
+      const Frag aop = read_frag<kScaleUnit>(stage, ro.b_data, ro.b_data2, 0, i);
       float4 sb4 = make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (SM == SM_FS1) sb4 = *reinterpret_cast<const float4*>(stage + ro.b_scale + i * 64);
 #pragma unroll
@@ -301,9 +319,17 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN
     }
     return;
   }
+  int sb_code = 0;  // SM_BE2: one E8M0 code for all of the wave's columns
+  if constexpr (SM == SM_BE2) sb_code = (int)e8m0_at_least(*reinterpret_cast<const float*>(stage + ro.b_scale));
 #pragma unroll
   for (int i = 0; i < LY::FRN; ++i) {
-    const Frag aop = read_frag<UNIT>(stage, ro.b_data, ro.b_data2, ro.b_scale, i);
+    Frag aop;
+    if constexpr (SM == SM_BE2) {
+      aop = read_frag<kScaleUnit>(stage, ro.b_data, ro.b_data2, 0, i);
+      aop.s = sb_code;
+    } else {
+      aop = read_frag<SK>(stage, ro.b_data, ro.b_data2, ro.b_scale, i);
+    }
 #pragma unroll
     for (int j = 0; j < LY::FRM; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop.v, bop[j].v, acc[i][j], MfmaFmt<FB>::v,
@@ -515,7 +541,7 @@ __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
   const int tn = in_band / band_rows;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, BM);
-  const Operand B = SM == SM_FS2 ? make_operand_2d(p.b, p.b_scale, n0, p.N - n0, p.K, BN)
+  const Operand B = b_2d(SM) ? make_operand_2d(p.b, p.b_scale, n0, p.N - n0, p.K, BN)
                                  : make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, BN);
   v4f acc[LY::FRN][LY::FRM];
   mainloop<LY, FA, FB, SM>(lds, acc, A, B, p.K, wave, lane);

@@ -66,6 +66,20 @@ __device__ __forceinline__ float e8m0_to_float(uint32_t code) {
   return __uint_as_float(bits);
 }
 
+// E8M0 code of the smallest E8M0 value >= s (the cast of an FP32 block
+// scale inverse): saturates at 2^127 (+inf included); +-0 and positive values
+// up to 2^-127 give code 0 (2^-127); NaN and negative values give 255.
+// Selects only, no branches: it runs inside the GEMM's MFMA loop.
+__device__ __forceinline__ uint32_t e8m0_at_least(float s) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t mag = u & 0x7FFFFFFFu;
+  const uint32_t e = mag >> 23, m = mag & 0x7FFFFFu;
+  // above 2^(e-127) rounds up; a subnormal rounds up only past 2^-127 (m = 0x400000)
+  const uint32_t c = min(e + (m > (e == 0 ? 0x400000u : 0u) ? 1u : 0u), 254u);
+  const bool bad = mag > 0x7F800000u || (u != mag && mag != 0);  // NaN, or negative non-zero
+  return bad ? 255u : c;
+}
+
 // Byte-wise saturation fix-up: the hardware converts give 0x7F (E4M3 NaN) or
 // 0x7C (E5M2 Inf) with the sign bit for magnitudes past the largest finite
 // value; those bytes are replaced by the largest finite code (one less).

@@ -99,7 +99,7 @@ def test_graph_replays_equal_eager_results_newer_ops():
         "dq_r": torch.empty((M, N), **u8), "ds_r": torch.empty((M, N // 32), **u8),
         "dq_c": torch.empty((N, M), **u8), "ds_c": torch.empty((N, M // 32), **u8), "db": torch.empty(N, **f32),
         "mx_d": torch.empty((M, N), **u8), "mx_s": torch.empty((M, N // 32), **u8), "mx_aux": torch.empty((M, N), **bf),
-        "dgelu": torch.empty((M, N), **bf), "acc": torch.empty((M, N), **f32),
+        "dgelu": torch.empty((M, N), **bf),
         "pa": torch.empty((M, K), **u8), "pa_inv": torch.empty(1, **f32),
         "pb": torch.empty((N, K), **u8), "pb_inv": torch.empty(1, **f32), "pt_d": torch.empty((M, N), **bf),
         "ba": torch.empty((M, K), **u8), "bsa": torch.empty((M, K // 128), **f32),
@@ -146,6 +146,8 @@ def test_graph_replays_equal_eager_results_newer_ops():
         snap.update({"state_" + k: v.clone() for k, v in state.items()})
         return snap
 
+    for v in out.values():
+        v.zero_()  # every output is written by the step: replays must reproduce all of them
     restore()
     step()
     torch.cuda.synchronize()
