@@ -229,7 +229,8 @@ te_status te_mxfp8_quantize_bgrad(const uint16_t* x, int64_t rows, int64_t cols,
  *            DGELU (read), NULL otherwise
  *   TE_EPI_ACCUMULATE needs d_dtype == TE_FP32 (TE_ERR_DTYPE otherwise).
  *   Shapes: M, N, K >= 0; K % 128 == 0, M % 16 == 0, N % 16 == 0 (the
- *   [HK-PR] checks; M and N need not be multiples of the tile size).
+ *   [HK-PR] checks; M and N need not be multiples of the tile size);
+ *   K <= 2^23 (the tile copies use 32-bit offsets), M, N < 2^31 - 256.
  *   M == 0 or N == 0 enqueues nothing; K == 0 gives D = epi(0).
  *   workspace: none is needed (te_mxfp8_gemm_workspace_size returns 0);
  *   pass NULL / 0.
@@ -296,7 +297,7 @@ te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scale, te_dtype
  *   b           uint8 [G * N, K] (experts stacked), b_scale [G * N, K/32]
  *   d           [total_m, N] (d_dtype as te_mxfp8_gemm)
  *   bias        bf16 [G, N] iff epi != NONE; aux bf16 [total_m, N] iff GELU-aux
- *   Shapes: total_m >= 0, N % 16 == 0, K % 128 == 0, K > 0, N > 0.
+ *   Shapes: total_m >= 0, N % 16 == 0, K % 128 == 0, 0 < K <= 2^23, N > 0.
  *   workspace: none (NULL / 0).
  */
 te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_splits, int64_t total_m,

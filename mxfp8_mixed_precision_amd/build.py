@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtemx.so")
-SOURCES = ["quantize.hip", "amax_cast.hip", "gemm.hip", "block_gemm.hip", "block_scale.hip", "block_quantize.hip", "status.hip"]
+SOURCES = ["quantize.hip", "amax_cast.hip", "gemm.hip", "block_gemm.hip", "block_gemm_e8m0.hip", "block_gemm_fp32.hip", "block_scale.hip",
+           "block_quantize.hip", "status.hip"]
 ARCH = "gfx950"
 
 

@@ -110,18 +110,16 @@ extern "C" te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_
   (void)workspace_bytes;
   TE_REQUIRE(M >= 0 && N >= 0 && K >= 0, TE_ERR_SHAPE);
   TE_REQUIRE(K % 128 == 0 && M % 16 == 0 && N % 16 == 0, TE_ERR_SHAPE);
-  TE_REQUIRE(M <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 31) - BK,
-             TE_ERR_SHAPE);
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  TE_REQUIRE(((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 31), TE_ERR_SHAPE);
+  TE_REQUIRE(dense_shape_ok(M, N, K), TE_ERR_SHAPE);
   te_status st = check_common(a, a_scale, a_fmt, b, b_scale, b_fmt, d, d_dtype, epi, bias, aux, M > 0 && N > 0, K > 0);
   if (st != TE_OK) return st;
   if (M == 0 || N == 0) return TE_OK;
   GemmParams p{a, a_scale, b, b_scale, d, bias, aux, M, N, K, nullptr, 0};
-  if (use_small_tile(big_tiles, K))
-    return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_dtype,
-                                 dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))), stream);
-  return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)big_tiles), stream);
+  const Tile t = pick_tile(M, N, K);
+  const dim3 grid = tile_grid(t, M, N);
+  if (t == Tile::SmallDeep) return launch2<SmallDeep, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
+  if (t == Tile::Small) return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
+  return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
 }
 
 extern "C" te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,
@@ -135,20 +133,18 @@ extern "C" te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scal
   TE_REQUIRE(d_fmt == TE_E4M3 || d_fmt == TE_E5M2, TE_ERR_DTYPE);
   TE_REQUIRE(M >= 0 && N >= 0 && K >= 0, TE_ERR_SHAPE);
   TE_REQUIRE(K % 128 == 0 && M % 16 == 0 && N % 32 == 0, TE_ERR_SHAPE);
-  TE_REQUIRE(M <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 31) - BK,
-             TE_ERR_SHAPE);
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  TE_REQUIRE(((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 31), TE_ERR_SHAPE);
+  TE_REQUIRE(dense_shape_ok(M, N, K), TE_ERR_SHAPE);
   // the common checks with the bf16 D this output stands for
   te_status st = check_common(a, a_scale, a_fmt, b, b_scale, b_fmt, d, TE_BF16, epi, bias, aux, M > 0 && N > 0, K > 0);
   if (st != TE_OK) return st;
   if (M == 0 || N == 0) return TE_OK;
   TE_REQUIRE(d_scale != nullptr, TE_ERR_NULL);
   GemmParams p{a, a_scale, b, b_scale, d, bias, aux, M, N, K, nullptr, 0, d_scale};
-  if (use_small_tile(big_tiles, K))
-    return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_fmt,
-                                 dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))), stream);
-  return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_fmt, dim3((unsigned)big_tiles), stream);
+  const Tile t = pick_tile(M, N, K);
+  const dim3 grid = tile_grid(t, M, N);
+  if (t == Tile::SmallDeep) return launch2<SmallDeep, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
+  if (t == Tile::Small) return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
+  return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
 }
 
 extern "C" te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_dtype a_fmt, const uint8_t* b,
@@ -160,10 +156,7 @@ extern "C" te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_
   TE_REQUIRE(epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX, TE_ERR_VALUE);
   TE_REQUIRE(M >= 0 && N >= 0 && K >= 0, TE_ERR_SHAPE);
   TE_REQUIRE(K % 128 == 0 && M % 16 == 0 && N % 16 == 0, TE_ERR_SHAPE);
-  TE_REQUIRE(M <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 31) - BK,
-             TE_ERR_SHAPE);
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  TE_REQUIRE(((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 31), TE_ERR_SHAPE);
+  TE_REQUIRE(dense_shape_ok(M, N, K), TE_ERR_SHAPE);
   // the scale pointers stand in for the block-scale arrays in the common checks
   te_status st = check_common(a, reinterpret_cast<const uint8_t*>(a_scale_inv), a_fmt, b,
                               reinterpret_cast<const uint8_t*>(b_scale_inv), b_fmt, d, d_dtype, epi, bias, aux,
@@ -173,10 +166,11 @@ extern "C" te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_
   TE_REQUIRE(a_scale_inv != nullptr && b_scale_inv != nullptr, TE_ERR_NULL);
   // the block-scale descriptors are never read in per-tensor mode; they point at the data
   GemmParams p{a, a, b, b, d, bias, aux, M, N, K, nullptr, 0, nullptr, a_scale_inv, b_scale_inv};
-  if (use_small_tile(big_tiles, K))
-    return launch_pt<Small>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128))),
-                            stream);
-  return launch_pt<Big>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)big_tiles), stream);
+  const Tile t = pick_tile(M, N, K);
+  const dim3 grid = tile_grid(t, M, N);
+  if (t == Tile::SmallDeep) return launch_pt<SmallDeep>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
+  if (t == Tile::Small) return launch_pt<Small>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
+  return launch_pt<Big>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
 }
 
 extern "C" te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_splits, int64_t total_m,
@@ -190,7 +184,7 @@ extern "C" te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_
   TE_REQUIRE(num_groups >= 1 && num_groups <= kMaxGroups, TE_ERR_SHAPE);
   TE_REQUIRE(total_m >= 0 && N > 0 && K > 0, TE_ERR_SHAPE);
   TE_REQUIRE(K % 128 == 0 && N % 16 == 0, TE_ERR_SHAPE);
-  TE_REQUIRE(total_m <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 31) - BK,
+  TE_REQUIRE(total_m <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 23),
              TE_ERR_SHAPE);
   TE_REQUIRE((total_m / 128 + num_groups) * ((N + 127) / 128) < ((int64_t)1 << 31), TE_ERR_SHAPE);
   TE_REQUIRE(m_splits != nullptr, TE_ERR_NULL);

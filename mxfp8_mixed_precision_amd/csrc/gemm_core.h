@@ -65,16 +65,23 @@ constexpr bool b_2d(int sm) { return sm == SM_FS2 || sm == SM_BE2; }
 // waves, each a (BM / NWM) x (BN / NWN) block of FRM x FRN MFMA tiles of
 // 16 x 16; the last NCOPY waves issue the stage copies.  One stage in LDS is
 // A data [BM][128], B data [BN][128], A scales [BM][4], B scales [BN][4];
-// two stages.
+// NSTAGE stages form a ring.
 //   Big:   256 x 256, 8 waves of 64 x 128 (two per SIMD, 128 accumulators),
 //          waves 4-7 copy; 132 KB of LDS, one workgroup per CU.
 //   Small: 128 x 128, 4 waves of 64 x 64 (64 accumulators), all four copy;
 //          66 KB of LDS, two workgroups per CU.  For grids the big tile
 //          cannot fill (few or ragged row tiles).
-template <int BM_, int BN_, int NWM_, int NWN_, int NCOPY_>
+//   SmallDeep: the small tile with 4 stages (132 KB of LDS, one workgroup
+//          per CU), for grids of at most one small tile per CU and long K.
+//          A 128 x 128 x 128 step computes for ~0.25 us, far less than the
+//          latency of its copies from L2 / MALL; three stages in flight
+//          cover it where one does not (measured on MI355X: 4096 x 1024 x
+//          4096 33.8 -> 28.3 us, 2048 x 2048 x 8192 55.3 -> 45.2 us; with
+//          K = 1024 the longer prologue costs a few percent).
+template <int BM_, int BN_, int NWM_, int NWN_, int NCOPY_, int NSTAGE_ = 2>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, NWM = NWM_, NWN = NWN_, NW = NWM * NWN, kThreads = 64 * NW;
-  static constexpr int NCOPY = NCOPY_;
+  static constexpr int NCOPY = NCOPY_, NSTAGE = NSTAGE_;
   static constexpr int WTM = BM / NWM, WTN = BN / NWN;
   static constexpr int FRM = WTM / 16, FRN = WTN / 16;
   static constexpr int kAData = BM * BK, kBData = BN * BK, kAScale = BM * 4, kBScale = BN * 4;
@@ -82,12 +89,17 @@ struct Cfg {
   static constexpr int kOffAScale = kAData + kBData;
   static constexpr int kOffBScale = kOffAScale + kAScale;
   static constexpr int kStage = kOffBScale + kBScale;
-  static constexpr int kLds = 2 * kStage;
+  static constexpr int kLds = NSTAGE * kStage;
+  // scale slices (64 rows of one operand) per copier wave: every copier issues
+  // the same number of copies per stage
+  static constexpr int kScaleSlicesPerCopier = 2 * (BM / 64) / NCOPY;
+  static_assert(2 * (BM / 64) % NCOPY == 0, "scale slices split evenly over the copier waves");
   static_assert(BM == BN, "one row clamp and one copy scheme serve both operands");
   static_assert(NCOPY % 2 == 0 && (BM / 8) % NCOPY == 0 && (BM / 64) <= NCOPY, "copy slices per copier wave");
 };
 using Big = Cfg<256, 256, 4, 2, 4>;
 using Small = Cfg<128, 128, 2, 2, 4>;
+using SmallDeep = Cfg<128, 128, 2, 2, 4, 4>;
 constexpr int kGroupM = 4;      // row-tile band of the raster order
 constexpr int kMaxGroups = 1024;
 
@@ -181,16 +193,14 @@ __device__ __forceinline__ void lds_dma4(const i32x4& rsrc, uint32_t lds_addr, i
 // scale slice c of both operands.
 struct CopyOffsets {
   int data;
-  int scale;
-  int scale_2d;  // SM_FS2 B scales: rows 64 c .. 64 c + 63 all lie in 128-row block c / 2
+  int scale;  // lane l's row of a 64-row scale slice: l * (K/32)
 };
 
 __device__ __forceinline__ CopyOffsets copy_offsets(int64_t K, int c, int lane) {
   const int chunk = (lane & 7) ^ (lane >> 4) ^ ((c & 1) << 2);
   CopyOffsets o;
   o.data = (int)((8 * c + (lane >> 3)) * K) + chunk * 16;
-  o.scale = (int)((64 * c + lane) * (K / 32));
-  o.scale_2d = (int)((c >> 1) * (K / 32));
+  o.scale = (int)(lane * (K / 32));
   return o;
 }
 
@@ -204,9 +214,20 @@ __device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, con
     lds_dma16(A.data, stage + q * 1024, off.data, so);
     lds_dma16(B.data, stage + C::kOffBData + q * 1024, off.data, so);
   }
-  if (SM != SM_PT && c < C::BM / 64) {
-    lds_dma4(A.scale, stage + C::kOffAScale + c * 256, off.scale, kt * 4);
-    lds_dma4(B.scale, stage + C::kOffBScale + c * 256, b_2d(SM) ? off.scale_2d : off.scale, kt * 4);
+  if constexpr (SM != SM_PT) {
+#pragma unroll
+    for (int i = 0; i < C::kScaleSlicesPerCopier; ++i) {
+      const int q = c + C::NCOPY * i, s64 = q >> 1;  // slice q: operand q & 1, rows 64 s64 .. 64 s64 + 63
+      const int slice_off = (int)(64 * s64 * (K / 32)) + kt * 4;
+      if (q & 1) {
+        if constexpr (b_2d(SM))  // the 64 rows lie in 128-row block s64 / 2: one scale row for all lanes
+          lds_dma4(B.scale, stage + C::kOffBScale + s64 * 256, 0, (int)((s64 >> 1) * (K / 32)) + kt * 4);
+        else
+          lds_dma4(B.scale, stage + C::kOffBScale + s64 * 256, off.scale, slice_off);
+      } else {
+        lds_dma4(A.scale, stage + C::kOffAScale + s64 * 256, off.scale, slice_off);
+      }
+    }
   }
 }
 
@@ -337,10 +358,19 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN
   }
 }
 
-// Double-buffered K loop: the copies of step kt+1 are in flight while step
-// kt computes; each stage is read only after s_waitcnt vmcnt(0) and a barrier
-// (all copies landed), and refilled only after the next barrier (all waves
-// finished reading it).
+// s_waitcnt vmcnt(N) lgkmcnt(0) expcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14));
+}
+
+// K loop over a ring of NSTAGE stages: the copies of steps kt+1 ..
+// kt+NSTAGE-1 are in flight while step kt computes.  Stage kt is read only
+// after each copier has waited until no more than the later stages' copies
+// are outstanding (vmcnt counts a wave's copies, which complete in issue
+// order) and a barrier; a stage is refilled only after the barrier that
+// follows its last read.  With two stages this is plain double buffering.
 //
 // Only the last NCOPY waves issue the copies.  A direct-to-LDS buffer load
 // holds up the wave that issues it for ~70-90 clocks (measured on gfx950,
@@ -363,13 +393,26 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
   const CopyOffsets off = copy_offsets(K, copier ? c : 0, lane);
   const ReadOffsets ro = read_offsets<LY, SM>(wm, wn, lane);
   const uint32_t lds_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
-  if (copier) load_stage<LY, SM>(lds_addr, A, B, off, K, 0, c);
+  constexpr int S = LY::NSTAGE;
+  static_assert(S >= 2 && S <= 4, "the waits below cover up to two later stages in flight");
+  // copies per copier wave and stage (the same for every copier)
+  constexpr int kPerStage = 2 * (LY::BM / 8 / LY::NCOPY) + (SM == SM_PT ? 0 : LY::kScaleSlicesPerCopier);
+  if (copier) {
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s)
+      if (s < kt_n) load_stage<LY, SM>(lds_addr + s * LY::kStage, A, B, off, K, s, c);
+  }
   for (int kt = 0; kt < kt_n; ++kt) {
-    __builtin_amdgcn_s_waitcnt(0);
+    // stage kt has landed once at most `ahead` later stages' copies are outstanding
+    const int ahead = min(S - 2, kt_n - 1 - kt);
+    if (S > 2 && ahead >= 2) wait_vmcnt<2 * kPerStage>();
+    else if (S > 2 && ahead == 1) wait_vmcnt<kPerStage>();
+    else __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (copier && kt + 1 < kt_n) load_stage<LY, SM>(lds_addr + ((kt + 1) & 1) * LY::kStage, A, B, off, K, kt + 1, c);
+    if (copier && kt + S - 1 < kt_n)
+      load_stage<LY, SM>(lds_addr + ((kt + S - 1) % S) * LY::kStage, A, B, off, K, kt + S - 1, c);
 
-    compute<LY, FA, FB, SM>(lds + (kt & 1) * LY::kStage, acc, ro);
+    compute<LY, FA, FB, SM>(lds + (kt % S) * LY::kStage, acc, ro);
   }
 }
 
@@ -629,6 +672,29 @@ __global__ __launch_bounds__(LY::kThreads) void mx_grouped_gemm_kernel(GemmParam
 inline bool use_small_tile(int64_t big_tiles, int64_t K) {
   const int64_t cus = device_cu_count();
   return big_tiles < cus || (big_tiles < 2 * cus && K <= 4096);
+}
+
+// Tile configuration of a dense GEMM: SmallDeep for grids of at most one
+// small tile per CU with K >= 2048 (16 or more K steps), else as above.
+enum class Tile { Big, Small, SmallDeep };
+
+inline Tile pick_tile(int64_t M, int64_t N, int64_t K) {
+  const int64_t small_tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (small_tiles <= (int64_t)device_cu_count() && K >= 2048) return Tile::SmallDeep;
+  return use_small_tile(((M + 255) / 256) * ((N + 255) / 256), K) ? Tile::Small : Tile::Big;
+}
+
+inline dim3 tile_grid(Tile t, int64_t M, int64_t N) {
+  return t == Tile::Big ? dim3((unsigned)(((M + 255) / 256) * ((N + 255) / 256)))
+                        : dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128)));
+}
+
+// Shape limits of the dense GEMMs beyond the divisibility rules: tile copies
+// use 32-bit buffer offsets (up to 225 K bytes) and a tile's rows x K bytes
+// must fit a buffer resource, so K <= 2^23; M, N and the tile count fit int.
+inline bool dense_shape_ok(int64_t M, int64_t N, int64_t K) {
+  return M <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 23) &&
+         ((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 31);
 }
 
 inline te_status check_common(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,

@@ -20,6 +20,15 @@ inline te_status launch_status() {
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// The blockwise FP8 GEMM in one scale mode (block_gemm_e8m0.hip,
+// block_gemm_fp32.hip), after te_fp8_block_gemm has checked the arguments.
+te_status launch_block_gemm_e8m0(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int b2d,
+                                 int64_t M, int64_t N, int64_t K, void* d, te_dtype d_dtype, te_epilogue epi,
+                                 const uint16_t* bias, uint16_t* aux, te_dtype fa, te_dtype fb, hipStream_t stream);
+te_status launch_block_gemm_fp32(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int b2d,
+                                 int64_t M, int64_t N, int64_t K, void* d, te_dtype d_dtype, te_epilogue epi,
+                                 const uint16_t* bias, uint16_t* aux, te_dtype fa, te_dtype fb, hipStream_t stream);
+
 }  // namespace temx
 
 #define TE_REQUIRE(cond, status) \

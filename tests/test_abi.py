@@ -116,6 +116,7 @@ def gemm(a=P, sa=P, fa=te.TE_E4M3, b=P, sb=P, fb=te.TE_E4M3, M=256, N=256, K=256
 
 def test_gemm_validation():
     assert gemm(K=192) == te.TE_ERR_SHAPE       # K % 128
+    assert gemm(K=(1 << 23) + 128) == te.TE_ERR_SHAPE  # beyond the 32-bit copy offsets
     assert gemm(M=72) == te.TE_ERR_SHAPE        # M % 16
     assert gemm(N=40) == te.TE_ERR_SHAPE        # N % 16
     assert gemm(M=-16) == te.TE_ERR_SHAPE
@@ -152,6 +153,7 @@ def mxout(a=P, sa=P, fa=te.TE_E4M3, b=P, sb=P, fb=te.TE_E4M3, M=256, N=256, K=25
 def test_gemm_mxout_validation():
     assert mxout(N=48) == te.TE_ERR_SHAPE                 # blocks of 32 along N
     assert mxout(K=192) == te.TE_ERR_SHAPE
+    assert mxout(K=(1 << 23) + 128) == te.TE_ERR_SHAPE
     assert mxout(df=te.TE_BF16) == te.TE_ERR_DTYPE
     assert mxout(df=te.TE_E8M0) == te.TE_ERR_DTYPE
     assert mxout(epi=te.TE_EPI_DGELU, aux=P3) == te.TE_ERR_VALUE      # forward epilogues only
@@ -196,6 +198,7 @@ def fp8gemm(a=P, sa=P3, fa=te.TE_E4M3, b=P, sb=P3, fb=te.TE_E4M3, M=256, N=256, 
 
 def test_fp8_gemm_validation():
     assert fp8gemm(K=192) == te.TE_ERR_SHAPE
+    assert fp8gemm(K=(1 << 23) + 128) == te.TE_ERR_SHAPE
     assert fp8gemm(epi=te.TE_EPI_DGELU, aux=P3) == te.TE_ERR_VALUE
     assert fp8gemm(fa=te.TE_E5M2, fb=te.TE_E5M2) == te.TE_ERR_DTYPE
     assert fp8gemm(dt=te.TE_E4M3) == te.TE_ERR_DTYPE
@@ -218,6 +221,7 @@ def test_block_gemm_workspace_and_validation():
     assert te.te_fp8_block_gemm_workspace_size(8192, 8192, 8192, "fp32") == 0
     for mode in (te.TE_BLOCK_SCALES_E8M0, te.TE_BLOCK_SCALES_FP32):
         assert blockgemm(mode=mode, K=192) == te.TE_ERR_SHAPE
+        assert blockgemm(mode=mode, K=(1 << 23) + 128) == te.TE_ERR_SHAPE
         assert blockgemm(mode=mode, N=40) == te.TE_ERR_SHAPE
         assert blockgemm(mode=mode, b2d=2) == te.TE_ERR_VALUE
         assert blockgemm(mode=mode, fa=te.TE_E5M2, fb=te.TE_E5M2) == te.TE_ERR_DTYPE
@@ -263,6 +267,7 @@ def test_grouped_validation():
     assert grouped(G=1025) == te.TE_ERR_SHAPE
     assert grouped(T=-1) == te.TE_ERR_SHAPE
     assert grouped(K=192) == te.TE_ERR_SHAPE
+    assert grouped(K=(1 << 23) + 128) == te.TE_ERR_SHAPE
     assert grouped(N=40) == te.TE_ERR_SHAPE
     assert grouped(K=0) == te.TE_ERR_SHAPE
     assert grouped(splits=None) == te.TE_ERR_NULL

@@ -102,7 +102,8 @@ def run(mode, qa, sa, fa, qb, sb, fb, b_2d, epi="none", bias=None, out_dtype=tor
 @pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("b_2d", [False, True])
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
-@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (272, 304, 384), (16, 16, 1024), (8192, 4112, 512)])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (272, 304, 384), (16, 16, 1024), (8192, 4112, 512),
+                                   (272, 304, 2176)])
 def test_block_gemm_exact_bitexact(mode, b_2d, fa, fb, M, N, K):
     if M * N > 1 << 22 and (fa, fb) != ("e4m3", "e4m3"):
         pytest.skip("the big-tile shape runs once per mode and B layout")

@@ -63,7 +63,8 @@ def per_tensor_operands(M, N, K, seed):
 
 
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
-@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256)])
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
+                                   (272, 400, 2176)])
 def test_per_tensor_gemm(epi, M, N, K):
     qa, ia, qb, ib = per_tensor_operands(M, N, K, 96 + K)
     bias_bits = None if epi == "none" else workloads.normal_bf16(97, N, (N,), 0.5)

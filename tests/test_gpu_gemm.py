@@ -40,7 +40,9 @@ def exact_codes(rng, shape, fmt):
 
 
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
-@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (272, 304, 384), (16, 16, 256), (512, 768, 1024)])
+# (272, 304, 2176) and (1024, 2048, 4096): one small tile per CU at most, K >= 2048 (the 4-stage tile)
+@pytest.mark.parametrize("M,N,K", [(256, 256, 128), (272, 304, 384), (16, 16, 256), (512, 768, 1024),
+                                   (272, 304, 2176), (1024, 2048, 4096)])
 def test_gemm_exact_integer_bitexact(fa, fb, M, N, K):
     rng = np.random.default_rng(M * 7 + N * 3 + K)
     qa, qb = exact_codes(rng, (M, K), fa), exact_codes(rng, (N, K), fb)
@@ -169,7 +171,7 @@ def test_hybrid_backward_sampled(name):
 
 
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
-@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640)])
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (1040, 784, 2176)])
 def test_ragged_shapes_and_epilogues(epi, M, N, K):
     spec = workloads.GemmSpec("ragged", M, N, K, "e4m3", "e4m3", epi,
                               workloads.TensorSpec(50, M, (M, K), 1.0, 0.01),
@@ -308,7 +310,8 @@ def backward_operands(M, N, K, seed):
     return qa, sa, qb, sb, oqa, osa, oqb, osb
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256)])
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
+                                   (272, 400, 2176)])
 def test_dgelu_epilogue(M, N, K):
     qa, sa, qb, sb, oqa, osa, oqb, osb = backward_operands(M, N, K, 70 + K)
     pre = workloads.normal_bf16(72, M + N, (M, N), 2.0, 0.0)   # the forward's saved pre-activation
@@ -345,7 +348,8 @@ def test_dgelu_epilogue(M, N, K):
         assert np.all(err[r, cc] <= bound[r, cc] + np.abs(slope[r, cc]) * h)
 
 
-@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256)])
+@pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
+                                   (272, 400, 2176)])
 def test_accumulate_epilogue(M, N, K):
     qa, sa, qb, sb, oqa, osa, oqb, osb = backward_operands(M, N, K, 80 + K)
     rng = np.random.default_rng(M + N + K)
@@ -412,7 +416,8 @@ def test_grouped_backward_epilogues_match_dense(epi):
 
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
 @pytest.mark.parametrize("M,N,K,out_fmt", [(16, 32, 128, "e4m3"), (272, 416, 256, "e4m3"), (1040, 800, 640, "e4m3"),
-                                           (4096 + 48, 4096 + 32, 256, "e4m3"), (272, 416, 256, "e5m2")])
+                                           (4096 + 48, 4096 + 32, 256, "e4m3"), (272, 416, 256, "e5m2"),
+                                           (272, 416, 2176, "e4m3")])
 def test_mxfp8_output_equals_quantized_bf16_output(epi, M, N, K, out_fmt):
     # the codes must be exactly the rowwise quantization of the bf16 D that
     # te_mxfp8_gemm writes for the same inputs (itself checked against the
