@@ -1,4 +1,5 @@
-// Entry points of the MXFP8, per-tensor FP8 and grouped GEMMs (kernels in gemm_core.h).
+// Entry points of the MXFP8, MXFP8-output, per-tensor FP8 and grouped GEMMs (kernels in
+// gemm_core.h).
 #include "gemm_core.h"
 
 namespace temx {

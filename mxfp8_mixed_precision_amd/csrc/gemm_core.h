@@ -1,12 +1,16 @@
-// MXFP8 GEMM ("TN": A [M, K], B [N, K], D = A . B^T) with bias / GELU(tanh) /
-// GELU-aux epilogues, dense and grouped, for gfx950.
+// The GEMM kernels of the library ("TN": A [M, K], B [N, K], D = A . B^T) for
+// gfx950: MXFP8, per-tensor FP8 and blockwise FP8 operands (template scaling
+// modes, see SM_* below), bias / GELU(tanh) / GELU-aux / dgelu / accumulate
+// epilogues and an MXFP8-output epilogue, dense and grouped.  Entry points:
+// gemm.hip (MXFP8, per-tensor, grouped) and block_gemm*.hip (blockwise).
 //
 // Method: "HipKittens MXFP8 GEMM Support" (ROCm/TransformerEngine PR #566):
 // an MXFP8 GEMM with BIAS and GELU AUX epilogues; review threads: 1-D MXFP8
 // scaling, K % 128 == 0, M % 16 == 0, N % 16 == 0, "TN" operands.  GELU is
 // the tanh approximation ("Getting Started", TE JAX quickstart).  The grouped
 // form is the single-launch grouped GEMM of "Transformer Engine On ROCm and
-// AMDGPU" ("Grouped GEMM using CK_Tile").
+// AMDGPU" ("Grouped GEMM using CK_Tile"); the blockwise modes follow its
+// section "Blockwise FP8 GEMM support on ROCm (gfx942 and gfx950)".
 //
 // Design for CDNA4:
 // * v_mfma_scale_f32_16x16x128_f8f6f4 consumes the fp8 codes and the E8M0
@@ -19,10 +23,11 @@
 //   epilogue stores 8 bytes (bf16) per lane straight from registers.
 // * 256 x 256 workgroup tile, 8 waves in 4 x 2 (two per SIMD), 64 x 128 per
 //   wave (4 x 8 MFMA tiles = 128 fp32 accumulators per lane), K step 128;
-//   a 128 x 128 tile (4 waves of 64 x 64) for grids the big tile cannot fill.
+//   a 128 x 128 tile (4 waves of 64 x 64) for grids the big tile cannot fill,
+//   with 2 or 4 LDS stages (see Cfg).
 // * A, B and their scale tiles are copied global -> LDS with direct-to-LDS
-//   buffer loads (buffer_load_dwordx4 / _dword ... lds), double-buffered
-//   (2 x 66 KB), issued by one wave per SIMD.
+//   buffer loads (buffer_load_dwordx4 / _dword ... lds) into a ring of
+//   stages, issued by one wave per SIMD.
 // * Workgroup -> tile mapping is XCD-aware: workgroups are dealt round-robin
 //   to the 8 XCDs, so each XCD is given a contiguous run of tiles (grouped in
 //   bands of 4 row-tiles) and its L2 sees the reuse.
