@@ -423,34 +423,48 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
 
 // Epilogue from registers.  acc[i][j][e] is D[m][n] with
 // m = m0 + WTM wm + 16 j + (lane & 15), n = n0 + WTN wn + 16 i + 4 (lane >> 4) + e.
+// A store instruction writes 32 bytes of each of 16 rows; the row fragments
+// are the outer loop, so the pieces of one row's line leave in consecutive
+// stores and meet in L2 before it writes the line back (measured: 4096 x
+// 4096 x 1024 with GELU aux 42.2 -> 37.8 us, against the column-fragment
+// order, whose scattered partial lines doubled the bytes written).
 template <class LY, int EPI, int OUT>
 __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], void* d, uint16_t* aux,
                                          const uint16_t* bias, int64_t m0, int64_t m_end, int64_t n0, int64_t N,
                                          int wave, int lane) {
   const int wm = wave / LY::NWN, wn = wave % LY::NWN;
   const int g = lane >> 4, r = lane & 15;
+  // bias of the lane's columns, all fragments
+  float bv[LY::FRN][4];
 #pragma unroll
   for (int i = 0; i < LY::FRN; ++i) {
     const int64_t n = n0 + wn * LY::WTN + 16 * i + 4 * g;
-    if (n >= N) continue;
-    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+    bv[i][0] = bv[i][1] = bv[i][2] = bv[i][3] = 0.f;
     if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
-      const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
-      b0 = bf16_bits_to_float(bb.x & 0xFFFFu);
-      b1 = bf16_bits_to_float(bb.x >> 16);
-      b2 = bf16_bits_to_float(bb.y & 0xFFFFu);
-      b3 = bf16_bits_to_float(bb.y >> 16);
+      if (n < N) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+        bv[i][0] = bf16_bits_to_float(bb.x & 0xFFFFu);
+        bv[i][1] = bf16_bits_to_float(bb.x >> 16);
+        bv[i][2] = bf16_bits_to_float(bb.y & 0xFFFFu);
+        bv[i][3] = bf16_bits_to_float(bb.y >> 16);
+      }
     }
+  }
+  // row fragments outermost: a row's pieces of the wave's columns leave in consecutive stores
 #pragma unroll
-    for (int j = 0; j < LY::FRM; ++j) {
-      const int64_t m = m0 + wm * LY::WTM + 16 * j + r;
-      if (m >= m_end) continue;
+  for (int j = 0; j < LY::FRM; ++j) {
+    const int64_t m = m0 + wm * LY::WTM + 16 * j + r;
+    if (m >= m_end) continue;
+#pragma unroll
+    for (int i = 0; i < LY::FRN; ++i) {
+      const int64_t n = n0 + wn * LY::WTN + 16 * i + 4 * g;
+      if (n >= N) continue;
       float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
       if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
-        v0 += b0;
-        v1 += b1;
-        v2 += b2;
-        v3 += b3;
+        v0 += bv[i][0];
+        v1 += bv[i][1];
+        v2 += bv[i][2];
+        v3 += bv[i][3];
       }
       if constexpr (EPI == TE_EPI_BIAS_GELU_AUX) {
         *reinterpret_cast<uint2*>(aux + m * N + n) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
@@ -498,30 +512,40 @@ __device__ __forceinline__ void epilogue_mx(const v4f (&acc)[LY::FRN][LY::FRM], 
   static_assert(EPI == TE_EPI_NONE || EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX, "forward epilogues only");
   const int wm = wave / LY::NWN, wn = wave % LY::NWN;
   const int g = lane >> 4, r = lane & 15;
+  constexpr int NB = LY::FRN / 2;  // 32-column blocks of the wave
+  float bv[NB][8];
 #pragma unroll
-  for (int b = 0; b < LY::FRN / 2; ++b) {
-    const int64_t nb = n0 + wn * LY::WTN + 32 * b;  // wave-uniform; with N % 32 == 0 a block is all in or all out
-    if (nb >= N) continue;
-    float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b) {
+    const int64_t nb = n0 + wn * LY::WTN + 32 * b;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) bv[b][k] = 0.f;
     if constexpr (EPI != TE_EPI_NONE) {
+      if (nb < N) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint2 bb = *reinterpret_cast<const uint2*>(bias + nb + 16 * h + 4 * g);
-        bv[4 * h + 0] = bf16_bits_to_float(bb.x & 0xFFFFu);
-        bv[4 * h + 1] = bf16_bits_to_float(bb.x >> 16);
-        bv[4 * h + 2] = bf16_bits_to_float(bb.y & 0xFFFFu);
-        bv[4 * h + 3] = bf16_bits_to_float(bb.y >> 16);
+        for (int h = 0; h < 2; ++h) {
+          const uint2 bb = *reinterpret_cast<const uint2*>(bias + nb + 16 * h + 4 * g);
+          bv[b][4 * h + 0] = bf16_bits_to_float(bb.x & 0xFFFFu);
+          bv[b][4 * h + 1] = bf16_bits_to_float(bb.x >> 16);
+          bv[b][4 * h + 2] = bf16_bits_to_float(bb.y & 0xFFFFu);
+          bv[b][4 * h + 3] = bf16_bits_to_float(bb.y >> 16);
+        }
       }
     }
+  }
+  // row fragments outermost, as in the bf16 epilogue: a row's pieces leave in consecutive stores
 #pragma unroll
-    for (int j = 0; j < LY::FRM; ++j) {
-      const int64_t m = m0 + wm * LY::WTM + 16 * j + r;
-      const bool row_ok = m < m_end;
+  for (int j = 0; j < LY::FRM; ++j) {
+    const int64_t m = m0 + wm * LY::WTM + 16 * j + r;
+    const bool row_ok = m < m_end;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int64_t nb = n0 + wn * LY::WTN + 32 * b;  // wave-uniform; with N % 32 == 0 a block is all in or all out
+      if (nb >= N) continue;
       float v[8];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * h + e] = acc[2 * b + h][j][e] + bv[4 * h + e];
+        for (int e = 0; e < 4; ++e) v[4 * h + e] = acc[2 * b + h][j][e] + bv[b][4 * h + e];
       if constexpr (EPI == TE_EPI_BIAS_GELU_AUX) {
         if (row_ok) {
 #pragma unroll
