@@ -18,8 +18,9 @@ FP32 block scales to MXFP8 E8M0 scales, against the CPU oracle.
   (its per-block product and fma add K/64 roundings).
 * Epilogues: with power-of-two scales and exact data both modes form the
   same fp32 accumulators, so every epilogue output of FP32 mode equals
-  E8M0 mode's bit for bit (E8M0 mode is the MXFP8 GEMM, whose epilogues are
-  checked against the oracle in test_gpu_gemm.py).
+  E8M0 mode's bit for bit; bias and GELU-aux outputs of both modes on
+  recipe data against the oracle's epilogue within the GEMM bound (GELU
+  outputs with the GELU slope), aux bit-identical to the bias epilogue's D.
 * The bench workload's GEMM at full size, sampled rows x columns.
 """
 
@@ -260,3 +261,19 @@ def test_block_square_full_size_sampled(mode):
     full_sa = np.ones((g.M, g.K // 128), np.float32)
     full_qa[rows], full_sa[rows] = oqa, osa
     check_recipe(mode, full_qa, full_sa, g.fmt_a, full_qb, full_sb, g.fmt_b, False, rows, cols, d)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("epi", ["bias", "bias_gelu_aux"])
+def test_block_gemm_forward_epilogues_vs_oracle(mode, epi):
+    """Bias and GELU-aux epilogues on recipe data (1-D x 2-D) against the oracle's epilogue of the blockwise
+    product: D (through GELU where it applies) and aux within the GEMM bound."""
+    M, N, K = 400, 528, 2176
+    qa, sa, qb, sb = recipe_operands(M, N, K, True, seed=91)
+    bias = workloads.normal_bf16(91, 5, (N,), 0.5)
+    d, aux = run(mode, qa, sa, "e4m3", qb, sb, "e4m3", True, epi, bias, torch.bfloat16)
+    check_recipe(mode, qa, sa, "e4m3", qb, sb, "e4m3", True, np.arange(M), np.arange(N), d, bias, epi)
+    if epi == "bias_gelu_aux":
+        # aux is the bf16 pre-activation: the bias epilogue's D for the same inputs, bit for bit
+        d_bias, _ = run(mode, qa, sa, "e4m3", qb, sb, "e4m3", True, "bias", bias, torch.bfloat16)
+        assert torch.equal(aux, d_bias)
