@@ -87,8 +87,15 @@ def _check(fn: str, status: int) -> None:
 
 
 def _ptr(t):
+    """Device address of a tensor argument.  Every pointer of the C ABI is a device pointer into a dense
+    row-major buffer, so host tensors and non-contiguous views are refused here (the library cannot tell
+    them apart from valid arguments)."""
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError(f"expected a GPU tensor, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor (row-major, no strides)")
     return t.data_ptr()
 
 

@@ -304,3 +304,25 @@ def test_import_fails_loudly_without_library(tmp_path):
     r = subprocess.run([sys.executable, "-c", "import mxfp8_mixed_precision_amd"], cwd=tmp_path,
                        capture_output=True, text=True)
     assert r.returncode != 0 and "libtemx.so is missing" in r.stderr
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    # every pointer of the ABI is a device pointer into a dense buffer: the binding checks before calling
+    import torch
+    x = torch.zeros((64, 64), dtype=torch.int16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        te.te_mxfp8_quantize(x, "e4m3", "row", x, x)
+
+    class FakeStrided:
+        is_cuda = True
+        device = "cuda:0"
+
+        def is_contiguous(self):
+            return False
+
+        def data_ptr(self):
+            raise AssertionError("must not be reached")
+
+    with pytest.raises(ValueError, match="contiguous"):
+        te._ptr(FakeStrided())
+    assert te._ptr(None) is None
