@@ -197,17 +197,21 @@ __global__ __launch_bounds__(kAmaxThreads) void delayed_update_kernel(const uint
                                                                       int len, int most_recent, int margin,
                                                                       float* __restrict__ scale,
                                                                       float* __restrict__ q_scale_inv) {
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < nparts; i += kAmaxThreads) m = max(m, partial[i]);
-  m = block_max(m);
-  const float amax = bf16_bits_to_float(m);
-  // shift: read every entry, wait, then write one place further
+  // every global read first (history entries, the old scale, the partial maxima): one memory
+  // round trip instead of three dependent ones
   float held[kMaxHistory / kAmaxThreads];
 #pragma unroll
   for (int k = 0; k < kMaxHistory / kAmaxThreads; ++k) {
     const int i = threadIdx.x + k * kAmaxThreads;
     held[k] = i < len ? history[i] : 0.0f;
   }
+  const float s_old = threadIdx.x == 0 ? *scale : 0.0f;
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += kAmaxThreads) m = max(m, partial[i]);
+  m = block_max(m);
+  const float amax = bf16_bits_to_float(m);
+  // every wave has read block_max's result (its LDS is reused below) and every history entry
+  // before any shifted write
   __syncthreads();
   uint32_t r = 0;  // max of the new history, over non-negative float bit patterns
 #pragma unroll
@@ -224,7 +228,6 @@ __global__ __launch_bounds__(kAmaxThreads) void delayed_update_kernel(const uint
   // over bit patterns (all entries are >= 0): a NaN sorts above inf and, like the
   // plain maximum, makes the result non-finite, so the scale is kept
   const float red = most_recent ? amax : __uint_as_float(max(__float_as_uint(amax), r));
-  const float s_old = *scale;
   *q_scale_inv = (float)(1.0 / (double)s_old);  // the inverse of the scale the cast used
   if (red > 0.0f && red <= FLT_MAX) {
     // correctly rounded fp32 quotient (see amax_final_kernel), then an exact power-of-two division
