@@ -39,11 +39,12 @@ PEAK_FP8_TFLOPS = 5000.0      # dense FP8 / MXFP8 MFMA, MI355X
 PEAK_HBM_GBS = 8000.0         # HBM3E, MI355X
 METRIC = "MXFP8 GEMM TFLOP/s + % of MI355X FP8 MFMA peak; quantize GB/s % of HBM"
 ROTATE = 4                     # copies of each bandwidth-bound input / output
-# kernels each kind of op launches, in order (names as the profiler reports them)
+# kernels each kind of op launches, in order (names as the profiler reports
+# them; "a|b": the library picks one of the two by size)
 KERNELS = {"quantize_row": ["quantize_rowwise_kernel"], "quantize_col": ["quantize_colwise_kernel"],
            "gemm": ["mx_gemm_kernel"], "grouped": ["mx_grouped_gemm_kernel"],
            "cast": ["amax_partial_kernel", "amax_final_kernel", "cast_kernel"],
-           "quantize_bgrad": ["quantize_colwise_kernel", "bgrad_final_kernel"],
+           "quantize_bgrad": ["quantize_both128_kernel|quantize_colwise_kernel", "bgrad_final_kernel"],
            "cast_delayed": ["cast_amax_kernel", "delayed_update_kernel"],
            "quantize_block1d": ["block_quantize_1d_kernel"], "quantize_block2d": ["block_quantize_2d_kernel"],
            "gemm_block_e8m0": ["mx_gemm_kernel"], "gemm_block_fp32": ["mx_gemm_kernel"]}
@@ -452,7 +453,7 @@ def _per_op(dispatches, record):
     for op in order:
         for kern in op["kernels"]:
             name, v = ours[i]
-            if kern not in name:
+            if not any(k in name for k in kern.split("|")):
                 raise SystemExit(f"dispatch {i}: expected {kern}, found {name[:80]}")
             totals[op["label"]] += v
             i += 1

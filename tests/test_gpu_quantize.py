@@ -189,13 +189,14 @@ def test_quantize_is_deterministic():
 
 def bgrad_bound(bits, bgrad_dtype):
     """|got - ref| allowed for the column sums: fp32 accumulation along a path
-    of at most 32 per-lane additions (4 rows x 8 blocks), 3 butterfly steps, 1
-    across row groups and 1 per 256-row tile, i.e. gamma_d * sum |x| with
-    d + 1 terms; bf16 output adds its rounding (2^-8 relative)."""
+    of at most 64 per-lane additions (8 rows x 8 blocks in the 128-column
+    kernel, 4 x 8 in the colwise kernel), at most 3 butterfly steps (2 and 3),
+    1 across row groups and 1 per 256-row tile, i.e. gamma_d * sum |x|
+    with d + 1 terms; bf16 output adds its rounding (2^-8 relative)."""
     ref = oracle.column_sums(bits)
     s = oracle.column_abs_sums(bits)
     tiles = -(-bits.shape[0] // 256)
-    d = 32 + 3 + 1 + tiles + 1
+    d = 64 + 3 + 1 + tiles + 1
     b32 = d * 2.0 ** -24 * s
     if bgrad_dtype == torch.bfloat16:
         return ref, 2.0 ** -8 * (np.abs(ref) + b32) + b32
@@ -271,12 +272,18 @@ def test_quantize_bgrad_deterministic():
 
 
 @pytest.mark.parametrize("bgrad_dtype", [torch.float32, torch.bfloat16])
-def test_quantize_bgrad_full_size_backward_dy(bgrad_dtype):
-    # the backward pass's output gradient dY [4096, 14336] (E5M2, N(0, 1e-3)):
-    # both copies equal the separate (oracle-pinned) kernels' outputs on the
-    # whole tensor, sampled rows / columns equal the oracle, bgrad within the bound
-    bits = workloads.hybrid_backward().gemms[0].a_src.make()
-    assert bits.shape == (4096, 14336)
+@pytest.mark.parametrize("shape", [(4096, 14336), (4128, 14368)])
+def test_quantize_bgrad_full_size_backward_dy(bgrad_dtype, shape):
+    # the backward pass's output gradient dY [4096, 14336] (E5M2, N(0, 1e-3)),
+    # and a shape whose last column and row tiles are partial (both run the
+    # 128-column kernel, two chunks per wave): both copies equal the separate
+    # (oracle-pinned) kernels' outputs on the whole tensor, sampled rows and
+    # columns (the last ones included) equal the oracle, bgrad within the bound
+    if shape == (4096, 14336):
+        bits = workloads.hybrid_backward().gemms[0].a_src.make()
+        assert bits.shape == shape
+    else:
+        bits = workloads.normal_bf16(81, 0, shape, 1e-3, 0.02)
     x = dev(bits)
     qr, sr, qc, sc, bg = te().mxfp8_quantize_bgrad(x, "e5m2", bgrad_dtype)
     q2r, s2r, _, _ = te().mxfp8_quantize(x, "e5m2", "row")
@@ -285,9 +292,12 @@ def test_quantize_bgrad_full_size_backward_dy(bgrad_dtype):
     assert torch.equal(qr, q2r) and torch.equal(sr, s2r), "fused rowwise copy differs from the rowwise kernel"
     assert torch.equal(qc, q2c) and torch.equal(sc, s2c), "fused colwise copy differs from the colwise kernel"
     f = oracle.E5M2
-    rows = sampled_rows(4096, k=16, seed=5)
+    rows = sampled_rows(shape[0], k=16, seed=5)
     oq, os_ = oracle.quantize_rowwise(bits[rows], f)
     assert np.array_equal(host(qr[rows]), oq) and np.array_equal(host(sr[rows]), os_)
+    cols = sampled_rows(shape[1], k=16, seed=6)
+    oq, os_ = oracle.quantize_colwise(np.ascontiguousarray(bits[:, cols]), f)
+    assert np.array_equal(host(qc[cols]), oq) and np.array_equal(host(sc[cols]), os_)
     ref, bound = bgrad_bound(bits, bgrad_dtype)
     assert np.all(np.abs(bgrad_host(bg) - ref) <= bound)
 
