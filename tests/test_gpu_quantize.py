@@ -302,6 +302,52 @@ def test_quantize_bgrad_full_size_backward_dy(bgrad_dtype, shape):
     assert np.all(np.abs(bgrad_host(bg) - ref) <= bound)
 
 
+def special_patch(kind, rng):
+    """A 32 x 32 bf16 patch: zeros, negative zeros, subnormals only, values
+    near the top of the bf16 range (either sign), or ones with one spike."""
+    if kind == 0:
+        return np.zeros((32, 32), np.uint16)
+    if kind == 1:
+        return np.full((32, 32), 0x8000, np.uint16)
+    if kind == 2:
+        return (np.arange(1024, dtype=np.uint16) % 127 + 1).reshape(32, 32)
+    if kind == 3:
+        sign = rng.integers(0, 2, (32, 32)).astype(np.uint16) << 15
+        return (0x7F00 | (np.arange(1024, dtype=np.uint16) & 0x3F)).reshape(32, 32) | sign
+    p = np.full((32, 32), 0x3F80, np.uint16)
+    p[rng.integers(0, 32), rng.integers(0, 32)] = 0x4700
+    return p
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_both_directions_special_blocks_large(fmt):
+    # a grid large enough for the 128-column fused kernel, with special 32 x 32
+    # patches at tile edges and in the partial last row and column tiles: the
+    # copies equal the separate kernels on the whole tensor and the oracle on
+    # the rows and columns through every patch
+    rows, cols = 4128, 14368
+    rng = np.random.default_rng(93)
+    bits = workloads.normal_bf16(92, 0, (rows, cols), 1.0, 0.0)
+    spots = [(0, 0), (96, 128), (128, 224), (512, 256), (2048, 8160), (3968, 14208), (4064, 14304), (4096, 14336),
+             (4096, 0), (0, 14336)]
+    for k, (r, c) in enumerate(spots):
+        bits[r:r + 32, c:c + 32] = special_patch(k % 5, rng)
+    x = dev(bits)
+    qr, sr, qc, sc = te().mxfp8_quantize(x, fmt, "both")
+    q2r, s2r, _, _ = te().mxfp8_quantize(x, fmt, "row")
+    _, _, q2c, s2c = te().mxfp8_quantize(x, fmt, "col")
+    torch.cuda.synchronize()
+    assert torch.equal(qr, q2r) and torch.equal(sr, s2r)
+    assert torch.equal(qc, q2c) and torch.equal(sc, s2c)
+    f = oracle.format_by_name(fmt)
+    rsel = np.array(sorted({r + d for r, _ in spots for d in (0, 13, 31)} | {rows - 1}))
+    oq, os_ = oracle.quantize_rowwise(bits[rsel], f)
+    assert np.array_equal(host(qr[rsel]), oq) and np.array_equal(host(sr[rsel]), os_)
+    csel = np.array(sorted({c + d for _, c in spots for d in (0, 17, 31)} | {cols - 1}))
+    oq, os_ = oracle.quantize_colwise(np.ascontiguousarray(bits[:, csel]), f)
+    assert np.array_equal(host(qc[csel]), oq) and np.array_equal(host(sc[csel]), os_)
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("shape", [(8192, 8192), (8288, 8224), (4096, 4096), (14336, 4096)])
 def test_both_directions_fused_equals_separate_full_size(fmt, shape):
