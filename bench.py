@@ -43,7 +43,7 @@ ROTATE = 4                     # copies of each bandwidth-bound input / output
 # them; "a|b": the library picks one of the two by size)
 KERNELS = {"quantize_row": ["quantize_rowwise_kernel"], "quantize_col": ["quantize_colwise_kernel"],
            "gemm": ["mx_gemm_kernel"], "grouped": ["mx_grouped_gemm_kernel"],
-           "cast": ["amax_partial_kernel", "amax_final_kernel", "cast_kernel"],
+           "cast": ["amax_partial_kernel", "cast_current_kernel"],
            "quantize_bgrad": ["quantize_both128_kernel|quantize_colwise_kernel", "bgrad_final_kernel"],
            "cast_delayed": ["cast_amax_kernel", "delayed_update_kernel"],
            "quantize_block1d": ["block_quantize_1d_kernel"], "quantize_block2d": ["block_quantize_2d_kernel"],

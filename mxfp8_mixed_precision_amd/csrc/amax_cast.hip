@@ -72,31 +72,30 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const uint16
   if (threadIdx.x == 0) partial[blockIdx.x] = m;
 }
 
-// Stage two: one workgroup reduces the partial maxima; with a format it
-// also writes scale and scale_inv.
-template <int FMT>  // 0 = amax only
+// scale = fl32(fmt_max / amax) (1 for amax 0, the largest finite float when
+// the quotient overflows).  A float32 quotient rounded once to float64 and
+// then to float32 equals the correctly rounded float32 quotient (53 >=
+// 2*24 + 2; Figueroa, "When is double rounding innocuous?", 1995), so this
+// and 1 / scale below are IEEE float32 divisions.
+template <int FMT>
+__device__ __forceinline__ float current_scale(float amax) {
+  float scale = 1.0f;
+  if (amax != 0.0f) {
+    scale = (float)((double)FmtTraits<FMT>::max_value / (double)amax);
+    if (!(scale <= FLT_MAX)) scale = FLT_MAX;
+  }
+  return scale;
+}
+
+// Stage two of the standalone amax: one workgroup reduces the partial
+// maxima.  (The current-scaling cast does this reduction inside its own
+// workgroups, below.)
 __global__ __launch_bounds__(kAmaxThreads) void amax_final_kernel(const uint32_t* __restrict__ partial, int nparts,
-                                                                  float* __restrict__ amax_out,
-                                                                  float* __restrict__ scale_out,
-                                                                  float* __restrict__ scale_inv_out) {
+                                                                  float* __restrict__ amax_out) {
   uint32_t m = 0;
   for (int i = threadIdx.x; i < nparts; i += kAmaxThreads) m = max(m, partial[i]);
   m = block_max(m);
-  if (threadIdx.x != 0) return;
-  const float amax = bf16_bits_to_float(m);
-  *amax_out = amax;
-  if constexpr (FMT != 0) {
-    // A float32 quotient rounded once to float64 and then to float32 equals the
-    // correctly rounded float32 quotient (53 >= 2*24 + 2; Figueroa, "When is
-    // double rounding innocuous?", 1995), so these are IEEE float32 divisions.
-    float scale = 1.0f;
-    if (amax != 0.0f) {
-      scale = (float)((double)FmtTraits<FMT>::max_value / (double)amax);
-      if (!(scale <= FLT_MAX)) scale = FLT_MAX;
-    }
-    *scale_out = scale;
-    *scale_inv_out = (float)(1.0 / (double)scale);
-  }
+  if (threadIdx.x == 0) *amax_out = bf16_bits_to_float(m);
 }
 
 // Cast: y = fl32(x * scale), clamped to the finite range, then the plain
@@ -121,24 +120,53 @@ __device__ __forceinline__ uint32_t cast4(uint32_t p0, uint32_t p1, float scale)
   return (uint32_t)r;
 }
 
+// Current-scaling cast with the final reduction folded in: every workgroup
+// reduces the partial maxima itself (a few KB from L2, issued after its own
+// loads of x so the two overlap), derives the scale, and casts 4 chunks per
+// thread; workgroup 0 writes amax, scale and scale_inv, and its thread 0 the
+// n % 8 tail.  One launch fewer than final reduction + cast.
+constexpr int kCastThreads = 256;
+constexpr int kCastUnroll = 4;
+
 template <int FMT>
-__global__ __launch_bounds__(256) void cast_kernel(const uint16_t* __restrict__ x, int64_t n,
-                                                   const float* __restrict__ scale_ptr, uint8_t* __restrict__ q) {
-  const float scale = *scale_ptr;
+__global__ __launch_bounds__(kCastThreads) void cast_current_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                   const uint32_t* __restrict__ partial, int nparts,
+                                                                   uint8_t* __restrict__ q,
+                                                                   float* __restrict__ amax_out,
+                                                                   float* __restrict__ scale_out,
+                                                                   float* __restrict__ scale_inv_out) {
+  static_assert(kCastThreads == kAmaxThreads, "block_max reduces over kAmaxThreads lanes");
   const int64_t nchunks = n / 8;
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c < nchunks) {
-    const uint4 v = load_nt16(reinterpret_cast<const uint4*>(x) + c);
-    uint2 r;
-    r.x = cast4<FMT>(v.x, v.y, scale);
-    r.y = cast4<FMT>(v.z, v.w, scale);
-    reinterpret_cast<uint2*>(q)[c] = r;
-  } else if (c == nchunks) {
-    // tail of n % 8 elements
-    for (int64_t i = nchunks * 8; i < n; ++i) {
-      const uint32_t h = x[i];
-      q[i] = (uint8_t)(cast4<FMT>(h, 0, scale) & 0xFFu);
+  const int64_t base = (int64_t)blockIdx.x * (kCastThreads * kCastUnroll) + threadIdx.x;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint4 v[kCastUnroll];
+#pragma unroll
+  for (int u = 0; u < kCastUnroll; ++u) {
+    const int64_t c = base + (int64_t)u * kCastThreads;
+    v[u] = c < nchunks ? load_nt16(xv + c) : make_uint4(0, 0, 0, 0);
+  }
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += kCastThreads) m = max(m, partial[i]);
+  m = block_max(m);
+  const float amax = bf16_bits_to_float(m);
+  const float scale = current_scale<FMT>(amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *amax_out = amax;
+    *scale_out = scale;
+    *scale_inv_out = (float)(1.0 / (double)scale);
+  }
+#pragma unroll
+  for (int u = 0; u < kCastUnroll; ++u) {
+    const int64_t c = base + (int64_t)u * kCastThreads;
+    if (c < nchunks) {
+      uint2 r;
+      r.x = cast4<FMT>(v[u].x, v[u].y, scale);
+      r.y = cast4<FMT>(v[u].z, v[u].w, scale);
+      store_nt8(reinterpret_cast<uint2*>(q) + c, r);
     }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    for (int64_t i = nchunks * 8; i < n; ++i) q[i] = (uint8_t)(cast4<FMT>(x[i], 0, scale) & 0xFFu);
   }
 }
 
@@ -230,7 +258,7 @@ __global__ __launch_bounds__(kAmaxThreads) void delayed_update_kernel(const uint
   const float red = most_recent ? amax : __uint_as_float(max(__float_as_uint(amax), r));
   *q_scale_inv = (float)(1.0 / (double)s_old);  // the inverse of the scale the cast used
   if (red > 0.0f && red <= FLT_MAX) {
-    // correctly rounded fp32 quotient (see amax_final_kernel), then an exact power-of-two division
+    // correctly rounded fp32 quotient (see current_scale), then an exact power-of-two division
     float s = (float)((double)FmtTraits<FMT>::max_value / (double)red);
     if (!(s <= FLT_MAX)) s = FLT_MAX;
     *scale = ldexpf(s, -margin);
@@ -263,8 +291,7 @@ extern "C" te_status te_amax_reduce(const uint16_t* x, int64_t n, float* amax_ou
   TE_REQUIRE(workspace_bytes >= (size_t)blocks * sizeof(uint32_t), TE_ERR_WORKSPACE);
   uint32_t* partial = static_cast<uint32_t*>(workspace);
   if (launch_amax(x, n, partial, blocks, stream) != TE_OK) return TE_ERR_HIP;
-  hipLaunchKernelGGL(amax_final_kernel<0>, dim3(1), dim3(kAmaxThreads), 0, stream, partial, (int)blocks, amax_out,
-                     nullptr, nullptr);
+  hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(kAmaxThreads), 0, stream, partial, (int)blocks, amax_out);
   return launch_status();
 }
 
@@ -283,19 +310,15 @@ extern "C" te_status te_fp8_cast_current_scaling(const uint16_t* x, int64_t n, t
   TE_REQUIRE(n / 8 / 256 < (int64_t)1 << 31, TE_ERR_SHAPE);
   uint32_t* partial = static_cast<uint32_t*>(workspace);
   if (launch_amax(x, n, partial, blocks, stream) != TE_OK) return TE_ERR_HIP;
+  // at least one workgroup, which writes amax, scale and scale_inv (n = 0 included)
+  int64_t grid = (n / 8 + kCastThreads * kCastUnroll - 1) / (kCastThreads * kCastUnroll);
+  if (grid < 1) grid = 1;
   if (fmt == TE_E4M3)
-    hipLaunchKernelGGL(amax_final_kernel<TE_E4M3>, dim3(1), dim3(kAmaxThreads), 0, stream, partial, (int)blocks,
-                       amax_out, scale_out, scale_inv_out);
+    hipLaunchKernelGGL(cast_current_kernel<TE_E4M3>, dim3((unsigned)grid), dim3(kCastThreads), 0, stream, x, n,
+                       partial, (int)blocks, q_out, amax_out, scale_out, scale_inv_out);
   else
-    hipLaunchKernelGGL(amax_final_kernel<TE_E5M2>, dim3(1), dim3(kAmaxThreads), 0, stream, partial, (int)blocks,
-                       amax_out, scale_out, scale_inv_out);
-  if (launch_status() != TE_OK) return TE_ERR_HIP;
-  if (n == 0) return TE_OK;
-  const int64_t grid = (n / 8 + 1 + 255) / 256;  // + 1 covers the tail thread
-  if (fmt == TE_E4M3)
-    hipLaunchKernelGGL(cast_kernel<TE_E4M3>, dim3((unsigned)grid), dim3(256), 0, stream, x, n, scale_out, q_out);
-  else
-    hipLaunchKernelGGL(cast_kernel<TE_E5M2>, dim3((unsigned)grid), dim3(256), 0, stream, x, n, scale_out, q_out);
+    hipLaunchKernelGGL(cast_current_kernel<TE_E5M2>, dim3((unsigned)grid), dim3(kCastThreads), 0, stream, x, n,
+                       partial, (int)blocks, q_out, amax_out, scale_out, scale_inv_out);
   return launch_status();
 }
 
