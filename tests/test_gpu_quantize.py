@@ -166,6 +166,25 @@ def test_current_scaling_cast(fmt, n):
     assert np.array_equal(host(q), oq)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("where", ["tail", "last_chunk", "first"])
+def test_current_scaling_cast_max_at_the_edges(fmt, where):
+    # 2^24 + 7 elements (1024 partial maxima, a 7-element tail): the tensor's
+    # largest magnitude sits in the tail, in the last full 16-byte chunk, or
+    # first; every workgroup of the cast must derive the same scale from it
+    n = (1 << 24) + 7
+    bits = workloads.normal_bf16(4, 3, (n,), 1.0, 0.0)
+    idx = {"tail": n - 2, "last_chunk": (n // 8) * 8 - 3, "first": 0}[where]
+    bits[idx] = 0xC4FA  # -2000.0, far above the N(0, 1) values
+    f = oracle.format_by_name(fmt)
+    q, a, s, si = te().fp8_cast_current_scaling(dev(bits), fmt)
+    torch.cuda.synchronize()
+    oq, oa, os_, osi = oracle.cast_current_scaling(bits, f)
+    assert oa == 2000.0
+    assert host(a)[0] == oa and host(s)[0] == os_ and host(si)[0] == osi
+    assert np.array_equal(host(q), oq)
+
+
 def test_current_scaling_zero_and_subnormal_tensors():
     for bits in (np.zeros(64, np.uint16), np.array([0x8000] * 63 + [0x0001], np.uint16)):
         q, a, s, si = te().fp8_cast_current_scaling(dev(bits), "e4m3")
