@@ -54,6 +54,26 @@ def test_gemm_exact_integer_bitexact(fa, fb, M, N, K):
     assert np.array_equal(host(d).astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3")])
+def test_big_tile_exact_integer_partial_scale_block(fa, fb):
+    # enough 256 x 256 tiles (24 x 25) for the big tile, whose scales travel in
+    # blocks of 4 K steps: K = 1152 is 9 steps, so the last block holds one
+    # step; a 48-column tail.  Exact-integer operands: every fp32 output is
+    # exact, so sampled rows (every tile boundary, the last row) must match
+    # the oracle bit for bit.
+    M, N, K = 6144, 6144 + 48, 1152
+    rng = np.random.default_rng(61)
+    qa, qb = exact_codes(rng, (M, K), fa), exact_codes(rng, (N, K), fb)
+    sa = rng.integers(125, 130, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(125, 130, size=(N, K // 32)).astype(np.uint8)
+    d, _ = te().mxfp8_gemm(dev(qa), dev(sa), fa, dev(qb), dev(sb), fb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, M - 1} | {256 * t + o for t in range(M // 256) for o in (0, 255)}
+                           | set(rng.choice(M, 16, replace=False).tolist())))
+    ref, _, _ = oracle.mx_gemm(qa[rows], sa[rows], oracle.format_by_name(fa), qb, sb, oracle.format_by_name(fb))
+    assert np.array_equal(host(d[rows]).astype(np.float64), ref)
+
+
 def test_gemm_k_zero_gives_epilogue_of_zero():
     M, N = 64, 48
     bias = workloads.normal_bf16(6, 1, (N,), 1.0)
@@ -288,6 +308,13 @@ def test_grouped_single_group_matches_dense_rows():
 
 def test_grouped_all_empty_but_one():
     check_grouped([0, 0, 0, 33, 0], N=64, K=128, epi="bias_gelu_aux", seed=33, full_cols=True)
+
+
+def test_grouped_big_tile_partial_scale_block():
+    # 32 ragged experts over 16384 rows and N = 2048 give enough 256 x 256
+    # tiles for the big tile; K = 1152 leaves a one-step last scale block
+    counts = workloads.moe_counts(16384, 32, seed=(7, 1))
+    check_grouped(counts.tolist(), N=2048, K=1152, epi="bias", seed=34, rows_per_expert=6)
 
 
 def test_moe_grouped_full_size_sampled():
