@@ -54,8 +54,8 @@ te_status launch_block_modes(const uint8_t* a, const float* sa, const uint8_t* b
   if (t == Tile::Small)
     return b2d ? launch_fs2<Small, SM2>(p, fa, fb, epi, d_dtype, grid, stream)
                : launch_fs2<Small, SM1>(p, fa, fb, epi, d_dtype, grid, stream);
-  return b2d ? launch_fs2<BigBlock, SM2>(p, fa, fb, epi, d_dtype, grid, stream)
-             : launch_fs2<BigBlock, SM1>(p, fa, fb, epi, d_dtype, grid, stream);
+  return b2d ? launch_fs2<Big, SM2>(p, fa, fb, epi, d_dtype, grid, stream)
+             : launch_fs2<Big, SM1>(p, fa, fb, epi, d_dtype, grid, stream);
 }
 
 }  // namespace

@@ -77,9 +77,9 @@ constexpr bool b_2d(int sm) { return sm == SM_FS2 || sm == SM_BE2; }
 //          ~70-90 clocks whatever its size, so one 16-byte scale copy per
 //          row and 4 steps replaces four 4-byte ones (measured on MI355X,
 //          bit-identical results: 8192^3 460 -> 444 us, 4096 x 4096 x 14336
-//          199 -> 191 us, the 32-expert grouped GEMM 170 -> 160 us).
-//   BigBlock: the big tile with each stage's scales in the stage (132 KB),
-//          for the blockwise modes, whose FP32 scale reads index the stage.
+//          199 -> 191 us, the 32-expert grouped GEMM 170 -> 160 us).  The
+//          blockwise modes' FP32 scales ([rows, K/128], 4 bytes per row and
+//          step) travel in the same 16-byte blocks.
 //   Small: 128 x 128, 4 waves of 64 x 64 (64 accumulators), all four copy;
 //          66 KB of LDS, two workgroups per CU.  For grids the big tile
 //          cannot fill (few or ragged row tiles).
@@ -118,7 +118,6 @@ struct Cfg {
   static_assert(NCOPY % 2 == 0 && (BM / 8) % NCOPY == 0 && (BM / 64) <= NCOPY, "copy slices per copier wave");
 };
 using Big = Cfg<256, 256, 4, 2, 4, 2, 4>;
-using BigBlock = Cfg<256, 256, 4, 2, 4>;  // the big tile with per-stage scale copies (blockwise FP32 scales)
 using Small = Cfg<128, 128, 2, 2, 4>;
 using SmallDeep = Cfg<128, 128, 2, 2, 4, 4>;
 constexpr int kGroupM = 4;      // row-tile band of the raster order
@@ -255,7 +254,9 @@ __device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, con
 // SB = 4: the 16 scale bytes of steps 4 blk .. 4 blk + 3 of each tile row
 // (A rows 0 .. BM-1, then B rows) into scale buffer sbuf; 64-row slice q of
 // the 2 BM / 64 is copied by copier q % NCOPY, lane l landing at row 64 s + l.
-template <class C>
+// With 2-D B blocks (b_2d) a B slice's 64 rows all take their 128-row block
+// row's scales.
+template <class C, int SM>
 __device__ __forceinline__ void load_scale_block(uint32_t sbuf, const Operand& A, const Operand& B,
                                                  const CopyOffsets& off, int64_t K, int blk, int c) {
 #pragma unroll
@@ -263,8 +264,13 @@ __device__ __forceinline__ void load_scale_block(uint32_t sbuf, const Operand& A
     const int q = c + C::NCOPY * i;
     const int s64 = q % (C::BM / 64);
     const int soff = (int)(64 * s64 * (K / 32)) + 16 * blk;
-    if (q < C::BM / 64) lds_dma16(A.scale, sbuf + s64 * 1024, off.scale, soff);
-    else lds_dma16(B.scale, sbuf + C::BM * 16 + s64 * 1024, off.scale, soff);
+    if (q < C::BM / 64) {
+      lds_dma16(A.scale, sbuf + s64 * 1024, off.scale, soff);
+    } else if constexpr (b_2d(SM)) {
+      lds_dma16(B.scale, sbuf + C::BM * 16 + s64 * 1024, 0, (int)((s64 >> 1) * (K / 32)) + 16 * blk);
+    } else {
+      lds_dma16(B.scale, sbuf + C::BM * 16 + s64 * 1024, off.scale, soff);
+    }
   }
 }
 
@@ -297,7 +303,11 @@ __device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) { 
   o.a_data2 = o.a_data ^ 64;
   o.b_data = LY::kOffBData + wn * LY::WTN * BK + lane_off;
   o.b_data2 = o.b_data ^ 64;
-  if constexpr (fp32_scales(SM)) {
+  if constexpr (LY::SB == 4 && SM != SM_MX) {  // blockwise scales in 4-step blocks: 16 bytes per row
+    static_assert(128 % LY::WTN == 0, "a wave's columns stay inside one 128-row block of B");
+    o.a_scale = (wm * LY::WTM + r) * 16;
+    o.b_scale = LY::BM * 16 + (wn * LY::WTN + ((SM == SM_FS1) ? 4 * g : (SM == SM_BE1) ? r : 0)) * 16;
+  } else if constexpr (fp32_scales(SM)) {
     static_assert(128 % LY::WTN == 0, "a wave's columns stay inside one 128-row block of B");
     o.a_scale = LY::kOffAScale + (wm * LY::WTM + r) * 4;
     o.b_scale = LY::kOffBScale + (wn * LY::WTN + (SM == SM_FS1 ? 4 * g : 0)) * 4;
@@ -305,7 +315,7 @@ __device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) { 
     static_assert(128 % LY::WTN == 0, "a wave's columns stay inside one 128-row block of B");
     o.a_scale = LY::kOffAScale + (wm * LY::WTM + r) * 4;
     o.b_scale = LY::kOffBScale + (wn * LY::WTN + (SM == SM_BE1 ? r : 0)) * 4;
-  } else if constexpr (LY::SB == 4) {  // offsets inside a scale buffer; + 4 (kt % 4) per step
+  } else if constexpr (LY::SB == 4) {  // MXFP8: offsets inside a scale buffer; + 4 (kt % 4) per step
     o.a_scale = (wm * LY::WTM + r) * 16 + g;
     o.b_scale = LY::BM * 16 + (wn * LY::WTN + r) * 16 + g;
   } else {
@@ -336,7 +346,8 @@ __device__ __forceinline__ Frag read_frag(const uint8_t* stage, int data_off, in
   Frag f;
   f.v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   if constexpr (SK == kScaleUnit) f.s = 127;
-  else if constexpr (SK == kScaleCast) f.s = (int)e8m0_at_least(*reinterpret_cast<const float*>(stage + scale_off + j * 64));
+  else if constexpr (SK == kScaleCast)
+    f.s = (int)e8m0_at_least(*reinterpret_cast<const float*>((SSTRIDE == 64 ? stage : sstage) + scale_off + j * SSTRIDE));
   else f.s = (int)(SSTRIDE == 64 ? stage : sstage)[scale_off + j * SSTRIDE];
   return f;
 }
@@ -346,7 +357,7 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN
                                         const uint8_t* sstage = nullptr) {
   constexpr int SK = SM == SM_MX ? kScaleByte : (SM == SM_BE1 || SM == SM_BE2) ? kScaleCast : kScaleUnit;
   constexpr int SST = LY::SB == 4 ? 256 : 64;  // scale bytes between fragments (16 rows)
-  static_assert(LY::SB == 1 || SM == SM_MX || SM == SM_PT, "scale blocks: MXFP8 (or no scales)");
+  const uint8_t* sbase = LY::SB == 4 ? sstage : stage;
   Frag bop[LY::FRM];
 #pragma unroll
   for (int j = 0; j < LY::FRM; ++j) bop[j] = read_frag<SK, SST>(stage, ro.a_data, ro.a_data2, ro.a_scale, j, sstage);
@@ -355,10 +366,10 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN
     // acc += (sa[m] * sb[n]) * P with one rounding (fma)
     float sa[LY::FRM];
 #pragma unroll
-    for (int j = 0; j < LY::FRM; ++j) sa[j] = *reinterpret_cast<const float*>(stage + ro.a_scale + j * 64);
+    for (int j = 0; j < LY::FRM; ++j) sa[j] = *reinterpret_cast<const float*>(sbase + ro.a_scale + j * SST);
     float sab[LY::FRM];
     if constexpr (SM == SM_FS2) {
-      const float sb = *reinterpret_cast<const float*>(stage + ro.b_scale);
+      const float sb = *reinterpret_cast<const float*>(sbase + ro.b_scale);
 #pragma unroll
       for (int j = 0; j < LY::FRM; ++j) sab[j] = sa[j] * sb;
     }
@@ -366,7 +377,12 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN
     for (int i = 0; i < LY::FRN; ++i) {
       const Frag aop = read_frag<kScaleUnit>(stage, ro.b_data, ro.b_data2, 0, i);
       float4 sb4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (SM == SM_FS1) sb4 = *reinterpret_cast<const float4*>(stage + ro.b_scale + i * 64);
+      if constexpr (SM == SM_FS1 && LY::SB == 1) {
+        sb4 = *reinterpret_cast<const float4*>(stage + ro.b_scale + i * 64);
+      } else if constexpr (SM == SM_FS1) {  // the four rows' floats are 16 bytes apart
+        const float* f = reinterpret_cast<const float*>(sbase + ro.b_scale + i * SST);
+        sb4 = make_float4(f[0], f[4], f[8], f[12]);
+      }
 #pragma unroll
       for (int j = 0; j < LY::FRM; ++j) {
         const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop.v, bop[j].v, v4f{0.f, 0.f, 0.f, 0.f},
@@ -385,7 +401,7 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN
     return;
   }
   int sb_code = 0;  // SM_BE2: one E8M0 code for all of the wave's columns
-  if constexpr (SM == SM_BE2) sb_code = (int)e8m0_at_least(*reinterpret_cast<const float*>(stage + ro.b_scale));
+  if constexpr (SM == SM_BE2) sb_code = (int)e8m0_at_least(*reinterpret_cast<const float*>(sbase + ro.b_scale));
 #pragma unroll
   for (int i = 0; i < LY::FRN; ++i) {
     Frag aop;
@@ -440,13 +456,13 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
   constexpr int S = LY::NSTAGE;
   static_assert(S >= 2 && S <= 4, "the waits below cover up to two later stages in flight");
   // copies per copier wave and stage (the same for every copier)
-  constexpr int kPerStage = 2 * (LY::BM / 8 / LY::NCOPY) + (SM == SM_PT ? 0 : LY::kScaleSlicesPerCopier);
-  constexpr bool kBlk = LY::SB == 4 && SM == SM_MX;
+  constexpr int kPerStage = 2 * (LY::BM / 8 / LY::NCOPY) + (SM == SM_PT || LY::SB == 4 ? 0 : LY::kScaleSlicesPerCopier);
+  constexpr bool kBlk = LY::SB == 4 && SM != SM_PT;
   if (copier) {
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
       if (s < kt_n) load_stage<LY, SM>(lds_addr + s * LY::kStage, A, B, off, K, s, c);
-    if constexpr (kBlk) load_scale_block<LY>(lds_addr + LY::kOffScaleBuf, A, B, off, K, 0, c);
+    if constexpr (kBlk) load_scale_block<LY, SM>(lds_addr + LY::kOffScaleBuf, A, B, off, K, 0, c);
   }
   for (int kt = 0; kt < kt_n; ++kt) {
     // stage kt has landed once at most `ahead` later stages' copies are outstanding
@@ -461,7 +477,7 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
       // block kt / 4 + 1 goes into the buffer block kt / 4 - 1 used, whose last reads precede this barrier
       const int nb = (kt >> 2) + 1;
       if (copier && (kt & 3) == 0 && 4 * nb < kt_n)
-        load_scale_block<LY>(lds_addr + LY::kOffScaleBuf + (nb & 1) * LY::kScaleBuf, A, B, off, K, nb, c);
+        load_scale_block<LY, SM>(lds_addr + LY::kOffScaleBuf + (nb & 1) * LY::kScaleBuf, A, B, off, K, nb, c);
       compute<LY, FA, FB, SM>(lds + (kt % S) * LY::kStage, acc, ro,
                               lds + LY::kOffScaleBuf + ((kt >> 2) & 1) * LY::kScaleBuf + 4 * (kt & 3));
     } else {
