@@ -509,7 +509,7 @@ def traffic_from(fetch_dir, write_dir):
           "same run:", ""]
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         md.append(f"- {c}: {out[c][1]:.1f} KiB per copy -> factor {out[c][2]:.4f}")
-    md += ["", "Commands (from the repository root, GPU box):", ""]
+    md += ["", "Commands (from the repository root):", ""]
     md += ["    " + c for c in data["workloads"][wl]["commands"]]
     md += ["", "| op | fetch MB | write MB | total MB | algorithmic MB | total / algorithmic |",
            "|---|---:|---:|---:|---:|---:|"]
@@ -534,7 +534,7 @@ def stats_from(stats_dir, command):
     with open(os.path.join(stats_dir, "ops.json")) as fh:
         record = json.load(fh)
     wl = record["workload"]
-    md = [f"# Kernel time, workload {wl}", "", "Command (from the repository root, GPU box):", "",
+    md = [f"# Kernel time, workload {wl}", "", "Command (from the repository root):", "",
           "    " + command, "", "rocprofv3 kernel statistics:", "",
           "| kernel | calls | avg us | min us | max us | total % |", "|---|---:|---:|---:|---:|---:|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
@@ -577,7 +577,7 @@ def mfma_from(pmc_dir, command):
     xcc, simds = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
     gemm_flops = sorted({o["flops"] for o in record["ops"] if o.get("flops")})
     wl = record["workload"]
-    md = [f"# MFMA utilisation, workload {wl}", "", "Command (from the repository root, GPU box):", "",
+    md = [f"# MFMA utilisation, workload {wl}", "", "Command (from the repository root):", "",
           "    " + command, "",
           "Per dispatch of each kernel that issues FP8 MFMAs (medians over the run's dispatches):", "",
           "- MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_F8 x 512 (the counter counts multiply and add operations / 512);",
