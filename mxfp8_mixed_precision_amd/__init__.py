@@ -109,6 +109,69 @@ def _fmt(f) -> int:
     return FORMATS[f] if isinstance(f, str) else int(f)
 
 
+# Argument checks of the wrappers.  The C ABI sees only addresses and sizes, so
+# a tensor of the wrong shape or element type would be read or written past
+# its end there; every wrapper checks its tensors against the sizes it passes
+# before calling the library.
+_BYTE_DTYPES = {torch.uint8, torch.int8} | {getattr(torch, n) for n in
+                                           ("float8_e4m3fn", "float8_e5m2", "float8_e8m0fnu") if hasattr(torch, n)}
+_BF16_DTYPES = {torch.bfloat16, torch.int16} | ({torch.uint16} if hasattr(torch, "uint16") else set())
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_tensor(t, name: str, shape, dtypes, kind: str, optional: bool = False) -> None:
+    """t must have exactly `shape` and a dtype in `dtypes` (None is accepted only when optional)."""
+    if t is None:
+        _require(optional, f"{name} is required")
+        return
+    _require(t.dtype in dtypes, f"{name}: expected {kind}, got {t.dtype}")
+    _require(tuple(t.shape) == tuple(int(v) for v in shape),
+             f"{name}: expected shape {tuple(int(v) for v in shape)}, got {tuple(t.shape)}")
+
+
+def _codes(t, name, shape, optional=False):
+    _check_tensor(t, name, shape, _BYTE_DTYPES, "1-byte codes (uint8)", optional)
+
+
+def _bf16(t, name, shape, optional=False):
+    _check_tensor(t, name, shape, _BF16_DTYPES, "bf16 (or its int16 bits)", optional)
+
+
+def _f32(t, name, shape, optional=False):
+    _check_tensor(t, name, shape, {torch.float32}, "float32", optional)
+
+
+def _scalar_f32(t, name):
+    _require(t is not None and t.dtype == torch.float32 and t.numel() >= 1, f"{name}: expected a float32 scalar")
+
+
+def _gemm_out(d, name, M, N, epi):
+    """D of the bf16/fp32-output GEMMs: [M, N] bf16 or float32; "accumulate" needs float32."""
+    _require(d is not None and d.dtype in (torch.bfloat16, torch.float32),
+             f"{name}: expected bfloat16 or float32, got {None if d is None else d.dtype}")
+    _require(epi != TE_EPI_ACCUMULATE or d.dtype == torch.float32, f"{name}: the accumulate epilogue needs float32")
+    _require(tuple(d.shape) == (M, N), f"{name}: expected shape {(M, N)}, got {tuple(d.shape)}")
+    return TE_BF16 if d.dtype == torch.bfloat16 else TE_FP32
+
+
+def _epi_tensors(bias, bias_shape, aux, M, N):
+    """bias (bf16, bias_shape) with the bias epilogues; aux (bf16 [M, N]) with GELU aux and dgelu."""
+    _bf16(bias, "bias", bias_shape, optional=True)
+    _bf16(aux, "aux", (M, N), optional=True)
+
+
+def _epilogue(epilogue) -> int:
+    return EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
+
+
+def _ws_bytes(workspace) -> int:
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
 # ---------------------------------------------------------------- entry points
 
 def te_amax_workspace_size(n: int) -> int:
@@ -116,11 +179,17 @@ def te_amax_workspace_size(n: int) -> int:
 
 
 def te_amax_reduce(x, amax_out, workspace, stream=None) -> None:
+    _bf16(x, "x", tuple(x.shape))
+    _scalar_f32(amax_out, "amax_out")
     _check("te_amax_reduce", _lib.te_amax_reduce(_ptr(x), x.numel(), _ptr(amax_out), _ptr(workspace),
                                                  workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def te_fp8_cast_current_scaling(x, fmt, q_out, amax_out, scale_out, scale_inv_out, workspace, stream=None) -> None:
+    _bf16(x, "x", tuple(x.shape))
+    _codes(q_out, "q_out", tuple(x.shape))
+    for t, n in ((amax_out, "amax_out"), (scale_out, "scale_out"), (scale_inv_out, "scale_inv_out")):
+        _scalar_f32(t, n)
     _check("te_fp8_cast_current_scaling", _lib.te_fp8_cast_current_scaling(
         _ptr(x), x.numel(), _fmt(fmt), _ptr(q_out), _ptr(amax_out), _ptr(scale_out), _ptr(scale_inv_out),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -129,6 +198,12 @@ def te_fp8_cast_current_scaling(x, fmt, q_out, amax_out, scale_out, scale_inv_ou
 def te_fp8_cast_delayed_scaling(x, fmt, q_out, q_scale_inv_out, scale, amax_history, workspace, algo="max",
                                 margin=0, stream=None) -> None:
     a = AMAX_ALGOS[algo] if isinstance(algo, str) else int(algo)
+    _bf16(x, "x", tuple(x.shape))
+    _codes(q_out, "q_out", tuple(x.shape))
+    _scalar_f32(q_scale_inv_out, "q_scale_inv_out")
+    _scalar_f32(scale, "scale")
+    _require(amax_history is not None and amax_history.dtype == torch.float32 and amax_history.dim() == 1,
+             "amax_history: expected a 1-D float32 tensor")
     _check("te_fp8_cast_delayed_scaling", _lib.te_fp8_cast_delayed_scaling(
         _ptr(x), x.numel(), _fmt(fmt), _ptr(q_out), _ptr(q_scale_inv_out), _ptr(scale), _ptr(amax_history),
         amax_history.numel(), a, int(margin), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -137,11 +212,17 @@ def te_fp8_cast_delayed_scaling(x, fmt, q_out, q_scale_inv_out, scale, amax_hist
 
 def te_fp8_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, d, epilogue="none", bias=None, aux=None,
                 workspace=None, stream=None) -> None:
+    _require(a.dim() == 2 and b.dim() == 2, "a and b must be 2-D")
     M, K = a.shape
     N = b.shape[0]
-    d_dtype = TE_BF16 if d.dtype == torch.bfloat16 else TE_FP32
-    epi = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _codes(a, "a", (M, K))
+    _codes(b, "b", (N, K))
+    _scalar_f32(a_scale_inv, "a_scale_inv")
+    _scalar_f32(b_scale_inv, "b_scale_inv")
+    epi = _epilogue(epilogue)
+    d_dtype = _gemm_out(d, "d", M, N, epi)
+    _epi_tensors(bias, (N,), aux, M, N)
+    ws_bytes = _ws_bytes(workspace)
     _check("te_fp8_gemm", _lib.te_fp8_gemm(
         _ptr(a), _ptr(a_scale_inv), _fmt(a_fmt), _ptr(b), _ptr(b_scale_inv), _fmt(b_fmt), M, N, K,
         _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _ptr(workspace), ws_bytes, _stream(stream)))
@@ -149,7 +230,13 @@ def te_fp8_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, d, epilogue="none"
 
 def te_mxfp8_quantize(x, fmt, direction, q_row=None, s_row=None, q_col=None, s_col=None, stream=None) -> None:
     d = DIRECTIONS[direction] if isinstance(direction, str) else int(direction)
+    _require(x.dim() == 2, "x must be 2-D")
     rows, cols = x.shape
+    _bf16(x, "x", (rows, cols))
+    _codes(q_row, "q_row", (rows, cols), optional=True)
+    _codes(s_row, "s_row", (rows, cols // 32), optional=True)
+    _codes(q_col, "q_col", (cols, rows), optional=True)
+    _codes(s_col, "s_col", (cols, rows // 32), optional=True)
     _check("te_mxfp8_quantize", _lib.te_mxfp8_quantize(
         _ptr(x), rows, cols, _fmt(fmt), d, _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _stream(stream)))
 
@@ -159,9 +246,16 @@ def te_mxfp8_quantize_bgrad_workspace_size(rows: int, cols: int) -> int:
 
 
 def te_mxfp8_quantize_bgrad(x, fmt, q_row, s_row, q_col, s_col, bgrad, workspace, stream=None) -> None:
+    _require(x.dim() == 2, "x must be 2-D")
     rows, cols = x.shape
+    _bf16(x, "x", (rows, cols))
+    _codes(q_row, "q_row", (rows, cols))
+    _codes(s_row, "s_row", (rows, cols // 32))
+    _codes(q_col, "q_col", (cols, rows))
+    _codes(s_col, "s_col", (cols, rows // 32))
+    _check_tensor(bgrad, "bgrad", (cols,), {torch.float32, torch.bfloat16}, "float32 or bfloat16")
     b_dtype = TE_FP32 if bgrad.dtype == torch.float32 else TE_BF16
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = _ws_bytes(workspace)
     _check("te_mxfp8_quantize_bgrad", _lib.te_mxfp8_quantize_bgrad(
         _ptr(x), rows, cols, _fmt(fmt), _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col), _ptr(bgrad), b_dtype,
         _ptr(workspace), ws_bytes, _stream(stream)))
@@ -171,13 +265,25 @@ def te_mxfp8_gemm_workspace_size(M: int, N: int, K: int) -> int:
     return int(_lib.te_mxfp8_gemm_workspace_size(M, N, K))
 
 
-def te_mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, d, epilogue="none", bias=None, aux=None,
-                  workspace=None, stream=None) -> None:
+def _mx_operands(a, a_scale, b, b_scale):
+    """Shapes of two MXFP8 operands: a [M, K] + [M, K/32], b [N, K] + [N, K/32] -> (M, N, K)."""
+    _require(a.dim() == 2 and b.dim() == 2, "a and b must be 2-D")
     M, K = a.shape
     N = b.shape[0]
-    d_dtype = TE_BF16 if d.dtype == torch.bfloat16 else TE_FP32
-    epi = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _codes(a, "a", (M, K))
+    _codes(a_scale, "a_scale", (M, K // 32))
+    _codes(b, "b", (N, K))
+    _codes(b_scale, "b_scale", (N, K // 32))
+    return M, N, K
+
+
+def te_mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, d, epilogue="none", bias=None, aux=None,
+                  workspace=None, stream=None) -> None:
+    M, N, K = _mx_operands(a, a_scale, b, b_scale)
+    epi = _epilogue(epilogue)
+    d_dtype = _gemm_out(d, "d", M, N, epi)
+    _epi_tensors(bias, (N,), aux, M, N)
+    ws_bytes = _ws_bytes(workspace)
     _check("te_mxfp8_gemm", _lib.te_mxfp8_gemm(
         _ptr(a), _ptr(a_scale), _fmt(a_fmt), _ptr(b), _ptr(b_scale), _fmt(b_fmt), M, N, K,
         _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _ptr(workspace), ws_bytes, _stream(stream)))
@@ -185,10 +291,12 @@ def te_mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, d, epilogue="none", bias
 
 def te_mxfp8_gemm_mxout(a, a_scale, a_fmt, b, b_scale, b_fmt, d, d_scale, d_fmt, epilogue="none", bias=None,
                         aux=None, workspace=None, stream=None) -> None:
-    M, K = a.shape
-    N = b.shape[0]
-    epi = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    M, N, K = _mx_operands(a, a_scale, b, b_scale)
+    epi = _epilogue(epilogue)
+    _codes(d, "d", (M, N))
+    _codes(d_scale, "d_scale", (M, N // 32))
+    _epi_tensors(bias, (N,), aux, M, N)
+    ws_bytes = _ws_bytes(workspace)
     _check("te_mxfp8_gemm_mxout", _lib.te_mxfp8_gemm_mxout(
         _ptr(a), _ptr(a_scale), _fmt(a_fmt), _ptr(b), _ptr(b_scale), _fmt(b_fmt), M, N, K,
         _ptr(d), _ptr(d_scale), _fmt(d_fmt), epi, _ptr(bias), _ptr(aux), _ptr(workspace), ws_bytes, _stream(stream)))
@@ -196,10 +304,15 @@ def te_mxfp8_gemm_mxout(a, a_scale, a_fmt, b, b_scale, b_fmt, d, d_scale, d_fmt,
 
 def te_mxfp8_grouped_gemm(m_splits, a, a_scale, a_fmt, b, b_scale, b_fmt, n: int, d, epilogue="none",
                           bias=None, aux=None, workspace=None, stream=None) -> None:
-    total_m, K = a.shape
-    d_dtype = TE_BF16 if d.dtype == torch.bfloat16 else TE_FP32
-    epi = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _require(m_splits is not None and m_splits.dtype == torch.int32 and m_splits.dim() == 1,
+             "m_splits: expected a 1-D int32 tensor (one row count per group)")
+    G = m_splits.numel()
+    total_m, _, K = _mx_operands(a, a_scale, b, b_scale)
+    _require(b.shape[0] == G * int(n), f"b: expected {G} x {int(n)} = {G * int(n)} rows, got {b.shape[0]}")
+    epi = _epilogue(epilogue)
+    d_dtype = _gemm_out(d, "d", total_m, int(n), epi)
+    _epi_tensors(bias, (G, int(n)), aux, total_m, int(n))
+    ws_bytes = _ws_bytes(workspace)
     _check("te_mxfp8_grouped_gemm", _lib.te_mxfp8_grouped_gemm(
         m_splits.numel(), _ptr(m_splits), total_m, _ptr(a), _ptr(a_scale), _fmt(a_fmt), _ptr(b), _ptr(b_scale),
         _fmt(b_fmt), n, K, _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _ptr(workspace), ws_bytes,
@@ -210,13 +323,23 @@ def _block_scaling(mode) -> int:
     return BLOCK_SCALINGS[mode] if isinstance(mode, str) else int(mode)
 
 
+def _block_scale_shape(rows, cols, block_2d):
+    return ((rows + 127) // 128 if block_2d else rows, cols // 128)
+
+
 def te_fp8_block_quantize(x, fmt, block_2d, q, scale_inv, stream=None) -> None:
+    _require(x.dim() == 2, "x must be 2-D")
     rows, cols = x.shape
+    _bf16(x, "x", (rows, cols))
+    _codes(q, "q", (rows, cols))
+    _f32(scale_inv, "scale_inv", _block_scale_shape(rows, cols, block_2d))
     _check("te_fp8_block_quantize", _lib.te_fp8_block_quantize(
         _ptr(x), rows, cols, _fmt(fmt), int(bool(block_2d)), _ptr(q), _ptr(scale_inv), _stream(stream)))
 
 
 def te_fp8_block_scales_to_mx(scale_inv, rows: int, cols: int, block_2d: bool, mx_scale, stream=None) -> None:
+    _f32(scale_inv, "scale_inv", _block_scale_shape(int(rows), int(cols), block_2d))
+    _codes(mx_scale, "mx_scale", (int(rows), int(cols) // 32))
     _check("te_fp8_block_scales_to_mx", _lib.te_fp8_block_scales_to_mx(
         _ptr(scale_inv), int(rows), int(cols), int(bool(block_2d)), _ptr(mx_scale), _stream(stream)))
 
@@ -227,11 +350,17 @@ def te_fp8_block_gemm_workspace_size(M: int, N: int, K: int, mode="e8m0") -> int
 
 def te_fp8_block_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, b_block_2d, d, epilogue="none", bias=None,
                       aux=None, mode="e8m0", workspace=None, stream=None) -> None:
+    _require(a.dim() == 2 and b.dim() == 2, "a and b must be 2-D")
     M, K = a.shape
     N = b.shape[0]
-    d_dtype = TE_BF16 if d.dtype == torch.bfloat16 else TE_FP32
-    epi = EPILOGUES[epilogue] if isinstance(epilogue, str) else int(epilogue)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _codes(a, "a", (M, K))
+    _codes(b, "b", (N, K))
+    _f32(a_scale_inv, "a_scale_inv", _block_scale_shape(M, K, False))
+    _f32(b_scale_inv, "b_scale_inv", _block_scale_shape(N, K, b_block_2d))
+    epi = _epilogue(epilogue)
+    d_dtype = _gemm_out(d, "d", M, N, epi)
+    _epi_tensors(bias, (N,), aux, M, N)
+    ws_bytes = _ws_bytes(workspace)
     _check("te_fp8_block_gemm", _lib.te_fp8_block_gemm(
         _ptr(a), _ptr(a_scale_inv), _fmt(a_fmt), _ptr(b), _ptr(b_scale_inv), _fmt(b_fmt), int(bool(b_block_2d)),
         M, N, K, _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _block_scaling(mode), _ptr(workspace), ws_bytes,

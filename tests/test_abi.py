@@ -311,7 +311,8 @@ def test_binding_refuses_host_and_strided_tensors():
     import torch
     x = torch.zeros((64, 64), dtype=torch.int16)
     with pytest.raises(ValueError, match="GPU tensor"):
-        te.te_mxfp8_quantize(x, "e4m3", "row", x, x)
+        te.te_mxfp8_quantize(x, "e4m3", "row", torch.zeros((64, 64), dtype=torch.uint8),
+                             torch.zeros((64, 2), dtype=torch.uint8))
 
     class FakeStrided:
         is_cuda = True
@@ -326,3 +327,82 @@ def test_binding_refuses_host_and_strided_tensors():
     with pytest.raises(ValueError, match="contiguous"):
         te._ptr(FakeStrided())
     assert te._ptr(None) is None
+
+
+def test_binding_checks_shapes_and_dtypes_before_the_call():
+    # host tensors of the right shape and dtype get as far as the device check; each wrong
+    # shape or dtype is refused first (the library itself never sees the tensor sizes)
+    import torch
+    u8, bf, f32, i32 = torch.uint8, torch.bfloat16, torch.float32, torch.int32
+
+    def t(shape, dtype):
+        return torch.zeros(shape, dtype=dtype)
+
+    M, N, K = 32, 48, 128
+    a, sa, b, sb = t((M, K), u8), t((M, K // 32), u8), t((N, K), u8), t((N, K // 32), u8)
+    d, bias, aux = t((M, N), bf), t((N,), bf), t((M, N), bf)
+
+    def refuse(match, fn, *args, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*args, **kw)
+
+    # MXFP8 GEMM: the valid call reaches the device check
+    refuse("GPU tensor", te.te_mxfp8_gemm, a, sa, "e4m3", b, sb, "e4m3", d, "bias_gelu_aux", bias, aux)
+    refuse("d: expected bfloat16 or float32", te.te_mxfp8_gemm, a, sa, "e4m3", b, sb, "e4m3", t((M, N), torch.float16))
+    refuse("accumulate epilogue needs float32", te.te_mxfp8_gemm, a, sa, "e4m3", b, sb, "e4m3", d, "accumulate")
+    refuse(r"d: expected shape \(32, 48\)", te.te_mxfp8_gemm, a, sa, "e4m3", b, sb, "e4m3", t((M, N - 16), bf))
+    refuse(r"b: expected shape \(48, 128\)", te.te_mxfp8_gemm, a, sa, "e4m3", t((N, K + 128), u8), sb, "e4m3", d)
+    refuse("a_scale: expected shape", te.te_mxfp8_gemm, a, t((M, K // 16), u8), "e4m3", b, sb, "e4m3", d)
+    refuse("b_scale: expected shape", te.te_mxfp8_gemm, a, sa, "e4m3", b, t((N - 16, K // 32), u8), "e4m3", d)
+    refuse("a: expected 1-byte codes", te.te_mxfp8_gemm, t((M, K), bf), sa, "e4m3", b, sb, "e4m3", d)
+    refuse("bias: expected shape", te.te_mxfp8_gemm, a, sa, "e4m3", b, sb, "e4m3", d, "bias", t((N + 16,), bf))
+    refuse("bias: expected bf16", te.te_mxfp8_gemm, a, sa, "e4m3", b, sb, "e4m3", d, "bias", t((N,), f32))
+    refuse("aux: expected shape", te.te_mxfp8_gemm, a, sa, "e4m3", b, sb, "e4m3", d, "bias_gelu_aux", bias,
+           t((M, N - 16), bf))
+    # MXFP8 output
+    refuse("GPU tensor", te.te_mxfp8_gemm_mxout, a, sa, "e4m3", b, sb, "e4m3", t((M, N), u8), t((M, N // 32), u8),
+           "e4m3")
+    refuse("d_scale: expected shape", te.te_mxfp8_gemm_mxout, a, sa, "e4m3", b, sb, "e4m3", t((M, N), u8),
+           t((M, N // 16), u8), "e4m3")
+    # grouped
+    G = 3
+    gb, gsb = t((G * N, K), u8), t((G * N, K // 32), u8)
+    splits = t((G,), i32)
+    refuse("GPU tensor", te.te_mxfp8_grouped_gemm, splits, a, sa, "e4m3", gb, gsb, "e4m3", N, d, "bias",
+           t((G, N), bf))
+    refuse("m_splits: expected a 1-D int32", te.te_mxfp8_grouped_gemm, t((G,), torch.int64), a, sa, "e4m3", gb, gsb,
+           "e4m3", N, d)
+    refuse("b: expected 3 x 48", te.te_mxfp8_grouped_gemm, splits, a, sa, "e4m3", b, sb, "e4m3", N, d)
+    refuse("bias: expected shape", te.te_mxfp8_grouped_gemm, splits, a, sa, "e4m3", gb, gsb, "e4m3", N, d, "bias",
+           bias)
+    refuse("d: expected bfloat16 or float32", te.te_mxfp8_grouped_gemm, splits, a, sa, "e4m3", gb, gsb, "e4m3", N,
+           t((M, N), torch.float16))
+    # per-tensor FP8 GEMM
+    one = t((1,), f32)
+    refuse("GPU tensor", te.te_fp8_gemm, a, one, "e4m3", b, one, "e4m3", d)
+    refuse("a_scale_inv: expected a float32 scalar", te.te_fp8_gemm, a, t((1,), bf), "e4m3", b, one, "e4m3", d)
+    refuse(r"b: expected shape", te.te_fp8_gemm, a, one, "e4m3", t((N, 2 * K), u8), one, "e4m3", d)
+    # blockwise GEMM
+    bsa, bsb2 = t((M, K // 128), f32), t(((N + 127) // 128, K // 128), f32)
+    refuse("GPU tensor", te.te_fp8_block_gemm, a, bsa, "e4m3", b, bsb2, "e4m3", True, d)
+    refuse("b_scale_inv: expected shape", te.te_fp8_block_gemm, a, bsa, "e4m3", b, bsb2, "e4m3", False, d)
+    refuse("a_scale_inv: expected float32", te.te_fp8_block_gemm, a, t((M, K // 128), bf), "e4m3", b, bsb2, "e4m3",
+           True, d)
+    # quantize
+    x = t((M, K), bf)
+    refuse("GPU tensor", te.te_mxfp8_quantize, x, "e4m3", "row", t((M, K), u8), t((M, K // 32), u8))
+    refuse("q_row: expected shape", te.te_mxfp8_quantize, x, "e4m3", "row", t((K, M), u8), t((M, K // 32), u8))
+    refuse("s_col: expected shape", te.te_mxfp8_quantize, x, "e4m3", "col", None, None, t((K, M), u8),
+           t((K, M // 16), u8))
+    refuse("x: expected bf16", te.te_mxfp8_quantize, t((M, K), f32), "e4m3", "row", t((M, K), u8),
+           t((M, K // 32), u8))
+    refuse("bgrad: expected shape", te.te_mxfp8_quantize_bgrad, x, "e5m2", t((M, K), u8), t((M, K // 32), u8),
+           t((K, M), u8), t((K, M // 32), u8), t((M,), f32), None)
+    refuse("q: expected shape", te.te_fp8_block_quantize, x, "e4m3", True, t((M, K - 32), u8), t((1, 1), f32))
+    refuse("scale_inv: expected shape", te.te_fp8_block_quantize, x, "e4m3", False, t((M, K), u8), t((1, 1), f32))
+    refuse("mx_scale: expected shape", te.te_fp8_block_scales_to_mx, t((M, 1), f32), M, K, False, t((M, 2), u8))
+    # casts
+    refuse("q_out: expected shape", te.te_fp8_cast_current_scaling, x, "e4m3", t((M * K - 1,), u8), one, one, one, None)
+    refuse("amax_out: expected a float32", te.te_amax_reduce, x, t((1,), bf), None)
+    refuse("amax_history: expected a 1-D float32", te.te_fp8_cast_delayed_scaling, x, "e4m3", t((M, K), u8), one, one,
+           t((16,), bf), None)
