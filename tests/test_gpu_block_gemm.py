@@ -31,7 +31,7 @@ import torch
 import mfma_model
 import oracle
 import workloads
-from gpu_util import bf16_rne, bf16_to_f64, dev, gemm_check, host
+from gpu_util import assert_stated_misses, bf16_rne, bf16_to_f64, dev, gemm_check, host
 
 pytestmark = pytest.mark.gpu
 
@@ -106,8 +106,6 @@ def run(mode, qa, sa, fa, qb, sb, fb, b_2d, epi="none", bias=None, out_dtype=tor
 @pytest.mark.parametrize("M,N,K", [(128, 128, 128), (272, 304, 384), (16, 16, 1024), (8192, 4112, 512),
                                    (272, 304, 2176)])
 def test_block_gemm_exact_bitexact(mode, b_2d, fa, fb, M, N, K):
-    if M * N > 1 << 22 and (fa, fb) != ("e4m3", "e4m3"):
-        pytest.skip("the big-tile shape runs once per mode and B layout")
     rng = np.random.default_rng([M, N, K, b_2d])
     qa, qb = exact_codes(rng, (M, K), fa), exact_codes(rng, (N, K), fb)
     sa, sb = exact_scales(rng, (M, K // 128)), exact_scales(rng, b_scale_shape(N, K, b_2d))
@@ -116,8 +114,15 @@ def test_block_gemm_exact_bitexact(mode, b_2d, fa, fb, M, N, K):
         sa_ref, sb_ref = oracle.pow2_at_least(sa), oracle.pow2_at_least(sb)
     else:
         sa_ref, sb_ref = sa, sb
-    ref, _, _ = oracle.block_gemm(qa, sa_ref, oracle.format_by_name(fa), qb, sb_ref, oracle.format_by_name(fb), b_2d)
-    assert np.array_equal(host(d).astype(np.float64), ref)
+    rows = np.arange(M)
+    if M * N > 1 << 22 and (fa, fb) != ("e4m3", "e4m3"):
+        # the big-tile shape with an E5M2 operand: every 256-row tile boundary, the last row and random rows
+        # (exact-integer data, so each sampled fp32 output must match bit for bit)
+        rows = np.array(sorted({0, M - 1} | {256 * t + o for t in range(M // 256) for o in (0, 255)}
+                               | set(rng.choice(M, 16, replace=False).tolist())))
+    ref, _, _ = oracle.block_gemm(qa[rows], sa_ref[rows], oracle.format_by_name(fa), qb, sb_ref,
+                                  oracle.format_by_name(fb), b_2d)
+    assert np.array_equal(host(d[rows]).astype(np.float64), ref)
 
 
 def test_block_gemm_k_zero_and_empty():
@@ -148,7 +153,7 @@ def e8m0_expanded(s, rows, b_2d):
     return np.repeat(c, 128, axis=0)[:rows] if b_2d else c
 
 
-def check_recipe(mode, qa, sa, fa, qb, sb, fb, b_2d, rows, cols, d, bias=None, epi="none"):
+def check_recipe(key, mode, qa, sa, fa, qb, sb, fb, b_2d, rows, cols, d, bias=None, epi="none"):
     """Sampled (or full) outputs against the oracle within the GEMM bound."""
     K = qa.shape[1]
     Fa, Fb = oracle.format_by_name(fa), oracle.format_by_name(fb)
@@ -167,8 +172,8 @@ def check_recipe(mode, qa, sa, fa, qb, sb, fb, b_2d, rows, cols, d, bias=None, e
     k_eff = K * 1.25 if mode == "fp32" else K
     ok, stated = gemm_check(got, ref, s, None if bias is None else bias[cols], k_eff, h_pairs,
                             through_gelu=epi == "bias_gelu_aux")
-    print(f"{mode}: {ok.mean():.6f} within bound, {stated.mean():.6f} within the stated tolerance alone")
     assert ok.all(), f"{(~ok).sum()} of {ok.size} outside the bound"
+    assert_stated_misses(f"{key}:{mode}:{epi}", int((~stated).sum()), stated.size)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -177,7 +182,8 @@ def test_block_gemm_recipe_full(mode, b_2d):
     M, N, K = 512, 656, 2048
     qa, sa, qb, sb = recipe_operands(M, N, K, b_2d, seed=51)
     d, _ = run(mode, qa, sa, "e4m3", qb, sb, "e4m3", b_2d, out_dtype=torch.bfloat16)
-    check_recipe(mode, qa, sa, "e4m3", qb, sb, "e4m3", b_2d, np.arange(M), np.arange(N), d)
+    check_recipe(f"block_recipe:{'2d' if b_2d else '1d'}", mode, qa, sa, "e4m3", qb, sb, "e4m3", b_2d, np.arange(M),
+                 np.arange(N), d)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -191,7 +197,8 @@ def test_block_gemm_fp32_scales_not_powers_of_two(mode, b_2d):
     sa = (sa * rng.uniform(1.0, 2.0, sa.shape)).astype(np.float32)
     sb = (sb * rng.uniform(1.0, 2.0, sb.shape)).astype(np.float32)
     d, _ = run(mode, qa, sa, "e5m2", qb, sb, "e4m3", b_2d)
-    check_recipe(mode, qa, sa, "e5m2", qb, sb, "e4m3", b_2d, np.arange(M), np.arange(N), d)
+    check_recipe(f"block_nonpow2:{'2d' if b_2d else '1d'}", mode, qa, sa, "e5m2", qb, sb, "e4m3", b_2d, np.arange(M),
+                 np.arange(N), d)
 
 
 @pytest.mark.parametrize("b_2d", [False, True])
@@ -260,7 +267,7 @@ def test_block_square_full_size_sampled(mode):
     full_qa = np.zeros((g.M, g.K), np.uint8)
     full_sa = np.ones((g.M, g.K // 128), np.float32)
     full_qa[rows], full_sa[rows] = oqa, osa
-    check_recipe(mode, full_qa, full_sa, g.fmt_a, full_qb, full_sb, g.fmt_b, False, rows, cols, d)
+    check_recipe("block_square_8192", mode, full_qa, full_sa, g.fmt_a, full_qb, full_sb, g.fmt_b, False, rows, cols, d)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -272,7 +279,7 @@ def test_block_gemm_forward_epilogues_vs_oracle(mode, epi):
     qa, sa, qb, sb = recipe_operands(M, N, K, True, seed=91)
     bias = workloads.normal_bf16(91, 5, (N,), 0.5)
     d, aux = run(mode, qa, sa, "e4m3", qb, sb, "e4m3", True, epi, bias, torch.bfloat16)
-    check_recipe(mode, qa, sa, "e4m3", qb, sb, "e4m3", True, np.arange(M), np.arange(N), d, bias, epi)
+    check_recipe("block_epilogue", mode, qa, sa, "e4m3", qb, sb, "e4m3", True, np.arange(M), np.arange(N), d, bias, epi)
     if epi == "bias_gelu_aux":
         # aux is the bf16 pre-activation: the bias epilogue's D for the same inputs, bit for bit
         d_bias, _ = run(mode, qa, sa, "e4m3", qb, sb, "e4m3", True, "bias", bias, torch.bfloat16)

@@ -16,7 +16,7 @@ import torch
 import mfma_model
 import oracle
 import workloads
-from gpu_util import bf16_to_f64, dev, gemm_check, host, model_outputs
+from gpu_util import assert_stated_misses, bf16_to_f64, dev, gemm_check, host, model_outputs
 
 pytestmark = pytest.mark.gpu
 
@@ -98,6 +98,7 @@ def test_per_tensor_gemm(epi, M, N, K):
                                                                 ri, ci)
     ok, stated = gemm_check(bf16_to_f64(got_bits), ref, s, b, K, h_pairs, through_gelu=epi == "bias_gelu_aux")
     assert ok.all(), f"{(~ok).sum()} of {ok.size} outside the bound"
+    assert_stated_misses(f"per_tensor:{M}x{N}x{K}:{epi}", int((~stated).sum()), stated.size)
 
 
 def test_per_tensor_gemm_fp32_output():
