@@ -42,12 +42,15 @@
  *   - Pointers are device pointers unless stated; the caller owns every
  *     buffer.  The library never allocates, frees or caches device memory
  *     and keeps no state between calls other than a per-device cache of the
- *     compute-unit count.
+ *     compute-unit count and of the architecture check.
  *   - All work is enqueued on `stream` (0 = the null stream); no entry point
  *     synchronizes the host.
  *   - Arguments are validated on the host before anything is enqueued; on
- *     failure a non-TE_OK status is returned and nothing runs.  A failed
- *     launch returns TE_ERR_HIP.  Nothing throws across the ABI.
+ *     failure a non-TE_OK status is returned and nothing runs.  A call with
+ *     work to enqueue then checks that the current device is a gfx950
+ *     (looked up once per device and cached) and returns TE_ERR_ARCH
+ *     otherwise.  A failed launch returns TE_ERR_HIP.  Nothing throws across
+ *     the ABI.
  *   - Data pointers must be 16-byte aligned (TE_ERR_ALIGN otherwise); scale
  *     pointers and scalar outputs have no alignment requirement beyond
  *     their type.
@@ -75,7 +78,8 @@ typedef enum {
   TE_ERR_DTYPE = 4,      /* unsupported format / dtype / format combination */
   TE_ERR_WORKSPACE = 5,  /* workspace smaller than the size query returns */
   TE_ERR_HIP = 6,        /* a HIP call or kernel launch failed */
-  TE_ERR_VALUE = 7       /* an enum argument is out of range */
+  TE_ERR_VALUE = 7,      /* an enum argument is out of range */
+  TE_ERR_ARCH = 8        /* the current device is not a gfx950 (the kernels are built for it only) */
 } te_status;
 
 typedef enum { TE_BF16 = 0, TE_FP32 = 1, TE_E4M3 = 2, TE_E5M2 = 3, TE_E8M0 = 4 } te_dtype;

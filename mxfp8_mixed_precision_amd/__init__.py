@@ -21,7 +21,7 @@ if not os.path.exists(_LIB_PATH):
 _lib = ctypes.CDLL(_LIB_PATH)
 
 # enum values of include/temx.h
-TE_OK, TE_ERR_NULL, TE_ERR_SHAPE, TE_ERR_ALIGN, TE_ERR_DTYPE, TE_ERR_WORKSPACE, TE_ERR_HIP, TE_ERR_VALUE = range(8)
+TE_OK, TE_ERR_NULL, TE_ERR_SHAPE, TE_ERR_ALIGN, TE_ERR_DTYPE, TE_ERR_WORKSPACE, TE_ERR_HIP, TE_ERR_VALUE, TE_ERR_ARCH = range(9)
 TE_BF16, TE_FP32, TE_E4M3, TE_E5M2, TE_E8M0 = range(5)
 TE_EPI_NONE, TE_EPI_BIAS, TE_EPI_BIAS_GELU_AUX, TE_EPI_DGELU, TE_EPI_ACCUMULATE = range(5)
 TE_ROWWISE, TE_COLWISE, TE_BOTH = 1, 2, 3

@@ -290,6 +290,7 @@ extern "C" te_status te_amax_reduce(const uint16_t* x, int64_t n, float* amax_ou
   const int64_t blocks = amax_blocks(n);
   TE_REQUIRE(workspace_bytes >= (size_t)blocks * sizeof(uint32_t), TE_ERR_WORKSPACE);
   uint32_t* partial = static_cast<uint32_t*>(workspace);
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   if (launch_amax(x, n, partial, blocks, stream) != TE_OK) return TE_ERR_HIP;
   hipLaunchKernelGGL(amax_final_kernel, dim3(1), dim3(kAmaxThreads), 0, stream, partial, (int)blocks, amax_out);
   return launch_status();
@@ -309,6 +310,7 @@ extern "C" te_status te_fp8_cast_current_scaling(const uint16_t* x, int64_t n, t
   TE_REQUIRE(workspace_bytes >= (size_t)blocks * sizeof(uint32_t), TE_ERR_WORKSPACE);
   TE_REQUIRE(n / 8 / 256 < (int64_t)1 << 31, TE_ERR_SHAPE);
   uint32_t* partial = static_cast<uint32_t*>(workspace);
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   if (launch_amax(x, n, partial, blocks, stream) != TE_OK) return TE_ERR_HIP;
   // at least one workgroup, which writes amax, scale and scale_inv (n = 0 included)
   int64_t grid = (n / 8 + kCastThreads * kCastUnroll - 1) / (kCastThreads * kCastUnroll);
@@ -342,6 +344,7 @@ extern "C" te_status te_fp8_cast_delayed_scaling(const uint16_t* x, int64_t n, t
   TE_REQUIRE(workspace_bytes >= (size_t)blocks * sizeof(uint32_t), TE_ERR_WORKSPACE);
   uint32_t* partial = static_cast<uint32_t*>(workspace);
   const int mr = algo == TE_AMAX_MOST_RECENT ? 1 : 0;
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   if (fmt == TE_E4M3) {
     hipLaunchKernelGGL(cast_amax_kernel<TE_E4M3>, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream, x, n, scale,
                        q_out, partial);

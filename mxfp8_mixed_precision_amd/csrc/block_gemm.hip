@@ -43,6 +43,7 @@ extern "C" te_status te_fp8_block_gemm(const uint8_t* a, const float* a_scale_in
   te_status st = check_common(a, sa, a_fmt, b, sb, b_fmt, d, d_dtype, epi, bias, aux, M > 0 && N > 0, K > 0);
   if (st != TE_OK) return st;
   if (M == 0 || N == 0) return TE_OK;
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   auto launch = mode == TE_BLOCK_SCALES_E8M0 ? launch_block_gemm_e8m0 : launch_block_gemm_fp32;
   return launch(a, a_scale_inv, b, b_scale_inv, b_block_2d, M, N, K, d, d_dtype, epi, bias, aux, a_fmt, b_fmt, stream);
 }

@@ -164,6 +164,7 @@ extern "C" te_status te_fp8_block_quantize(const uint16_t* x, int64_t rows, int6
   TE_REQUIRE(x != nullptr && q != nullptr && scale_inv != nullptr, TE_ERR_NULL);
   TE_REQUIRE(aligned16(x) && aligned16(q), TE_ERR_ALIGN);
   TE_REQUIRE(((uintptr_t)scale_inv & 3u) == 0, TE_ERR_ALIGN);
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   return fmt == TE_E4M3 ? launch_block_quantize<TE_E4M3>(x, rows, cols, block_2d, q, scale_inv, stream)
                         : launch_block_quantize<TE_E5M2>(x, rows, cols, block_2d, q, scale_inv, stream);
 }

@@ -47,6 +47,7 @@ extern "C" te_status te_fp8_block_scales_to_mx(const float* scale_inv, int64_t r
   if (rows == 0 || kb == 0) return TE_OK;
   TE_REQUIRE(scale_inv != nullptr && mx_scale != nullptr, TE_ERR_NULL);
   TE_REQUIRE(((uintptr_t)scale_inv & 3u) == 0 && ((uintptr_t)mx_scale & 3u) == 0, TE_ERR_ALIGN);
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   const int64_t count = rows * kb;
   hipLaunchKernelGGL(block_scale_expand_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream,
                      scale_inv, reinterpret_cast<uint32_t*>(mx_scale), count, kb, block_2d ? 7 : 0);

@@ -115,6 +115,7 @@ extern "C" te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_
   te_status st = check_common(a, a_scale, a_fmt, b, b_scale, b_fmt, d, d_dtype, epi, bias, aux, M > 0 && N > 0, K > 0);
   if (st != TE_OK) return st;
   if (M == 0 || N == 0) return TE_OK;
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   GemmParams p{a, a_scale, b, b_scale, d, bias, aux, M, N, K, nullptr, 0};
   const Tile t = pick_tile(M, N, K);
   const dim3 grid = tile_grid(t, M, N);
@@ -140,6 +141,7 @@ extern "C" te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scal
   if (st != TE_OK) return st;
   if (M == 0 || N == 0) return TE_OK;
   TE_REQUIRE(d_scale != nullptr, TE_ERR_NULL);
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   GemmParams p{a, a_scale, b, b_scale, d, bias, aux, M, N, K, nullptr, 0, d_scale};
   const Tile t = pick_tile(M, N, K);
   const dim3 grid = tile_grid(t, M, N);
@@ -165,6 +167,7 @@ extern "C" te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_
   if (st != TE_OK) return st;
   if (M == 0 || N == 0) return TE_OK;
   TE_REQUIRE(a_scale_inv != nullptr && b_scale_inv != nullptr, TE_ERR_NULL);
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   // the block-scale descriptors are never read in per-tensor mode; they point at the data
   GemmParams p{a, a, b, b, d, bias, aux, M, N, K, nullptr, 0, nullptr, a_scale_inv, b_scale_inv};
   const Tile t = pick_tile(M, N, K);
@@ -193,6 +196,7 @@ extern "C" te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_
   te_status st = check_common(a, a_scale, a_fmt, b, b_scale, b_fmt, d, d_dtype, epi, bias, aux, total_m > 0, true);
   if (st != TE_OK) return st;
   if (total_m == 0) return TE_OK;
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   GemmParams p{a, a_scale, b, b_scale, d, bias, aux, total_m, N, K, m_splits, num_groups};
   int grid = device_cu_count();
   grid = grid < 8 ? 8 : (grid / 8) * 8;

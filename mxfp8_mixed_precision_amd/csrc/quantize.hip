@@ -560,6 +560,7 @@ extern "C" te_status te_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t 
   TE_REQUIRE(aligned16(x), TE_ERR_ALIGN);
   TE_REQUIRE(!row || aligned16(q_row), TE_ERR_ALIGN);
   TE_REQUIRE(!col || aligned16(q_col), TE_ERR_ALIGN);
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   return fmt == TE_E4M3 ? launch_quantize<TE_E4M3>(x, rows, cols, dir, q_row, s_row, q_col, s_col, stream)
                         : launch_quantize<TE_E5M2>(x, rows, cols, dir, q_row, s_row, q_col, s_col, stream);
 }
@@ -588,6 +589,7 @@ extern "C" te_status te_mxfp8_quantize_bgrad(const uint16_t* x, int64_t rows, in
     TE_REQUIRE(((uintptr_t)workspace & 3u) == 0, TE_ERR_ALIGN);
     TE_REQUIRE(workspace_bytes >= te_mxfp8_quantize_bgrad_workspace_size(rows, cols), TE_ERR_WORKSPACE);
   }
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   int tiles = 0;
   float* ws = static_cast<float*>(workspace);
   if (rows > 0) {

@@ -20,6 +20,10 @@ inline te_status launch_status() {
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Whether the current device is a gfx950, the only target the kernels are
+// built for (looked up once per device and cached).
+bool device_is_gfx950();
+
 // The blockwise FP8 GEMM in one scale mode (block_gemm_e8m0.hip,
 // block_gemm_fp32.hip), after te_fp8_block_gemm has checked the arguments.
 te_status launch_block_gemm_e8m0(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int b2d,

@@ -35,8 +35,9 @@ def test_header_symbols_are_exported():
 
 def test_status_strings():
     assert te.te_status_str(te.TE_OK) == "TE_OK"
-    for s in range(1, 8):
+    for s in range(1, 9):
         assert te.te_status_str(s).startswith("TE_ERR_")
+    assert te.te_status_str(te.TE_ERR_ARCH).startswith("TE_ERR_ARCH")
     assert te.te_status_str(99) == "unknown te_status"
 
 
@@ -406,3 +407,17 @@ def test_binding_checks_shapes_and_dtypes_before_the_call():
     refuse("amax_out: expected a float32", te.te_amax_reduce, x, t((1,), bf), None)
     refuse("amax_history: expected a 1-D float32", te.te_fp8_cast_delayed_scaling, x, "e4m3", t((M, K), u8), one, one,
            t((16,), bf), None)
+
+
+def test_valid_call_without_a_gfx950_returns_arch_error():
+    # a call that passes validation checks the device before enqueuing anything; with no GPU
+    # (this container) that check fails.  Skipped where a GPU is visible: there the call would
+    # launch on the fake addresses.
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible")
+    assert quant() == te.TE_ERR_ARCH
+    assert L.te_mxfp8_gemm(P, P2, te.TE_E4M3, P, P2, te.TE_E4M3, 16, 16, 128, P3, te.TE_BF16, te.TE_EPI_NONE,
+                           None, None, None, 0, None) == te.TE_ERR_ARCH
+    # the checks before it still come first
+    assert quant(x=BAD) == te.TE_ERR_ALIGN
