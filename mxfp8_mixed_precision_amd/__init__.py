@@ -41,6 +41,7 @@ _SIGS = {
     "te_amax_workspace_size": (_sz, [_i64]),
     "te_amax_reduce": (ctypes.c_int, [_vp, _i64, _vp, _vp, _sz, _vp]),
     "te_fp8_cast_current_scaling": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "te_fp8_cast_current_scaling_noalloc": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp]),
     "te_fp8_cast_delayed_scaling": (ctypes.c_int, [_vp, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, ctypes.c_int,
                                                    ctypes.c_int, ctypes.c_int, _vp, _sz, _vp]),
     "te_fp8_gemm": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _i64, _i64, _i64,
@@ -195,6 +196,16 @@ def te_fp8_cast_current_scaling(x, fmt, q_out, amax_out, scale_out, scale_inv_ou
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def te_fp8_cast_current_scaling_noalloc(x, fmt, q_out, amax_out, scale_out, scale_inv_out, stream=None) -> None:
+    _bf16(x, "x", tuple(x.shape))
+    _codes(q_out, "q_out", tuple(x.shape))
+    for t, n in ((amax_out, "amax_out"), (scale_out, "scale_out"), (scale_inv_out, "scale_inv_out")):
+        _scalar_f32(t, n)
+    _check("te_fp8_cast_current_scaling_noalloc", _lib.te_fp8_cast_current_scaling_noalloc(
+        _ptr(x), x.numel(), _fmt(fmt), _ptr(q_out), _ptr(amax_out), _ptr(scale_out), _ptr(scale_inv_out),
+        _stream(stream)))
+
+
 def te_fp8_cast_delayed_scaling(x, fmt, q_out, q_scale_inv_out, scale, amax_history, workspace, algo="max",
                                 margin=0, stream=None) -> None:
     a = AMAX_ALGOS[algo] if isinstance(algo, str) else int(algo)
@@ -249,10 +260,11 @@ def te_mxfp8_quantize_bgrad(x, fmt, q_row, s_row, q_col, s_col, bgrad, workspace
     _require(x.dim() == 2, "x must be 2-D")
     rows, cols = x.shape
     _bf16(x, "x", (rows, cols))
-    _codes(q_row, "q_row", (rows, cols))
-    _codes(s_row, "s_row", (rows, cols // 32))
-    _codes(q_col, "q_col", (cols, rows))
-    _codes(s_col, "s_col", (cols, rows // 32))
+    empty = rows == 0  # no codes to write: the outputs may be None
+    _codes(q_row, "q_row", (rows, cols), optional=empty)
+    _codes(s_row, "s_row", (rows, cols // 32), optional=empty)
+    _codes(q_col, "q_col", (cols, rows), optional=empty)
+    _codes(s_col, "s_col", (cols, rows // 32), optional=empty)
     _check_tensor(bgrad, "bgrad", (cols,), {torch.float32, torch.bfloat16}, "float32 or bfloat16")
     b_dtype = TE_FP32 if bgrad.dtype == torch.float32 else TE_BF16
     ws_bytes = _ws_bytes(workspace)

@@ -32,7 +32,7 @@ def test_graph_replays_equal_eager_results():
     total = sum(counts)
     xg = dev(workloads.normal_bf16(80, 3, (total, K), 1.0))
     wg = dev(workloads.normal_bf16(80, 4, (G * N, K), 0.05))
-    gbias = dev(workloads.normal_bf16(80, 5, (G * N,), 0.5))
+    gbias = dev(workloads.normal_bf16(80, 5, (G, N), 0.5))
     u8 = dict(dtype=torch.uint8, device="cuda")
     bf = dict(dtype=torch.bfloat16, device="cuda")
     f32 = dict(dtype=torch.float32, device="cuda")
