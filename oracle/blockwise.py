@@ -84,8 +84,9 @@ def quantize_2d(x_bf16, fmt: FP8Format):
 
 
 def block_gemm(qa, sa_inv, fmt_a: FP8Format, qb, sb_inv, fmt_b: FP8Format, b_2d: bool,
-               bias_bf16=None, epi: str = "none", aux_in=None, c_in=None):
-    """D = epilogue(sum_kb sa[m, kb] sb[n(, /128), kb] A_q[m, kb] . B_q[n, kb]).
+               bias_bf16=None, epi: str = "none", aux_in=None, c_in=None, beta: float = 1.0):
+    """D = epilogue(sum_kb sa[m, kb] sb[n(, /128), kb] A_q[m, kb] . B_q[n, kb]); with the accumulate
+    epilogue D = beta C + that sum.
 
     Returns (D, aux, S) with S = sum_k |sa A_q| |sb B_q| (the tolerance weight).
     """
@@ -101,7 +102,7 @@ def block_gemm(qa, sa_inv, fmt_a: FP8Format, qb, sb_inv, fmt_b: FP8Format, b_2d:
     b_hat = b * np.repeat(sb, BLOCK, axis=1)
     y = np.matmul(a_hat, b_hat.T)
     s = np.matmul(np.abs(a_hat), np.abs(b_hat).T)
-    d, aux = epilogue(y, bias_bf16, epi, aux_in, c_in)
+    d, aux = epilogue(y, bias_bf16, epi, aux_in, c_in, beta)
     return d, aux, s
 
 

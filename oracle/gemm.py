@@ -26,7 +26,9 @@ definition written out, in float64):
     it by GELU's derivative at the saved pre-activation aux (bf16 [M, N]):
     D = Y * gelu_tanh'(aux).  That is the gradient of the pre-activation.
   - accumulate: the weight-gradient GEMM adds into an existing fp32 main
-    gradient C [M, N]: D = C + Y (beta = 1).
+    gradient C [M, N]: D = beta C + Y, beta = 1 unless given ("Transformer
+    Engine On ROCm and AMDGPU", "Blockwise FP8 GEMM support on ROCm (gfx942
+    and gfx950)", lists beta among the blockwise GEMM's epilogues).
 * gelu_tanh(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) (the
   tanh approximation of Hendrycks and Gimpel, "Gaussian Error Linear
   Units", 2016; the pages only name the tanh approximation).
@@ -79,11 +81,11 @@ def dgelu_tanh(x) -> np.ndarray:
     return s + 2.0 * x * s * (1.0 - s) * du
 
 
-def epilogue(y, bias_bf16, epi: str, aux_in=None, c_in=None):
+def epilogue(y, bias_bf16, epi: str, aux_in=None, c_in=None, beta: float = 1.0):
     """Apply an epilogue to float64 GEMM results y [M, N].
 
     aux_in: bf16 bit patterns [M, N] of the saved pre-activation (dgelu only);
-    c_in: the fp32 values [M, N] accumulated into (accumulate only).
+    c_in: the fp32 values [M, N] accumulated into, times beta (accumulate only).
     Returns (D, aux) as float64; aux is None unless epi == "bias_gelu_aux".
     """
     if epi not in EPILOGUES:
@@ -93,7 +95,7 @@ def epilogue(y, bias_bf16, epi: str, aux_in=None, c_in=None):
     if epi == "dgelu":
         return y * dgelu_tanh(bf16_to_float64(np.asarray(aux_in))), None
     if epi == "accumulate":
-        return np.asarray(c_in, dtype=np.float64) + y, None
+        return float(beta) * np.asarray(c_in, dtype=np.float64) + y, None
     b = bf16_to_float64(np.asarray(bias_bf16))
     pre = y + b[None, :]
     if epi == "bias":

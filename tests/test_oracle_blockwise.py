@@ -118,3 +118,17 @@ def test_block_gemm_brute_force_fp32_scales_and_orientation():
                         sum(Fraction(float(va[m, k])) * Fraction(float(vb[n, k])) for k in range(kb * 128, (kb + 1) * 128))
                         for kb in range(2))
             assert abs(Fraction(float(d[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 48)
+
+
+def test_block_gemm_accumulate_beta_hand_case():
+    # one-hot operands pick single products: Y = [[0, 1, 0], [0, 0, 2]]; D = beta C + Y, worked by hand
+    qa = np.zeros((2, 128), np.uint8); qa[0, 3] = 0x38; qa[1, 70] = 0x40   # 1.0, 2.0 (E4M3)
+    qb = np.zeros((3, 128), np.uint8); qb[1, 3] = 0x38; qb[2, 70] = 0x38
+    sa, sb = np.ones((2, 1), np.float32), np.ones((3, 1), np.float32)
+    c = np.array([[0, 1, 2], [3, 4, 5]], np.float32)
+    d, _, _ = block_gemm(qa, sa, E4M3, qb, sb, E4M3, False, epi="accumulate", c_in=c, beta=-0.5)
+    assert np.array_equal(d, [[0.0, 0.5, -1.0], [-1.5, -2.0, -0.5]])
+    d, _, _ = block_gemm(qa, sa, E4M3, qb, sb, E4M3, False, epi="accumulate", c_in=c, beta=0.0)
+    assert np.array_equal(d, [[0.0, 1.0, 0.0], [0.0, 0.0, 2.0]])
+    d, _, _ = block_gemm(qa, sa, E4M3, qb, sb, E4M3, False, epi="accumulate", c_in=c)   # beta defaults to 1
+    assert np.array_equal(d, [[0.0, 2.0, 2.0], [3.0, 4.0, 7.0]])
