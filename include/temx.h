@@ -82,7 +82,7 @@ typedef enum {
   TE_ERR_ARCH = 8        /* the current device is not a gfx950 (the kernels are built for it only) */
 } te_status;
 
-typedef enum { TE_BF16 = 0, TE_FP32 = 1, TE_E4M3 = 2, TE_E5M2 = 3, TE_E8M0 = 4 } te_dtype;
+typedef enum { TE_BF16 = 0, TE_FP32 = 1, TE_E4M3 = 2, TE_E5M2 = 3, TE_E8M0 = 4, TE_FP16 = 5 } te_dtype;
 
 typedef enum {
   TE_EPI_NONE = 0,
@@ -369,7 +369,13 @@ te_status te_fp8_block_scales_to_mx(const float* scale_inv, int64_t rows, int64_
  *                TE_BLOCK_SCALES_FP32: each K block's product is computed
  *                with unit scales and added to the fp32 accumulator times
  *                fl32(sa * sb) with one fused multiply-add; no workspace.
- *   d, d_dtype, epi, bias, aux: as te_mxfp8_gemm (every epilogue).
+ *   d, d_dtype, epi, bias, aux: as te_mxfp8_gemm (every epilogue), and D
+ *                may also be TE_FP16 (IEEE half, round to nearest even; beyond
+ *                the half range it becomes +-inf) for every epilogue but
+ *                TE_EPI_ACCUMULATE (fp32 D).
+ *   beta         TE_EPI_ACCUMULATE: D = fl32(beta * D + acc) with one
+ *                rounding (a fused multiply-add; beta = 1 gives D += acc, as
+ *                in te_mxfp8_gemm).  Ignored by the other epilogues.
  *   Shapes as te_mxfp8_gemm: K % 128 == 0, M % 16 == 0, N % 16 == 0.
  *   Scale pointers are 4-byte aligned and may be NULL when M, N or K is 0.
  *   workspace    none is needed (te_fp8_block_gemm_workspace_size returns
@@ -380,7 +386,7 @@ te_status te_fp8_block_gemm(const uint8_t* a, const float* a_scale_inv, te_dtype
                             const uint8_t* b, const float* b_scale_inv, te_dtype b_fmt, int b_block_2d,
                             int64_t M, int64_t N, int64_t K,
                             void* d, te_dtype d_dtype, te_epilogue epi,
-                            const uint16_t* bias, uint16_t* aux, te_block_scaling mode,
+                            const uint16_t* bias, uint16_t* aux, te_block_scaling mode, float beta,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -22,7 +22,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 # enum values of include/temx.h
 TE_OK, TE_ERR_NULL, TE_ERR_SHAPE, TE_ERR_ALIGN, TE_ERR_DTYPE, TE_ERR_WORKSPACE, TE_ERR_HIP, TE_ERR_VALUE, TE_ERR_ARCH = range(9)
-TE_BF16, TE_FP32, TE_E4M3, TE_E5M2, TE_E8M0 = range(5)
+TE_BF16, TE_FP32, TE_E4M3, TE_E5M2, TE_E8M0, TE_FP16 = range(6)
 TE_EPI_NONE, TE_EPI_BIAS, TE_EPI_BIAS_GELU_AUX, TE_EPI_DGELU, TE_EPI_ACCUMULATE = range(5)
 TE_ROWWISE, TE_COLWISE, TE_BOTH = 1, 2, 3
 TE_AMAX_MAX, TE_AMAX_MOST_RECENT = 0, 1
@@ -61,8 +61,8 @@ _SIGS = {
     "te_fp8_block_scales_to_mx": (ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp]),
     "te_fp8_block_gemm_workspace_size": (_sz, [_i64, _i64, _i64, ctypes.c_int]),
     "te_fp8_block_gemm": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, ctypes.c_int, _i64, _i64,
-                                         _i64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _sz,
-                                         _vp]),
+                                         _i64, _vp, ctypes.c_int, ctypes.c_int, _vp, _vp, ctypes.c_int, ctypes.c_float,
+                                         _vp, _sz, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -150,13 +150,19 @@ def _scalar_f32(t, name):
     _require(t is not None and t.dtype == torch.float32 and t.numel() >= 1, f"{name}: expected a float32 scalar")
 
 
-def _gemm_out(d, name, M, N, epi):
-    """D of the bf16/fp32-output GEMMs: [M, N] bf16 or float32; "accumulate" needs float32."""
-    _require(d is not None and d.dtype in (torch.bfloat16, torch.float32),
-             f"{name}: expected bfloat16 or float32, got {None if d is None else d.dtype}")
+_OUT_DTYPES = {torch.bfloat16: TE_BF16, torch.float32: TE_FP32, torch.float16: TE_FP16}
+
+
+def _gemm_out(d, name, M, N, epi, allow_fp16=False):
+    """D of the bf16/fp32-output GEMMs: [M, N] bf16 or float32 (float16 too where allowed); "accumulate"
+    needs float32."""
+    kinds = (torch.bfloat16, torch.float32) + ((torch.float16,) if allow_fp16 else ())
+    _require(d is not None and d.dtype in kinds,
+             f"{name}: expected {' or '.join(str(k).replace('torch.', '') for k in kinds)}, "
+             f"got {None if d is None else d.dtype}")
     _require(epi != TE_EPI_ACCUMULATE or d.dtype == torch.float32, f"{name}: the accumulate epilogue needs float32")
     _require(tuple(d.shape) == (M, N), f"{name}: expected shape {(M, N)}, got {tuple(d.shape)}")
-    return TE_BF16 if d.dtype == torch.bfloat16 else TE_FP32
+    return _OUT_DTYPES[d.dtype]
 
 
 def _epi_tensors(bias, bias_shape, aux, M, N):
@@ -361,7 +367,7 @@ def te_fp8_block_gemm_workspace_size(M: int, N: int, K: int, mode="e8m0") -> int
 
 
 def te_fp8_block_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, b_block_2d, d, epilogue="none", bias=None,
-                      aux=None, mode="e8m0", workspace=None, stream=None) -> None:
+                      aux=None, mode="e8m0", workspace=None, stream=None, beta=1.0) -> None:
     _require(a.dim() == 2 and b.dim() == 2, "a and b must be 2-D")
     M, K = a.shape
     N = b.shape[0]
@@ -370,13 +376,13 @@ def te_fp8_block_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, b_block_2d, 
     _f32(a_scale_inv, "a_scale_inv", _block_scale_shape(M, K, False))
     _f32(b_scale_inv, "b_scale_inv", _block_scale_shape(N, K, b_block_2d))
     epi = _epilogue(epilogue)
-    d_dtype = _gemm_out(d, "d", M, N, epi)
+    d_dtype = _gemm_out(d, "d", M, N, epi, allow_fp16=True)
     _epi_tensors(bias, (N,), aux, M, N)
     ws_bytes = _ws_bytes(workspace)
     _check("te_fp8_block_gemm", _lib.te_fp8_block_gemm(
         _ptr(a), _ptr(a_scale_inv), _fmt(a_fmt), _ptr(b), _ptr(b_scale_inv), _fmt(b_fmt), int(bool(b_block_2d)),
-        M, N, K, _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _block_scaling(mode), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        M, N, K, _ptr(d), d_dtype, epi, _ptr(bias), _ptr(aux), _block_scaling(mode), float(beta), _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 # ------------------------------------------------------- allocating helpers
@@ -512,9 +518,10 @@ def fp8_block_scales_to_mx(scale_inv, rows: int, cols: int, block_2d: bool, stre
 
 
 def fp8_block_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, b_block_2d=True, epilogue="none", bias=None,
-                   out_dtype=torch.bfloat16, aux=None, out=None, mode="e8m0", workspace=None, stream=None):
+                   out_dtype=torch.bfloat16, aux=None, out=None, mode="e8m0", workspace=None, stream=None, beta=1.0):
     """Blockwise FP8 GEMM -> (D, aux); scale inverses float [M, K/128] for A and [N, K/128] (1-D) or
-    [ceil(N/128), K/128] (2-D) for B; mode "e8m0" (scales cast to powers of two) or "fp32"."""
+    [ceil(N/128), K/128] (2-D) for B; mode "e8m0" (scales cast to powers of two) or "fp32"; D bf16, fp16
+    or fp32; "accumulate" adds into the fp32 ``out`` scaled by ``beta``."""
     M, K = a.shape
     N = b.shape[0]
     d = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=a.device)
@@ -524,5 +531,5 @@ def fp8_block_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, b_block_2d=True
         ws_bytes = te_fp8_block_gemm_workspace_size(M, N, K, mode)
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=a.device) if ws_bytes else None
     te_fp8_block_gemm(a, a_scale_inv, a_fmt, b, b_scale_inv, b_fmt, b_block_2d, d, epilogue, bias, aux, mode,
-                      workspace, stream)
+                      workspace, stream, beta)
     return d, (aux if epilogue == "bias_gelu_aux" else None)

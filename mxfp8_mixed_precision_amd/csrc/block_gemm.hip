@@ -17,7 +17,9 @@
 //   on the cast scales.
 // * TE_BLOCK_SCALES_FP32 (SM_FS1 / SM_FS2): each block's product is computed
 //   with unit scales and added to the accumulators times sa * sb.
-// No workspace either way.
+// No workspace either way.  The same section lists fp16 output and a beta
+// epilogue among the blockwise GEMM's options: D may be fp16, and the
+// accumulate epilogue scales the fp32 D it adds to by beta.
 #include "gemm_core.h"
 
 using namespace temx;
@@ -28,7 +30,7 @@ extern "C" te_status te_fp8_block_gemm(const uint8_t* a, const float* a_scale_in
                                        const uint8_t* b, const float* b_scale_inv, te_dtype b_fmt, int b_block_2d,
                                        int64_t M, int64_t N, int64_t K, void* d, te_dtype d_dtype,
                                        te_epilogue epi, const uint16_t* bias, uint16_t* aux,
-                                       te_block_scaling mode, void* workspace, size_t workspace_bytes,
+                                       te_block_scaling mode, float beta, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream) {
   TE_REQUIRE(mode == TE_BLOCK_SCALES_E8M0 || mode == TE_BLOCK_SCALES_FP32, TE_ERR_VALUE);
   TE_REQUIRE(b_block_2d == 0 || b_block_2d == 1, TE_ERR_VALUE);
@@ -40,10 +42,12 @@ extern "C" te_status te_fp8_block_gemm(const uint8_t* a, const float* a_scale_in
   const uint8_t* sa = reinterpret_cast<const uint8_t*>(a_scale_inv);
   const uint8_t* sb = reinterpret_cast<const uint8_t*>(b_scale_inv);
   // the scale arrays stand in for the E8M0 ones in the common checks (non-NULL, 4-byte aligned when read)
-  te_status st = check_common(a, sa, a_fmt, b, sb, b_fmt, d, d_dtype, epi, bias, aux, M > 0 && N > 0, K > 0);
+  te_status st =
+      check_common(a, sa, a_fmt, b, sb, b_fmt, d, d_dtype, epi, bias, aux, M > 0 && N > 0, K > 0, /*allow_fp16=*/true);
   if (st != TE_OK) return st;
   if (M == 0 || N == 0) return TE_OK;
   TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   auto launch = mode == TE_BLOCK_SCALES_E8M0 ? launch_block_gemm_e8m0 : launch_block_gemm_fp32;
-  return launch(a, a_scale_inv, b, b_scale_inv, b_block_2d, M, N, K, d, d_dtype, epi, bias, aux, a_fmt, b_fmt, stream);
+  return launch(a, a_scale_inv, b, b_scale_inv, b_block_2d, M, N, K, d, d_dtype, epi, bias, aux, beta, a_fmt, b_fmt,
+                stream);
 }

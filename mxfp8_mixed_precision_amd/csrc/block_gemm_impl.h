@@ -16,8 +16,9 @@ te_status launch_fs5(const GemmParams& p, dim3 grid, hipStream_t stream) {
 
 template <class C, int FA, int FB, int EPI, int SM>
 te_status launch_fs4(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stream) {
-  return out == TE_BF16 ? launch_fs5<C, FA, FB, EPI, TE_BF16, SM>(p, grid, stream)
-                        : launch_fs5<C, FA, FB, EPI, TE_FP32, SM>(p, grid, stream);
+  if (out == TE_BF16) return launch_fs5<C, FA, FB, EPI, TE_BF16, SM>(p, grid, stream);
+  if (out == TE_FP16) return launch_fs5<C, FA, FB, EPI, TE_FP16, SM>(p, grid, stream);
+  return launch_fs5<C, FA, FB, EPI, TE_FP32, SM>(p, grid, stream);
 }
 
 template <class C, int FA, int FB, int SM>
@@ -43,9 +44,11 @@ te_status launch_fs2(const GemmParams& p, te_dtype fa, te_dtype fb, te_epilogue 
 template <int SM1, int SM2>
 te_status launch_block_modes(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int b2d,
                              int64_t M, int64_t N, int64_t K, void* d, te_dtype d_dtype, te_epilogue epi,
-                             const uint16_t* bias, uint16_t* aux, te_dtype fa, te_dtype fb, hipStream_t stream) {
+                             const uint16_t* bias, uint16_t* aux, float beta, te_dtype fa, te_dtype fb,
+                             hipStream_t stream) {
   GemmParams p{a, reinterpret_cast<const uint8_t*>(sa), b, reinterpret_cast<const uint8_t*>(sb), d, bias, aux,
                M, N, K, nullptr, 0};
+  p.beta = beta;
   const Tile t = pick_tile(M, N, K);
   const dim3 grid = tile_grid(t, M, N);
   if (t == Tile::SmallDeep)

@@ -496,7 +496,7 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
 template <class LY, int EPI, int OUT>
 __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], void* d, uint16_t* aux,
                                          const uint16_t* bias, int64_t m0, int64_t m_end, int64_t n0, int64_t N,
-                                         int wave, int lane) {
+                                         int wave, int lane, float beta = 1.0f) {
   const int wm = wave / LY::NWN, wn = wave % LY::NWN;
   const int g = lane >> 4, r = lane & 15;
   // bias of the lane's columns, all fragments
@@ -545,16 +545,19 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], voi
         v2 *= dgelu_tanh(bf16_bits_to_float(pa.y & 0xFFFFu));
         v3 *= dgelu_tanh(bf16_bits_to_float(pa.y >> 16));
       }
-      if constexpr (EPI == TE_EPI_ACCUMULATE) {  // fp32 D is read and added to
+      if constexpr (EPI == TE_EPI_ACCUMULATE) {  // fp32 D is read, scaled by beta and added to (one rounding)
         const float4 c = *reinterpret_cast<const float4*>(static_cast<float*>(d) + m * N + n);
-        v0 = c.x + v0;
-        v1 = c.y + v1;
-        v2 = c.z + v2;
-        v3 = c.w + v3;
+        v0 = __builtin_fmaf(beta, c.x, v0);
+        v1 = __builtin_fmaf(beta, c.y, v1);
+        v2 = __builtin_fmaf(beta, c.z, v2);
+        v3 = __builtin_fmaf(beta, c.w, v3);
       }
       if constexpr (OUT == TE_BF16) {
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(d) + m * N + n) =
             make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+      } else if constexpr (OUT == TE_FP16) {
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(d) + m * N + n) =
+            make_uint2(pack_f16x2(v0, v1), pack_f16x2(v2, v3));
       } else {
         *reinterpret_cast<float4*>(static_cast<float*>(d) + m * N + n) = make_float4(v0, v1, v2, v3);
       }
@@ -658,6 +661,7 @@ struct GemmParams {
   uint8_t* d_scale;         // MXFP8 output only: E8M0 scales [M, N/32]
   const float* alpha_a;     // per-tensor FP8 only: a_scale_inv and b_scale_inv (device scalars)
   const float* alpha_b;
+  float beta = 1.0f;        // accumulate epilogue: D = fl32(beta D + acc)
 };
 
 // Dense: one workgroup per tile, operands scaled as SM says (SM_PT: the
@@ -703,7 +707,7 @@ __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
     epilogue_mx<LY, EPI, OUT>(acc, static_cast<uint8_t*>(p.d), p.d_scale, p.aux, p.bias, m0, p.M, n0, p.N, wave,
                               lane);
   else
-    epilogue<LY, EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
+    epilogue<LY, EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane, p.beta);
 }
 
 // Grouped: a persistent grid walks the flat list of (expert row-tile,
@@ -800,13 +804,13 @@ inline bool dense_shape_ok(int64_t M, int64_t N, int64_t K) {
 
 inline te_status check_common(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,
                        const uint8_t* b_scale, te_dtype b_fmt, void* d, te_dtype d_dtype, te_epilogue epi,
-                       const uint16_t* bias, uint16_t* aux, bool any_rows, bool any_k) {
+                       const uint16_t* bias, uint16_t* aux, bool any_rows, bool any_k, bool allow_fp16 = false) {
   TE_REQUIRE(epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX || epi == TE_EPI_DGELU ||
                  epi == TE_EPI_ACCUMULATE,
              TE_ERR_VALUE);
   TE_REQUIRE(is_fp8(a_fmt) && is_fp8(b_fmt), TE_ERR_DTYPE);
   TE_REQUIRE(!(a_fmt == TE_E5M2 && b_fmt == TE_E5M2), TE_ERR_DTYPE);
-  TE_REQUIRE(d_dtype == TE_BF16 || d_dtype == TE_FP32, TE_ERR_DTYPE);
+  TE_REQUIRE(d_dtype == TE_BF16 || d_dtype == TE_FP32 || (allow_fp16 && d_dtype == TE_FP16), TE_ERR_DTYPE);
   TE_REQUIRE(epi != TE_EPI_ACCUMULATE || d_dtype == TE_FP32, TE_ERR_DTYPE);
   TE_REQUIRE((epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX) == (bias != nullptr), TE_ERR_NULL);
   TE_REQUIRE((epi == TE_EPI_BIAS_GELU_AUX || epi == TE_EPI_DGELU) == (aux != nullptr), TE_ERR_NULL);

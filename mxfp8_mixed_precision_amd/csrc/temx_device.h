@@ -140,6 +140,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
 
+// Round-to-nearest-even fp32 -> IEEE half of two values, packed (lo = a);
+// magnitudes beyond the half range become +-inf.
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  v2h r = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // GELU, tanh form: 0.5 x (1 + tanh(u)) with u = sqrt(2/pi) (x + 0.044715 x^3),
 // evaluated as x / (1 + 2^(-2 u log2 e)) (the same function; no cancellation
 // for negative x).

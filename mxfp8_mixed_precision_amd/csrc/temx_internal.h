@@ -28,10 +28,12 @@ bool device_is_gfx950();
 // block_gemm_fp32.hip), after te_fp8_block_gemm has checked the arguments.
 te_status launch_block_gemm_e8m0(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int b2d,
                                  int64_t M, int64_t N, int64_t K, void* d, te_dtype d_dtype, te_epilogue epi,
-                                 const uint16_t* bias, uint16_t* aux, te_dtype fa, te_dtype fb, hipStream_t stream);
+                                 const uint16_t* bias, uint16_t* aux, float beta, te_dtype fa, te_dtype fb,
+                                 hipStream_t stream);
 te_status launch_block_gemm_fp32(const uint8_t* a, const float* sa, const uint8_t* b, const float* sb, int b2d,
                                  int64_t M, int64_t N, int64_t K, void* d, te_dtype d_dtype, te_epilogue epi,
-                                 const uint16_t* bias, uint16_t* aux, te_dtype fa, te_dtype fb, hipStream_t stream);
+                                 const uint16_t* bias, uint16_t* aux, float beta, te_dtype fa, te_dtype fb,
+                                 hipStream_t stream);
 
 }  // namespace temx
 

@@ -55,8 +55,12 @@ STATED_MISS_CEILING: dict = {
     "big_ragged:4144x4176x256:bias_gelu_aux:D": 5,  # 2 of 5550
     "big_ragged:4144x4176x256:bias_gelu_aux:aux": 10,  # 7 of 5550
     "big_ragged:4144x4176x256:none:D": 5,  # 2 of 5550
+    "block_beta:e8m0": 8,  # 5 of 335872
+    "block_beta:fp32": 8,  # 5 of 335872
     "block_epilogue:e8m0:bias": 10,  # 7 of 211200
     "block_epilogue:fp32:bias": 10,  # 7 of 211200
+    "block_fp16:e8m0:bias": 6,  # 3 of 211200
+    "block_fp16:fp32:bias": 6,  # 3 of 211200
     "block_nonpow2:1d:e8m0:none": 8,  # 5 of 153600
     "block_nonpow2:1d:fp32:none": 6,  # 3 of 153600
     "block_nonpow2:2d:e8m0:none": 8,  # 5 of 153600

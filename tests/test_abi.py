@@ -124,6 +124,7 @@ def test_gemm_validation():
     assert gemm(fa=te.TE_E5M2, fb=te.TE_E5M2) == te.TE_ERR_DTYPE
     assert gemm(fa=te.TE_BF16) == te.TE_ERR_DTYPE
     assert gemm(dt=te.TE_E4M3) == te.TE_ERR_DTYPE
+    assert gemm(dt=te.TE_FP16) == te.TE_ERR_DTYPE                          # fp16 D: the blockwise GEMM only
     assert gemm(epi=6) == te.TE_ERR_VALUE
     assert gemm(epi=te.TE_EPI_BIAS) == te.TE_ERR_NULL                       # bias missing
     assert gemm(bias=P3) == te.TE_ERR_NULL                                  # bias without epilogue
@@ -211,10 +212,11 @@ def test_fp8_gemm_validation():
 
 def blockgemm(a=P, sa=P3, fa=te.TE_E4M3, b=P, sb=P3, fb=te.TE_E4M3, b2d=1, M=256, N=256, K=256, d=P2,
               dt=te.TE_BF16, epi=te.TE_EPI_NONE, bias=None, aux=None, mode=te.TE_BLOCK_SCALES_E8M0, ws=None,
-              ws_bytes=None):
+              ws_bytes=None, beta=1.0):
     if ws_bytes is None:
         ws_bytes = te.te_fp8_block_gemm_workspace_size(M, N, K, mode)
-    return L.te_fp8_block_gemm(a, sa, fa, b, sb, fb, b2d, M, N, K, d, dt, epi, bias, aux, mode, ws, ws_bytes, None)
+    return L.te_fp8_block_gemm(a, sa, fa, b, sb, fb, b2d, M, N, K, d, dt, epi, bias, aux, mode, beta, ws, ws_bytes,
+                               None)
 
 
 def test_block_gemm_workspace_and_validation():
@@ -228,6 +230,8 @@ def test_block_gemm_workspace_and_validation():
         assert blockgemm(mode=mode, fa=te.TE_E5M2, fb=te.TE_E5M2) == te.TE_ERR_DTYPE
         assert blockgemm(mode=mode, dt=te.TE_E4M3) == te.TE_ERR_DTYPE
         assert blockgemm(mode=mode, epi=te.TE_EPI_ACCUMULATE) == te.TE_ERR_DTYPE
+        assert blockgemm(mode=mode, epi=te.TE_EPI_ACCUMULATE, dt=te.TE_FP16) == te.TE_ERR_DTYPE   # fp32 D only
+        assert blockgemm(mode=mode, dt=te.TE_FP16, a=BAD) == te.TE_ERR_ALIGN   # fp16 D passes the dtype check
         assert blockgemm(mode=mode, epi=te.TE_EPI_BIAS) == te.TE_ERR_NULL
         assert blockgemm(mode=mode, epi=te.TE_EPI_DGELU) == te.TE_ERR_NULL
         assert blockgemm(mode=mode, sa=None) == te.TE_ERR_NULL
@@ -421,3 +425,4 @@ def test_valid_call_without_a_gfx950_returns_arch_error():
                            None, None, None, 0, None) == te.TE_ERR_ARCH
     # the checks before it still come first
     assert quant(x=BAD) == te.TE_ERR_ALIGN
+

@@ -22,6 +22,12 @@ FP32 block scales to MXFP8 E8M0 scales, against the CPU oracle.
   recipe data against the oracle's epilogue within the GEMM bound (GELU
   outputs with the GELU slope), aux bit-identical to the bias epilogue's D.
 * The bench workload's GEMM at full size, sampled rows x columns.
+* fp16 D: exact-integer data bit-exact against the half rounding of the
+  oracle's result (both tiles), overflow to infinity past the half range,
+  and the bias / GELU-aux epilogues on recipe data within the GEMM bound.
+* beta: the accumulate epilogue D = fl32(beta C + acc), bit-exact against
+  the oracle's beta C + Y on exact data for beta = -0.75, 0 and 2, and
+  within the GEMM bound on recipe data for beta = 0.3.
 """
 
 import numpy as np
@@ -92,10 +98,11 @@ def b_scale_shape(N, K, b_2d):
     return (-(-N // 128) if b_2d else N, K // 128)
 
 
-def run(mode, qa, sa, fa, qb, sb, fb, b_2d, epi="none", bias=None, out_dtype=torch.float32, aux=None, out=None):
+def run(mode, qa, sa, fa, qb, sb, fb, b_2d, epi="none", bias=None, out_dtype=torch.float32, aux=None, out=None,
+        beta=1.0):
     d, aux_out = te().fp8_block_gemm(dev(qa), dev(sa), fa, dev(qb), dev(sb), fb, b_2d, epi,
                                      None if bias is None else dev(bias), out_dtype,
-                                     None if aux is None else dev(aux), out, mode)
+                                     None if aux is None else dev(aux), out, mode, beta=beta)
     torch.cuda.synchronize()
     return d, aux_out
 
@@ -284,3 +291,107 @@ def test_block_gemm_forward_epilogues_vs_oracle(mode, epi):
         # aux is the bf16 pre-activation: the bias epilogue's D for the same inputs, bit for bit
         d_bias, _ = run(mode, qa, sa, "e4m3", qb, sb, "e4m3", True, "bias", bias, torch.bfloat16)
         assert torch.equal(aux, d_bias)
+
+
+# ------------------------------------------------------------ fp16 output and beta
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("b_2d", [False, True])
+@pytest.mark.parametrize("M,N,K", [(272, 304, 384), (8192, 4112, 512)])
+def test_block_gemm_fp16_output_exact(mode, b_2d, M, N, K):
+    """Exact-integer data: every fp32 accumulator is exact, so the fp16 D must be the round-to-nearest-even
+    half of the oracle's result, bit for bit (both tiles; sampled tile-boundary rows on the big one)."""
+    rng = np.random.default_rng([M, N, K, b_2d, 16])
+    qa, qb = exact_codes(rng, (M, K), "e4m3"), exact_codes(rng, (N, K), "e5m2")
+    sa, sb = exact_scales(rng, (M, K // 128)), exact_scales(rng, b_scale_shape(N, K, b_2d))
+    d, _ = run(mode, qa, sa, "e4m3", qb, sb, "e5m2", b_2d, out_dtype=torch.float16)
+    sa_ref, sb_ref = (oracle.pow2_at_least(sa), oracle.pow2_at_least(sb)) if mode == "e8m0" else (sa, sb)
+    rows = np.arange(M)
+    if M > 2048:
+        rows = np.array(sorted({0, M - 1} | {256 * t + o for t in range(M // 256) for o in (0, 255)}))
+    ref, _, _ = oracle.block_gemm(qa[rows], sa_ref[rows], oracle.E4M3, qb, sb_ref, oracle.E5M2, b_2d)
+    assert np.array_equal(ref.astype(np.float32).astype(np.float64), ref)   # exact in fp32
+    got = d[rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ref.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_block_gemm_fp16_output_overflows_to_inf(mode):
+    """Outputs beyond the half range become +-inf (scales of 2^9 make |D| reach ~2^17); the rest round as usual."""
+    M, N, K = 272, 304, 384
+    rng = np.random.default_rng(17)
+    # non-negative codes on A, so the sums grow; rows alternate between scales 2^9 (overflow) and 2^-4
+    qa, qb = exact_codes(rng, (M, K), "e4m3") & 0x7F, exact_codes(rng, (N, K), "e4m3")
+    qb[: N // 2] &= 0x7F
+    sa = np.full((M, K // 128), 512.0, np.float32)
+    sa[1::2] = 2.0 ** -4
+    sb = np.ones((N, K // 128), np.float32)
+    d, _ = run(mode, qa, sa, "e4m3", qb, sb, "e4m3", False, out_dtype=torch.float16)
+    ref, _, _ = oracle.block_gemm(qa, sa, oracle.E4M3, qb, sb, oracle.E4M3, False)
+    with np.errstate(over="ignore"):
+        want = ref.astype(np.float16)
+    assert np.isinf(want).any() and np.isfinite(want).any()
+    assert np.array_equal(d.view(torch.int16).cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("epi", ["bias", "bias_gelu_aux"])
+def test_block_gemm_fp16_output_recipe(mode, epi):
+    """Recipe data through the bias and GELU-aux epilogues with fp16 D, against the oracle within the GEMM bound;
+    aux (bf16) equals the bf16-output run's bit for bit."""
+    M, N, K = 400, 528, 2176
+    qa, sa, qb, sb = recipe_operands(M, N, K, True, seed=92)
+    bias = workloads.normal_bf16(92, 5, (N,), 0.5)
+    d, aux = run(mode, qa, sa, "e4m3", qb, sb, "e4m3", True, epi, bias, torch.float16)
+    check_recipe("block_fp16", mode, qa, sa, "e4m3", qb, sb, "e4m3", True, np.arange(M), np.arange(N),
+                 d.float(), bias, epi)
+    if epi == "bias_gelu_aux":
+        _, aux16 = run(mode, qa, sa, "e4m3", qb, sb, "e4m3", True, epi, bias, torch.bfloat16)
+        assert torch.equal(aux, aux16)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("b_2d", [False, True])
+@pytest.mark.parametrize("beta", [-0.75, 0.0, 2.0])
+def test_block_gemm_accumulate_beta_exact(mode, b_2d, beta):
+    """D = fl32(beta C + acc) with one rounding: on exact-integer data (exact accumulators) and C holding
+    small dyadic values, equal bit for bit to the float32 rounding of the oracle's beta C + Y."""
+    M, N, K = 1040, 784, 640
+    rng = np.random.default_rng([M, N, K, b_2d, 7])
+    qa, qb = exact_codes(rng, (M, K), "e4m3"), exact_codes(rng, (N, K), "e5m2")
+    sa, sb = exact_scales(rng, (M, K // 128)), exact_scales(rng, b_scale_shape(N, K, b_2d))
+    c = (rng.integers(-64, 65, size=(M, N)) * 0.25).astype(np.float32)
+    out = dev(c)
+    run(mode, qa, sa, "e4m3", qb, sb, "e5m2", b_2d, "accumulate", out_dtype=torch.float32, out=out, beta=beta)
+    sa_ref, sb_ref = (oracle.pow2_at_least(sa), oracle.pow2_at_least(sb)) if mode == "e8m0" else (sa, sb)
+    ref, _, _ = oracle.block_gemm(qa, sa_ref, oracle.E4M3, qb, sb_ref, oracle.E5M2, b_2d, epi="accumulate", c_in=c,
+                                  beta=beta)
+    assert np.array_equal(host(out), ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_block_gemm_accumulate_beta_recipe(mode):
+    """Recipe data, beta = 0.3, against the oracle's beta C + Y within the GEMM bound on the product."""
+    M, N, K = 512, 656, 2048
+    qa, sa, qb, sb = recipe_operands(M, N, K, True, seed=93)
+    rng = np.random.default_rng(94)
+    c = (rng.standard_normal((M, N)) * 0.5).astype(np.float32)
+    out = dev(c)
+    run(mode, qa, sa, "e4m3", qb, sb, "e4m3", True, "accumulate", out_dtype=torch.float32, out=out, beta=0.3)
+    sa_ref, sb_ref = (oracle.pow2_at_least(sa), oracle.pow2_at_least(sb)) if mode == "e8m0" else (sa, sb)
+    sb_rows = np.repeat(sb_ref, 128, axis=0)[:N]
+    ref, _, s = oracle.block_gemm(qa, sa_ref, oracle.E4M3, qb, sb_rows, oracle.E4M3, False, epi="accumulate",
+                                  c_in=c, beta=0.3)
+    got = host(out).astype(np.float64)
+    y_ref = ref - 0.3 * c.astype(np.float64)
+    ea, eb = e8m0_expanded(sa, M, False), e8m0_expanded(sb, N, True)
+    k_eff = K * 1.25 if mode == "fp32" else K
+    # the product's bound, plus the fp32 rounding of beta C + acc
+    bound = 2.0 ** -8 * np.abs(y_ref) + 1e-5 * s + (k_eff / 16.0) * 2.0 ** -24 * s + 2.0 ** -24 * np.abs(ref)
+    err = np.abs(got - ref)
+    r, cc = np.nonzero(err > bound)
+    if r.size:
+        h = mfma_model.truncation_bound_pairs(qa, ea, oracle.E4M3, qb, eb, oracle.E4M3, r, cc)
+        assert np.all(err[r, cc] <= bound[r, cc] + h)
+    stated = err <= 2.0 ** -8 * np.abs(y_ref) + 1e-5 * s
+    assert_stated_misses(f"block_beta:{mode}", int((~stated).sum()), stated.size)
