@@ -136,6 +136,26 @@ te_status te_fp8_cast_current_scaling(const uint16_t* x, int64_t n, te_dtype fmt
                                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The current-scaling cast above, allocating nothing and taking no
+ * workspace: for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * stage-one partial maxima live in a static device array of the library
+ * (4 KB: at most 1024 partials, one per amax workgroup, which serves every
+ * n the entry point accepts).  Each GPU holds its own copy from the first
+ * call on it until the process ends; its address is looked up on that first
+ * call with the device current.  Arguments, results and errors are those of
+ * te_fp8_cast_current_scaling (minus the workspace); the results are
+ * bit-identical to it.  Calls on one GPU share the array, so calls that
+ * overlap in time on one GPU (different streams, or different host threads)
+ * race and give unspecified results; calls in one stream are ordered and
+ * safe.  Nothing in the array needs clearing between calls: each call
+ * writes every entry it reads.
+ */
+te_status te_fp8_cast_current_scaling_noalloc(const uint16_t* x, int64_t n, te_dtype fmt, uint8_t* q_out,
+                                              float* amax_out, float* scale_out, float* scale_inv_out,
+                                              hipStream_t stream);
+
+/*
  * Delayed-scaling FP8 cast ([TE-JAX] README example and "Enabling
  * Quantization": DelayedScaling with margin, interval, an amax history of
  * length 16 and the "max" algorithm; [FP8-WF] Step 4: a history window of

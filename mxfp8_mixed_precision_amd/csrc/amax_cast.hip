@@ -13,6 +13,9 @@
 // non-NaN bf16), so it does not depend on the reduction order.
 #include <float.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "temx_device.h"
 
 namespace temx {
@@ -270,6 +273,66 @@ te_status launch_amax(const uint16_t* x, int64_t n, uint32_t* partial, int64_t b
   return launch_status();
 }
 
+// The checks both current-scaling entry points share (everything but the
+// partial-maxima buffer).
+te_status check_cast_current(const uint16_t* x, int64_t n, te_dtype fmt, const uint8_t* q_out, const float* amax_out,
+                             const float* scale_out, const float* scale_inv_out) {
+  TE_REQUIRE(is_fp8(fmt), TE_ERR_DTYPE);
+  TE_REQUIRE(n >= 0, TE_ERR_SHAPE);
+  TE_REQUIRE(amax_out != nullptr && scale_out != nullptr && scale_inv_out != nullptr, TE_ERR_NULL);
+  TE_REQUIRE(n == 0 || (x != nullptr && q_out != nullptr), TE_ERR_NULL);
+  TE_REQUIRE(n == 0 || (aligned16(x) && aligned16(q_out)), TE_ERR_ALIGN);
+  TE_REQUIRE(n / 8 / 256 < (int64_t)1 << 31, TE_ERR_SHAPE);
+  return TE_OK;
+}
+
+// Stage one of the amax into `partial` (blocks entries), then the cast with
+// the final reduction folded in.
+te_status launch_cast_current(const uint16_t* x, int64_t n, te_dtype fmt, uint8_t* q_out, float* amax_out,
+                              float* scale_out, float* scale_inv_out, uint32_t* partial, int64_t blocks,
+                              hipStream_t stream) {
+  if (launch_amax(x, n, partial, blocks, stream) != TE_OK) return TE_ERR_HIP;
+  // at least one workgroup, which writes amax, scale and scale_inv (n = 0 included)
+  int64_t grid = (n / 8 + kCastThreads * kCastUnroll - 1) / (kCastThreads * kCastUnroll);
+  if (grid < 1) grid = 1;
+  if (fmt == TE_E4M3)
+    hipLaunchKernelGGL(cast_current_kernel<TE_E4M3>, dim3((unsigned)grid), dim3(kCastThreads), 0, stream, x, n,
+                       partial, (int)blocks, q_out, amax_out, scale_out, scale_inv_out);
+  else
+    hipLaunchKernelGGL(cast_current_kernel<TE_E5M2>, dim3((unsigned)grid), dim3(kCastThreads), 0, stream, x, n,
+                       partial, (int)blocks, q_out, amax_out, scale_out, scale_inv_out);
+  return launch_status();
+}
+
+// Partial maxima of te_fp8_cast_current_scaling_noalloc, for callers that
+// cannot allocate: one uint32 per amax workgroup, at most kAmaxMaxBlocks
+// (4 KB), in static device memory.  Every GPU the library runs on holds its
+// own copy until the process ends; calls on one GPU share it (each call
+// writes every entry it reads, so nothing needs clearing between calls).
+constexpr int64_t kScratchPartials = kAmaxMaxBlocks;
+static __device__ __align__(256) uint32_t scratch[kScratchPartials];
+
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// with that device current (in host code the array's name is only a
+// host-side stand-in).  nullptr if the lookup fails.
+uint32_t* scratch_partials() {
+  static std::atomic<uint32_t*> cache[64];
+  static std::mutex lookup;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  uint32_t* ptr = cache[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  std::lock_guard<std::mutex> guard(lookup);
+  ptr = cache[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return nullptr;
+    ptr = static_cast<uint32_t*>(addr);
+    cache[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
 }  // namespace
 }  // namespace temx
 
@@ -299,29 +362,30 @@ extern "C" te_status te_amax_reduce(const uint16_t* x, int64_t n, float* amax_ou
 extern "C" te_status te_fp8_cast_current_scaling(const uint16_t* x, int64_t n, te_dtype fmt, uint8_t* q_out,
                                                  float* amax_out, float* scale_out, float* scale_inv_out,
                                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  TE_REQUIRE(is_fp8(fmt), TE_ERR_DTYPE);
-  TE_REQUIRE(n >= 0, TE_ERR_SHAPE);
-  TE_REQUIRE(amax_out != nullptr && scale_out != nullptr && scale_inv_out != nullptr && workspace != nullptr,
-             TE_ERR_NULL);
-  TE_REQUIRE(n == 0 || (x != nullptr && q_out != nullptr), TE_ERR_NULL);
-  TE_REQUIRE(n == 0 || (aligned16(x) && aligned16(q_out)), TE_ERR_ALIGN);
+  const te_status st = check_cast_current(x, n, fmt, q_out, amax_out, scale_out, scale_inv_out);
+  if (st != TE_OK) return st;
+  TE_REQUIRE(workspace != nullptr, TE_ERR_NULL);
   TE_REQUIRE(((uintptr_t)workspace & 3u) == 0, TE_ERR_ALIGN);
   const int64_t blocks = amax_blocks(n);
   TE_REQUIRE(workspace_bytes >= (size_t)blocks * sizeof(uint32_t), TE_ERR_WORKSPACE);
-  TE_REQUIRE(n / 8 / 256 < (int64_t)1 << 31, TE_ERR_SHAPE);
-  uint32_t* partial = static_cast<uint32_t*>(workspace);
   TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
-  if (launch_amax(x, n, partial, blocks, stream) != TE_OK) return TE_ERR_HIP;
-  // at least one workgroup, which writes amax, scale and scale_inv (n = 0 included)
-  int64_t grid = (n / 8 + kCastThreads * kCastUnroll - 1) / (kCastThreads * kCastUnroll);
-  if (grid < 1) grid = 1;
-  if (fmt == TE_E4M3)
-    hipLaunchKernelGGL(cast_current_kernel<TE_E4M3>, dim3((unsigned)grid), dim3(kCastThreads), 0, stream, x, n,
-                       partial, (int)blocks, q_out, amax_out, scale_out, scale_inv_out);
-  else
-    hipLaunchKernelGGL(cast_current_kernel<TE_E5M2>, dim3((unsigned)grid), dim3(kCastThreads), 0, stream, x, n,
-                       partial, (int)blocks, q_out, amax_out, scale_out, scale_inv_out);
-  return launch_status();
+  return launch_cast_current(x, n, fmt, q_out, amax_out, scale_out, scale_inv_out, static_cast<uint32_t*>(workspace),
+                             blocks, stream);
+}
+
+extern "C" te_status te_fp8_cast_current_scaling_noalloc(const uint16_t* x, int64_t n, te_dtype fmt, uint8_t* q_out,
+                                                         float* amax_out, float* scale_out, float* scale_inv_out,
+                                                         hipStream_t stream) {
+  const te_status st = check_cast_current(x, n, fmt, q_out, amax_out, scale_out, scale_inv_out);
+  if (st != TE_OK) return st;
+  const int64_t blocks = amax_blocks(n);
+  // the amax grid is capped at kAmaxMaxBlocks workgroups, so every n fits the scratch
+  static_assert(kScratchPartials >= kAmaxMaxBlocks, "one scratch entry per amax workgroup");
+  TE_REQUIRE(blocks <= kScratchPartials, TE_ERR_WORKSPACE);
+  TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
+  uint32_t* partial = scratch_partials();
+  TE_REQUIRE(partial != nullptr, TE_ERR_HIP);
+  return launch_cast_current(x, n, fmt, q_out, amax_out, scale_out, scale_inv_out, partial, blocks, stream);
 }
 
 extern "C" te_status te_fp8_cast_delayed_scaling(const uint16_t* x, int64_t n, te_dtype fmt, uint8_t* q_out,

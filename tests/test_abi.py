@@ -426,3 +426,13 @@ def test_valid_call_without_a_gfx950_returns_arch_error():
     # the checks before it still come first
     assert quant(x=BAD) == te.TE_ERR_ALIGN
 
+
+def test_cast_current_noalloc_validation():
+    cast = L.te_fp8_cast_current_scaling_noalloc
+    assert cast(P, 1024, te.TE_BF16, P2, P3, P3, P3, None) == te.TE_ERR_DTYPE
+    assert cast(P, -1, te.TE_E4M3, P2, P3, P3, P3, None) == te.TE_ERR_SHAPE
+    assert cast(P, 1024, te.TE_E4M3, P2, None, P3, P3, None) == te.TE_ERR_NULL
+    assert cast(None, 1024, te.TE_E4M3, P2, P3, P3, P3, None) == te.TE_ERR_NULL
+    assert cast(P, 1024, te.TE_E4M3, None, P3, P3, P3, None) == te.TE_ERR_NULL
+    assert cast(BAD, 1024, te.TE_E4M3, P2, P3, P3, P3, None) == te.TE_ERR_ALIGN
+    assert cast(P, 1024, te.TE_E4M3, BAD, P3, P3, P3, None) == te.TE_ERR_ALIGN
