@@ -204,7 +204,7 @@ extern "C" te_status te_mxfp8_grouped_gemm(int32_t num_groups, const int32_t* m_
   // rows, counting one ragged tail tile per group (32 experts x ~512 rows x
   // 1536 columns: big tiles 172 us, small 222 us)
   const int64_t big_tiles = (total_m / 256 + num_groups) * ((N + 255) / 256);
-  if (use_small_tile(big_tiles, K))
+  if (use_small_tile(big_tiles))
     return launch2<Small, true>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)(2 * grid)), stream);
   return launch2<Big, true>(p, a_fmt, b_fmt, epi, d_dtype, dim3((unsigned)grid), stream);
 }

@@ -565,6 +565,97 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], voi
   }
 }
 
+// Epilogue of the 2-byte outputs (bf16 / fp16 D, and the bf16 GELU aux)
+// through LDS.  Stored straight from the MFMA layout, a wave store writes 32
+// bytes into each of 16 rows: 16 partial lines per instruction, which left
+// the store path the slowest part of a decoder-sized GEMM.  Here each wave
+// first writes its WTM x WTN block of 2-byte results to a region of LDS of its
+// own (row q at q * 2 WTN bytes, 16-byte chunk c at chunk c ^ (q % CH), CH
+// chunks per row: the 8-byte writes and the 16-byte reads are both free of
+// bank conflicts), then reads it back row-major, 16 bytes per lane, and
+// stores 2 WTN contiguous bytes of each of 64 / CH rows per instruction.
+// The LDS is free once every wave has finished the last step's reads (the
+// barrier below); with the GELU aux the region is used twice, aux first
+// (LDS accesses of one wave complete in issue order).
+template <class LY>
+__device__ __forceinline__ void store_region(const uint8_t* region, uint16_t* out, int64_t mb, int64_t m_end,
+                                             int64_t nb, int64_t N, int lane) {
+  constexpr int RB = LY::WTN * 2, CH = RB / 16;
+#pragma unroll
+  for (int t = 0; t < LY::WTM * CH / 64; ++t) {
+    const int q = (64 * t + lane) / CH, c = (64 * t + lane) % CH;
+    const uint4 v = *reinterpret_cast<const uint4*>(region + q * RB + ((c ^ (q & (CH - 1))) << 4));
+    const int64_t m = mb + q, n = nb + 8 * c;  // N % 16 == 0: a chunk of 8 columns is all in or all out
+    if (m < m_end && n < N) *reinterpret_cast<uint4*>(out + m * N + n) = v;
+  }
+}
+
+constexpr bool staged_epilogue(int epi, int out) {
+  return (out == TE_BF16 || out == TE_FP16) &&
+         (epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX);
+}
+
+template <class LY, int EPI, int OUT>
+__device__ __forceinline__ void epilogue_lds(const v4f (&acc)[LY::FRN][LY::FRM], uint8_t* lds, void* d,
+                                             uint16_t* aux, const uint16_t* bias, int64_t m0, int64_t m_end,
+                                             int64_t n0, int64_t N, int wave, int lane) {
+  static_assert(OUT == TE_BF16 || OUT == TE_FP16, "2-byte outputs");
+  static_assert(EPI == TE_EPI_NONE || EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX, "forward epilogues");
+  constexpr int RB = LY::WTN * 2, CH = RB / 16, kRegion = LY::WTM * RB;
+  static_assert((CH & (CH - 1)) == 0 && CH <= 16 && LY::NW * kRegion <= LY::kLds, "staging layout");
+  const int wm = wave / LY::NWN, wn = wave % LY::NWN;
+  const int g = lane >> 4, r = lane & 15;
+  uint8_t* region = lds + wave * kRegion;
+  const int64_t mb = m0 + wm * LY::WTM, nb = n0 + wn * LY::WTN;
+  float bv[LY::FRN][4];
+#pragma unroll
+  for (int i = 0; i < LY::FRN; ++i) {
+    const int64_t n = nb + 16 * i + 4 * g;
+    bv[i][0] = bv[i][1] = bv[i][2] = bv[i][3] = 0.f;
+    if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
+      if (n < N) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
+        bv[i][0] = bf16_bits_to_float(bb.x & 0xFFFFu);
+        bv[i][1] = bf16_bits_to_float(bb.x >> 16);
+        bv[i][2] = bf16_bits_to_float(bb.y & 0xFFFFu);
+        bv[i][3] = bf16_bits_to_float(bb.y >> 16);
+      }
+    }
+  }
+  __syncthreads();  // every wave's reads of the last stage are done: the LDS is free
+  // lane (g, r) of fragment (i, j): row 16 j + r, 8 bytes at byte 32 i + 8 g = chunk 2 i + g / 2, half g % 2
+  const int wr_off = r * RB + ((g & 1) << 3);
+  constexpr int kPasses = EPI == TE_EPI_BIAS_GELU_AUX ? 2 : 1;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const bool to_aux = kPasses == 2 && pass == 0;
+#pragma unroll
+    for (int j = 0; j < LY::FRM; ++j) {
+#pragma unroll
+      for (int i = 0; i < LY::FRN; ++i) {
+        float v0 = acc[i][j][0] + bv[i][0], v1 = acc[i][j][1] + bv[i][1];
+        float v2 = acc[i][j][2] + bv[i][2], v3 = acc[i][j][3] + bv[i][3];
+        uint2 w;
+        if (EPI == TE_EPI_BIAS_GELU_AUX && !to_aux) {
+          v0 = gelu_tanh(v0);
+          v1 = gelu_tanh(v1);
+          v2 = gelu_tanh(v2);
+          v3 = gelu_tanh(v3);
+        }
+        if (OUT == TE_FP16 && !to_aux)
+          w = make_uint2(pack_f16x2(v0, v1), pack_f16x2(v2, v3));
+        else
+          w = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+        const int q = 16 * j + r, chunk = 2 * i + (g >> 1);
+        *reinterpret_cast<uint2*>(region + wr_off + 16 * j * RB + ((chunk ^ (q & (CH - 1))) << 4)) = w;
+      }
+    }
+    asm volatile("" ::: "memory");
+    store_region<LY>(region, to_aux ? aux : static_cast<uint16_t*>(d), mb, m_end, nb, N, lane);
+    asm volatile("" ::: "memory");
+  }
+}
+
 // MXFP8 rowwise output.  The epilogue's fp32 results are rounded to bf16
 // exactly as for a bf16 D and then quantized in 32-column blocks (one E8M0
 // scale each, as the rowwise quantize kernel does), so the codes equal the
@@ -706,6 +797,8 @@ __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
   if constexpr (OUT == TE_E4M3 || OUT == TE_E5M2)
     epilogue_mx<LY, EPI, OUT>(acc, static_cast<uint8_t*>(p.d), p.d_scale, p.aux, p.bias, m0, p.M, n0, p.N, wave,
                               lane);
+  else if constexpr (staged_epilogue(EPI, OUT))
+    epilogue_lds<LY, EPI, OUT>(acc, lds, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
   else
     epilogue<LY, EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane, p.beta);
 }
@@ -762,31 +855,34 @@ __global__ __launch_bounds__(LY::kThreads) void mx_grouped_gemm_kernel(GemmParam
     __syncthreads();  // the previous tile's last reads of stage 0/1 are done
     mainloop<LY, FA, FB>(lds, acc, A, B, p.K, wave, lane);
     const bool has_bias = EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX;
-    epilogue<LY, EPI, OUT>(acc, p.d, p.aux, has_bias ? p.bias + (int64_t)e * p.N : nullptr, m0, m_end,
-                           n0, p.N, wave, lane);
+    const uint16_t* bias = has_bias ? p.bias + (int64_t)e * p.N : nullptr;
+    if constexpr (staged_epilogue(EPI, OUT))
+      epilogue_lds<LY, EPI, OUT>(acc, lds, p.d, p.aux, bias, m0, m_end, n0, p.N, wave, lane);
+    else
+      epilogue<LY, EPI, OUT>(acc, p.d, p.aux, bias, m0, m_end, n0, p.N, wave, lane);
   }
 }
 
-// The big tile unless its grid leaves CUs idle.  Measured on MI355X (256 CUs):
-// the small tile (4x the tiles, two workgroups per CU) is faster with fewer
-// 256 x 256 tiles than CUs (4096 x 1024 x 4096: 33 vs 56 us; 4096 x 3072 x
-// 1024: 24 vs 26 us), and with up to two tiles per CU when K is short
-// (4096 x 4096 x 1024 + GELU aux: 42 vs 48 us, where the small tiles overlap
-// one round's output stores with the next round's MFMAs); the big tile wins
-// with long K (4096 x 4096 x 14336: 215 vs 299 us) and on larger grids.
-inline bool use_small_tile(int64_t big_tiles, int64_t K) {
-  const int64_t cus = device_cu_count();
-  return big_tiles < cus || (big_tiles < 2 * cus && K <= 4096);
+// The big tile unless its grid leaves most CUs idle.  Measured on MI355X
+// (256 CUs, bf16 D through the LDS-staged epilogue; big / small tile):
+// 4096 x 3072 x 1024 (192 big tiles) 21.1 / 23.1 us, 4096 x 2560 x 2048
+// (160) 31.2 / 34.9, 4096 x 4096 x 1024 + GELU aux (256) 30.6 / 34.3,
+// 8192 x 4096 x 1024 (512) 46.9 / 55.0, but 4096 x 2048 x 1024 (128)
+// 18.9 / 14.7 and 4096 x 1024 x 4096 (64) 46.9 / 31.5: below about 5/8 of a
+// big tile per CU the small tile's 4x finer grid wins.
+inline bool use_small_tile(int64_t big_tiles) {
+  return 8 * big_tiles < 5 * (int64_t)device_cu_count();
 }
 
 // Tile configuration of a dense GEMM: SmallDeep for grids of at most one
-// small tile per CU with K >= 2048 (16 or more K steps), else as above.
+// small tile per CU with K >= 2048 (16 or more K steps; 4096 x 1024 x 4096:
+// 26.7 us against 31.5 for Small), else as above.
 enum class Tile { Big, Small, SmallDeep };
 
 inline Tile pick_tile(int64_t M, int64_t N, int64_t K) {
   const int64_t small_tiles = ((M + 127) / 128) * ((N + 127) / 128);
   if (small_tiles <= (int64_t)device_cu_count() && K >= 2048) return Tile::SmallDeep;
-  return use_small_tile(((M + 255) / 256) * ((N + 255) / 256), K) ? Tile::Small : Tile::Big;
+  return use_small_tile(((M + 255) / 256) * ((N + 255) / 256)) ? Tile::Small : Tile::Big;
 }
 
 inline dim3 tile_grid(Tile t, int64_t M, int64_t N) {
