@@ -15,8 +15,13 @@ One JSON line is printed.  `value` is the whole-step throughput: the GEMM
 flops of a step divided by the measured wall time of a step (quantize time
 included).  Per-kernel averages come from HIP events recorded between the
 launches on the launch stream inside the timed region; `roofline` reports
-the dominant kernel against MI355X's published peak, `kernels` every
-kernel, `cpu_baseline` the CPU oracle timed on a bounded sample.
+the dominant kernel against MI355X's published peak (HIP-event timing),
+and beside it, when summaries taken on the current kernel sources are
+committed under profiles/, that kernel's rocprofv3 average duration and
+its counter-measured HBM traffic (both looked up, and labelled so);
+`targets` says which headline targets apply to the workload and whether
+this run meets them; `kernels` lists every kernel, `cpu_baseline` the CPU
+oracle timed on a bounded sample.
 
 Bandwidth measurements rotate over several copies of every bf16 input and
 quantize output (more than the 256 MB last-level cache), so a kernel's
@@ -525,15 +530,53 @@ def traffic_from(fetch_dir, write_dir):
     print(f"wrote {TRAFFIC_JSON} and {path}")
 
 
-def stats_from(stats_dir, command):
-    """Summarise a rocprofv3 --kernel-trace --stats CSV next to the bench line it profiled."""
+KERNEL_TIME_JSON = os.path.join(ROOT, "profiles", "kernel_time.json")
+
+
+def _read_trace(csv_path):
+    """Dispatches of one rocprofv3 kernel-trace CSV: [(kernel name, duration in us)] in dispatch order."""
     import csv
-    csvs = [os.path.join(r, f) for r, _, fs in os.walk(stats_dir) for f in fs if f.endswith("kernel_stats.csv")]
-    with open(csvs[0]) as fh:
+    with open(csv_path) as fh:
+        rows = list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(r["Kernel_Name"], (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in rows]
+
+
+def rocprof_kernel_time(workload, label):
+    """rocprofv3 average duration (us) of one op's kernels from the committed kernel-trace summary, if it
+    was taken on the current kernel sources; else None."""
+    try:
+        with open(KERNEL_TIME_JSON) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if data.get("sources_hash") != kernel_sources_hash():
+        return None
+    return data.get("workloads", {}).get(workload, {}).get("ops_avg_us", {}).get(label)
+
+
+def stats_from(stats_dir, command):
+    """Summarise a rocprofv3 --kernel-trace --stats run next to the bench line it profiled: the
+    per-kernel statistics, and each op's average kernel duration from the trace (its kernels summed,
+    over every launch of the run), which also goes into profiles/kernel_time.json."""
+    import csv
+    files = [os.path.join(r, f) for r, _, fs in os.walk(stats_dir) for f in fs]
+    with open([f for f in files if f.endswith("kernel_stats.csv")][0]) as fh:
         rows = list(csv.DictReader(fh))
     with open(os.path.join(stats_dir, "ops.json")) as fh:
         record = json.load(fh)
     wl = record["workload"]
+    per_op = _per_op(_read_trace([f for f in files if f.endswith("kernel_trace.csv")][0]), record)
+    try:
+        with open(KERNEL_TIME_JSON) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        data = {}
+    if data.get("sources_hash") != kernel_sources_hash():
+        data = {"sources_hash": kernel_sources_hash(), "workloads": {}}
+    data["workloads"][wl] = {"command": command, "ops_avg_us": {k: round(v, 3) for k, v in per_op.items()}}
+    with open(KERNEL_TIME_JSON, "w") as fh:
+        json.dump(data, fh, indent=1)
     md = [f"# Kernel time, workload {wl}", "", "Command (from the repository root):", "",
           "    " + command, "", "rocprofv3 kernel statistics:", "",
           "| kernel | calls | avg us | min us | max us | total % |", "|---|---:|---:|---:|---:|---:|"]
@@ -542,11 +585,18 @@ def stats_from(stats_dir, command):
         short = name.replace("void ", "").replace("temx::(anonymous namespace)::", "").split("(")[0]
         md.append(f"| `{short[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    ops = {o["label"]: o for o in record["ops"]}
+    events = {k["name"]: k["avg_ms"] * 1e3 for k in (record.get("bench_line") or {}).get("kernels", [])}
+    md += ["", "Per op: the average duration of its kernels in the trace above (every launch of the run), and",
+           "the HIP-event average of the same run (bench.py, back-to-back launches after the timed region):", "",
+           "| op | rocprof avg us | HIP events avg us | rocprof TFLOP/s | rocprof GB/s |", "|---|---:|---:|---:|---:|"]
+    for lab, us in per_op.items():
+        o = ops[lab]
+        tf = f"{o['flops'] / (us * 1e-6) / 1e12:.1f}" if o.get("flops") else ""
+        gb = f"{o['bytes'] / (us * 1e-6) / 1e9:.1f}" if o.get("bytes") else ""
+        ev = f"{events[lab]:.2f}" if lab in events else ""
+        md.append(f"| {lab} | {us:.2f} | {ev} | {tf} | {gb} |")
     if record.get("bench_line"):
-        md += ["", "Per-op averages from HIP events in the same run (bench.py):", "",
-               "| op | avg us |", "|---|---:|"]
-        for k in record["bench_line"]["kernels"]:
-            md.append(f"| {k['name']} | {k['avg_ms'] * 1e3:.2f} |")
         md += ["", "bench.py line of this run:", "", "    " + json.dumps(record["bench_line"]["summary"])]
     md += ["", f"Kernel sources hash: {kernel_sources_hash()}", ""]
     path = os.path.join(ROOT, "profiles", f"{wl}_kernel_stats.md")
@@ -612,6 +662,26 @@ def mfma_from(pmc_dir, command):
 
 
 # --------------------------------------------------------------------- main
+
+TARGET_QUANTIZE_FRAC_HBM = 0.70   # every MXFP8 quantize kernel, of MI355X's HBM peak
+TARGET_GEMM_8192_FRAC = 0.60      # the 8192^3 MXFP8 GEMM, of the dense FP8 MFMA peak, per rocprof
+
+
+def targets(w, kernels, roof):
+    """The headline targets that apply to this workload, each with what this run measured and whether it
+    is met (the GEMM target by the rocprof figure when one is committed for these sources)."""
+    out = {}
+    q = [k["frac_hbm_peak"] for k in kernels if k["kind"] == "quantize" and "frac_hbm_peak" in k]
+    if q:
+        out["quantize_frac_hbm"] = {"target": TARGET_QUANTIZE_FRAC_HBM, "min_measured": min(q),
+                                    "met": min(q) >= TARGET_QUANTIZE_FRAC_HBM}
+    if w.name == "square_8192":
+        by = roof["rocprof"]["frac"] if roof.get("rocprof") else roof["frac"]
+        out["gemm_8192_frac_fp8_peak"] = {"target": TARGET_GEMM_8192_FRAC, "events": roof["frac"],
+                                          "rocprof": roof["rocprof"]["frac"] if roof.get("rocprof") else None,
+                                          "met": by >= TARGET_GEMM_8192_FRAC}
+    return out
+
 
 def arithmetic(w):
     kinds = {g.scaling for g in w.gemms} or {"mx"}
@@ -753,8 +823,22 @@ def main():
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     w = workloads.ALL[args.workload]()
-    roof["traffic"] = measured_traffic(w.name, dlabel)
     roof["kernel"] = dlabel
+    roof["timing"] = "HIP events on the launch stream, the op's launches back to back after the timed region"
+    # the same kernel's rocprofv3 average, looked up from the committed kernel-trace summary
+    r_us = rocprof_kernel_time(w.name, dlabel)
+    if r_us is not None:
+        r_ach = (dflops / (r_us * 1e-6) / 1e12) if dkind == "gemm" else (dbytes / (r_us * 1e-6) / 1e9)
+        roof["rocprof"] = {"avg_us": r_us, "achieved": round(r_ach, 1), "frac": round(r_ach / roof["peak"], 4),
+                           "source": f"profiles/{w.name}_kernel_stats.md (rocprofv3 --kernel-trace on these kernel "
+                                     f"sources, {kernel_sources_hash()}; looked up, not measured in this run)"}
+    else:
+        roof["rocprof"] = None
+    roof["traffic"] = measured_traffic(w.name, dlabel)
+    roof["traffic_source"] = (
+        f"profiles/{w.name}_traffic.md (rocprofv3 FETCH_SIZE and WRITE_SIZE runs on these kernel sources, "
+        f"{kernel_sources_hash()}; looked up, not measured in this run)" if roof["traffic"] is not None else
+        "no counter summary taken on the current kernel sources")
 
     value = step.flops / (ms_per_step * 1e-3) / 1e12
     qk = [k for k in kernels if k["kind"] == "quantize"]
@@ -778,6 +862,7 @@ def main():
         "roofline": roof,
         "quantize_gbs_min": min((k["gbs"] for k in qk), default=None),
         "quantize_frac_hbm_min": min((k["frac_hbm_peak"] for k in qk), default=None),
+        "targets": targets(w, kernels, roof),
         "kernels": kernels,
     }
     if args.copy_calibration:
