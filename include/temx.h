@@ -140,7 +140,7 @@ te_status te_fp8_cast_current_scaling(const uint16_t* x, int64_t n, te_dtype fmt
  * workspace: for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
  * stage-one partial maxima live in a static device array of the library
- * (4 KB: at most 1024 partials, one per amax workgroup, which serves every
+ * (2 KB: at most 512 partials, one per amax workgroup, which serves every
  * n the entry point accepts).  Each GPU holds its own copy from the first
  * call on it until the process ends; its address is looked up on that first
  * call with the device current.  Arguments, results and errors are those of

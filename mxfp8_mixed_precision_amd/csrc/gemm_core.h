@@ -596,7 +596,7 @@ constexpr bool staged_epilogue(int epi, int out) {
 }
 
 template <class LY, int EPI, int OUT>
-__device__ __forceinline__ void epilogue_lds(const v4f (&acc)[LY::FRN][LY::FRM], uint8_t* lds, void* d,
+__device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8_t* lds, void* d,
                                              uint16_t* aux, const uint16_t* bias, int64_t m0, int64_t m_end,
                                              int64_t n0, int64_t N, int wave, int lane) {
   static_assert(OUT == TE_BF16 || OUT == TE_FP16, "2-byte outputs");
@@ -607,18 +607,23 @@ __device__ __forceinline__ void epilogue_lds(const v4f (&acc)[LY::FRN][LY::FRM],
   const int g = lane >> 4, r = lane & 15;
   uint8_t* region = lds + wave * kRegion;
   const int64_t mb = m0 + wm * LY::WTM, nb = n0 + wn * LY::WTN;
-  float bv[LY::FRN][4];
+  // the bias is added in place (the accumulators are not needed afterwards): fewer live registers than
+  // keeping the bias beside them through both passes
+  if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
 #pragma unroll
-  for (int i = 0; i < LY::FRN; ++i) {
-    const int64_t n = nb + 16 * i + 4 * g;
-    bv[i][0] = bv[i][1] = bv[i][2] = bv[i][3] = 0.f;
-    if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
+    for (int i = 0; i < LY::FRN; ++i) {
+      const int64_t n = nb + 16 * i + 4 * g;
       if (n < N) {
         const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
-        bv[i][0] = bf16_bits_to_float(bb.x & 0xFFFFu);
-        bv[i][1] = bf16_bits_to_float(bb.x >> 16);
-        bv[i][2] = bf16_bits_to_float(bb.y & 0xFFFFu);
-        bv[i][3] = bf16_bits_to_float(bb.y >> 16);
+        const float b0 = bf16_bits_to_float(bb.x & 0xFFFFu), b1 = bf16_bits_to_float(bb.x >> 16);
+        const float b2 = bf16_bits_to_float(bb.y & 0xFFFFu), b3 = bf16_bits_to_float(bb.y >> 16);
+#pragma unroll
+        for (int j = 0; j < LY::FRM; ++j) {
+          acc[i][j][0] += b0;
+          acc[i][j][1] += b1;
+          acc[i][j][2] += b2;
+          acc[i][j][3] += b3;
+        }
       }
     }
   }
@@ -633,8 +638,7 @@ __device__ __forceinline__ void epilogue_lds(const v4f (&acc)[LY::FRN][LY::FRM],
     for (int j = 0; j < LY::FRM; ++j) {
 #pragma unroll
       for (int i = 0; i < LY::FRN; ++i) {
-        float v0 = acc[i][j][0] + bv[i][0], v1 = acc[i][j][1] + bv[i][1];
-        float v2 = acc[i][j][2] + bv[i][2], v3 = acc[i][j][3] + bv[i][3];
+        float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
         uint2 w;
         if (EPI == TE_EPI_BIAS_GELU_AUX && !to_aux) {
           v0 = gelu_tanh(v0);
@@ -815,13 +819,17 @@ __global__ __launch_bounds__(LY::kThreads) void mx_grouped_gemm_kernel(GemmParam
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = p.groups;
   const int64_t total_m = p.M;
+  // the splits are loaded all at once (one thread each), then scanned by one thread from LDS: a serial
+  // pass over global memory waited on each load in turn (~4 us for 32 experts)
+  for (int e = threadIdx.x; e < G; e += LY::kThreads) row_off[e + 1] = p.m_splits[e];
+  __syncthreads();
   if (threadIdx.x == 0) {
     int tiles = 0;
     int64_t off = 0;
     tile_prefix[0] = 0;
     row_off[0] = 0;
     for (int e = 0; e < G; ++e) {
-      int64_t me = p.m_splits[e];
+      int64_t me = row_off[e + 1];
       me = me < 0 ? 0 : me;
       int64_t end = off + me;
       end = end > total_m ? total_m : end;
