@@ -879,7 +879,7 @@ def main():
         rec = {"workload": w.name, "pre": pre, "warmup": args.warmup, "steps": args.steps,
                "attr_launches": attr_launches,
                "calibration_copies": 3 if args.copy_calibration else 0,
-               "command": f"timeout -s KILL 120 rocprofv3 --pmc PMC --output-format csv -d {rdir} -o run -- "
+               "command": f"timeout -s KILL 170 rocprofv3 --pmc PMC --output-format csv -d {rdir} -o run -- "
                           f"python bench.py --workload {args.workload} --steps {args.steps} "
                           f"--warmup {args.warmup} --no-cpu-baseline --copy-calibration "
                           f"--record-ops {os.path.relpath(os.path.abspath(args.record_ops), ROOT)}",

@@ -373,31 +373,45 @@ __device__ __forceinline__ void compute(const uint8_t* stage, v4f (&acc)[LY::FRN
 #pragma unroll
       for (int j = 0; j < LY::FRM; ++j) sab[j] = sa[j] * sb;
     }
-#pragma unroll
-    for (int i = 0; i < LY::FRN; ++i) {
-      const Frag aop = read_frag<kScaleUnit>(stage, ro.b_data, ro.b_data2, 0, i);
-      float4 sb4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (SM == SM_FS1 && LY::SB == 1) {
-        sb4 = *reinterpret_cast<const float4*>(stage + ro.b_scale + i * 64);
-      } else if constexpr (SM == SM_FS1) {  // the four rows' floats are 16 bytes apart
-        const float* f = reinterpret_cast<const float*>(sbase + ro.b_scale + i * SST);
-        sb4 = make_float4(f[0], f[4], f[8], f[12]);
-      }
+    // The products of fragment i are added one fragment later, so the FRM MFMAs of fragment i + 1 issue
+    // between an MFMA and the FMAs that read its result.  With the FMAs right after their MFMA the
+    // compiler filled the gap with wait states once the register assignment left it no independent
+    // work (measured on MI355X, 8192^3 with 1-D x 2-D FP32 scales: 543 us that way, 488 us this way).
+    // Each accumulator still takes its K blocks' products in K order.
+    v4f t[2][LY::FRM];
+    float4 sb4[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    auto add = [&](int i) {
+      const int h = i & 1;
 #pragma unroll
       for (int j = 0; j < LY::FRM; ++j) {
-        const v4f t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop.v, bop[j].v, v4f{0.f, 0.f, 0.f, 0.f},
-                                                                       MfmaFmt<FB>::v, MfmaFmt<FA>::v, 0, 127, 0, 127);
         if constexpr (SM == SM_FS2) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sab[j], t[e], acc[i][j][e]);
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(sab[j], t[h][j][e], acc[i][j][e]);
         } else {
-          acc[i][j][0] = __builtin_fmaf(sa[j] * sb4.x, t[0], acc[i][j][0]);
-          acc[i][j][1] = __builtin_fmaf(sa[j] * sb4.y, t[1], acc[i][j][1]);
-          acc[i][j][2] = __builtin_fmaf(sa[j] * sb4.z, t[2], acc[i][j][2]);
-          acc[i][j][3] = __builtin_fmaf(sa[j] * sb4.w, t[3], acc[i][j][3]);
+          acc[i][j][0] = __builtin_fmaf(sa[j] * sb4[h].x, t[h][j][0], acc[i][j][0]);
+          acc[i][j][1] = __builtin_fmaf(sa[j] * sb4[h].y, t[h][j][1], acc[i][j][1]);
+          acc[i][j][2] = __builtin_fmaf(sa[j] * sb4[h].z, t[h][j][2], acc[i][j][2]);
+          acc[i][j][3] = __builtin_fmaf(sa[j] * sb4[h].w, t[h][j][3], acc[i][j][3]);
         }
       }
+    };
+#pragma unroll
+    for (int i = 0; i < LY::FRN; ++i) {
+      const int h = i & 1;
+      const Frag aop = read_frag<kScaleUnit>(stage, ro.b_data, ro.b_data2, 0, i);
+      if constexpr (SM == SM_FS1 && LY::SB == 1) {
+        sb4[h] = *reinterpret_cast<const float4*>(stage + ro.b_scale + i * 64);
+      } else if constexpr (SM == SM_FS1) {  // the four rows' floats are 16 bytes apart
+        const float* f = reinterpret_cast<const float*>(sbase + ro.b_scale + i * SST);
+        sb4[h] = make_float4(f[0], f[4], f[8], f[12]);
+      }
+#pragma unroll
+      for (int j = 0; j < LY::FRM; ++j)
+        t[h][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop.v, bop[j].v, v4f{0.f, 0.f, 0.f, 0.f},
+                                                                   MfmaFmt<FB>::v, MfmaFmt<FA>::v, 0, 127, 0, 127);
+      if (i > 0) add(i - 1);
     }
+    add(LY::FRN - 1);
     return;
   }
   int sb_code = 0;  // SM_BE2: one E8M0 code for all of the wave's columns
