@@ -7,6 +7,7 @@ as a package module: importing the package loads the library being rebuilt.
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -37,22 +38,54 @@ def compile_flags() -> list[str]:
     ]
 
 
+_FUNC = re.compile(r"remark: Function Name: (\S+)")
+_SCRATCH = re.compile(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)")
+
+
+def spilled_kernels(remarks: str) -> list[tuple[str, int]]:
+    """(kernel, scratch bytes per lane) for every kernel of the compiler's resource report that uses
+    scratch memory (register spills)."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = _FUNC.search(line)
+        if m:
+            name = m.group(1)
+            continue
+        m = _SCRATCH.search(line)
+        if m and name is not None and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libtemx.so; returns its path."""
+    """Compile every HIP source and link libtemx.so; returns its path.  Fails if any kernel spills
+    registers to scratch memory: every kernel of the library is meant to run from registers, and a
+    spill (from a change elsewhere in a kernel's template) costs far more than it shows in the source."""
     obj_dir = os.path.join(PKG, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     cc = hipcc()
     objs, procs = [], []
     for src in SOURCES:  # compiled in parallel (the GEMM sources take the longest)
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags(), "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd)))
+        procs.append((src, subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True)))
         objs.append(obj)
-    failed = [src for src, proc in procs if proc.wait() != 0]
+    failed, spills = [], []
+    for src, proc in procs:
+        _, err = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(err)
+            failed.append(src)
+        else:
+            spills += [(src, k, b) for k, b in spilled_kernels(err)]
     if failed:
         raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
+    if spills:
+        listing = "; ".join(f"{src}: {k} ({b} B/lane)" for src, k, b in spills[:10])
+        raise RuntimeError(f"{len(spills)} kernel(s) spill registers to scratch: {listing}")
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
