@@ -53,6 +53,7 @@ KERNELS = {"quantize_row": ["quantize_rowwise_kernel"], "quantize_col": ["quanti
            "cast_delayed": ["cast_amax_kernel", "delayed_update_kernel"],
            "quantize_block1d": ["block_quantize_1d_kernel"], "quantize_block2d": ["block_quantize_2d_kernel"],
            "gemm_block_e8m0": ["mx_gemm_kernel"], "gemm_block_fp32": ["mx_gemm_kernel"]}
+ATTR_RUNS = 7                  # timed runs of each op's back-to-back launches (per-op mean, median, p10, p90)
 CALIBRATION_BYTES = 512 << 20  # one device-to-device copy of this many bytes reads and writes it once
 
 
@@ -99,6 +100,16 @@ class Step:
     @property
     def flops(self):
         return sum(o[3] for o in self.ops)
+
+
+def percentile(sorted_vals, q):
+    """Linear-interpolation percentile of an ascending list."""
+    if len(sorted_vals) == 1:
+        return sorted_vals[0]
+    x = (len(sorted_vals) - 1) * q / 100.0
+    i = int(x)
+    j = min(i + 1, len(sorted_vals) - 1)
+    return sorted_vals[i] + (sorted_vals[j] - sorted_vals[i]) * (x - i)
 
 
 def q_bytes(rows, cols):
@@ -776,34 +787,40 @@ def main():
 
     # Per-op attribution, right after the timed region on the same stream: each
     # op launched back to back over the rotating buffers (one captured graph of
-    # all its timed launches, replayed once to warm up and once timed),
-    # bracketed by two HIP events, so no marker sits between its launches.
+    # all its timed launches, replayed once to warm up and then ATTR_RUNS times,
+    # each replay bracketed by two HIP events, so no marker sits between its
+    # launches).
     reps = max(1, args.steps // ROTATE)
     kernels = []
     attr_launches = []
     for label, kind, fn, flops, nbytes in step.ops:
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+        # ATTR_RUNS timed runs of the op's reps * ROTATE back-to-back launches: the mean over all of them, and
+        # the median, p10 and p90 of the per-run averages
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(ATTR_RUNS)]
         if graphs is None:
             fn(0)
-            e0.record(stream)
-            for i in range(reps * ROTATE):
-                fn(i % ROTATE)
-            e1.record(stream)
-            attr_launches.append(1 + reps * ROTATE)
+            for e0, e1 in evs:
+                e0.record(stream)
+                for i in range(reps * ROTATE):
+                    fn(i % ROTATE)
+                e1.record(stream)
+            attr_launches.append(1 + ATTR_RUNS * reps * ROTATE)
         else:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for i in range(reps * ROTATE):
                     fn(i % ROTATE)
             g.replay()
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            attr_launches.append(2 * reps * ROTATE)
+            for e0, e1 in evs:
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+            attr_launches.append((1 + ATTR_RUNS) * reps * ROTATE)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / (reps * ROTATE)
-        ent = {"name": label, "kind": kind, "avg_ms": round(ms, 5)}
+        runs = sorted(e0.elapsed_time(e1) / (reps * ROTATE) for e0, e1 in evs)
+        ms = sum(runs) / len(runs)
+        ent = {"name": label, "kind": kind, "avg_ms": round(ms, 5), "median_ms": round(percentile(runs, 50), 5),
+               "p10_ms": round(percentile(runs, 10), 5), "p90_ms": round(percentile(runs, 90), 5)}
         if flops:
             ent["tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
             ent["frac_fp8_peak"] = round(ent["tflops"] / PEAK_FP8_TFLOPS, 4)

@@ -48,3 +48,12 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_percentile_interpolates_linearly():
+    import bench
+    v = [1.0, 2.0, 3.0, 4.0, 5.0]
+    assert bench.percentile(v, 50) == 3.0
+    assert bench.percentile(v, 0) == 1.0 and bench.percentile(v, 100) == 5.0
+    assert abs(bench.percentile(v, 10) - 1.4) < 1e-12 and abs(bench.percentile(v, 90) - 4.6) < 1e-12
+    assert bench.percentile([7.0], 90) == 7.0
