@@ -824,6 +824,9 @@ def main():
         if flops:
             ent["tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
             ent["frac_fp8_peak"] = round(ent["tflops"] / PEAK_FP8_TFLOPS, 4)
+            if nbytes:  # the roofline's attainable rate at this op's arithmetic intensity (HBM-limited below the ridge)
+                attainable = min(PEAK_FP8_TFLOPS, flops / nbytes * PEAK_HBM_GBS / 1e3)
+                ent["frac_attainable"] = round(ent["tflops"] / attainable, 4)
         if nbytes:
             ent["gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
             ent["frac_hbm_peak"] = round(ent["gbs"] / PEAK_HBM_GBS, 4)
