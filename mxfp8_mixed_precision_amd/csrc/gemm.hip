@@ -7,10 +7,14 @@ namespace {
 
 template <class C, bool GROUPED, int FA, int FB, int EPI, int OUT>
 te_status launch5(const GemmParams& p, dim3 grid, hipStream_t stream) {
-  if constexpr (GROUPED)
+  if constexpr (std::is_same<C, Big4>::value) {
+    static_assert(!GROUPED, "the 4-wave tile serves dense GEMMs");
+    hipLaunchKernelGGL((mx_gemm4_kernel<FA, FB, EPI, OUT>), grid, dim3(C::kThreads), 0, stream, p);
+  } else if constexpr (GROUPED) {
     hipLaunchKernelGGL((mx_grouped_gemm_kernel<C, FA, FB, EPI, OUT>), grid, dim3(C::kThreads), 0, stream, p);
-  else
+  } else {
     hipLaunchKernelGGL((mx_gemm_kernel<C, FA, FB, EPI, OUT>), grid, dim3(C::kThreads), 0, stream, p);
+  }
   return launch_status();
 }
 
@@ -22,10 +26,17 @@ te_status launch4(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stre
 
 template <class C, int FA, int FB, int EPI>
 te_status launch_pt4(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stream) {
-  if (out == TE_BF16)
-    hipLaunchKernelGGL((mx_gemm_kernel<C, FA, FB, EPI, TE_BF16, SM_PT>), grid, dim3(C::kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((mx_gemm_kernel<C, FA, FB, EPI, TE_FP32, SM_PT>), grid, dim3(C::kThreads), 0, stream, p);
+  if constexpr (std::is_same<C, Big4>::value) {
+    if (out == TE_BF16)
+      hipLaunchKernelGGL((mx_gemm4_kernel<FA, FB, EPI, TE_BF16, SM_PT>), grid, dim3(C::kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((mx_gemm4_kernel<FA, FB, EPI, TE_FP32, SM_PT>), grid, dim3(C::kThreads), 0, stream, p);
+  } else {
+    if (out == TE_BF16)
+      hipLaunchKernelGGL((mx_gemm_kernel<C, FA, FB, EPI, TE_BF16, SM_PT>), grid, dim3(C::kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((mx_gemm_kernel<C, FA, FB, EPI, TE_FP32, SM_PT>), grid, dim3(C::kThreads), 0, stream, p);
+  }
   return launch_status();
 }
 
@@ -121,6 +132,7 @@ extern "C" te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_
   const dim3 grid = tile_grid(t, M, N);
   if (t == Tile::SmallDeep) return launch2<SmallDeep, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   if (t == Tile::Small) return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
+  if (K % Big4::kKAlign == 0) return launch2<Big4, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
 }
 
@@ -147,6 +159,7 @@ extern "C" te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scal
   const dim3 grid = tile_grid(t, M, N);
   if (t == Tile::SmallDeep) return launch2<SmallDeep, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
   if (t == Tile::Small) return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
+  if (K % Big4::kKAlign == 0) return launch2<Big4, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
   return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
 }
 
@@ -174,6 +187,7 @@ extern "C" te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_
   const dim3 grid = tile_grid(t, M, N);
   if (t == Tile::SmallDeep) return launch_pt<SmallDeep>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   if (t == Tile::Small) return launch_pt<Small>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
+  if (K % Big4::kKAlign == 0) return launch_pt<Big4>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   return launch_pt<Big>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
 }
 

@@ -120,6 +120,26 @@ struct Cfg {
 using Big = Cfg<256, 256, 4, 2, 4, 2, 4>;
 using Small = Cfg<128, 128, 2, 2, 4>;
 using SmallDeep = Cfg<128, 128, 2, 2, 4, 4>;
+
+// The 4-wave big tile (mainloop4): 256 x 256, one wave per SIMD in 2 x 2,
+// each 128 x 128 (8 x 8 MFMA tiles, 256 fp32 accumulators held in AGPRs).
+// LDS: two 64-KB stages (A codes [256][128], then B codes), then two scale
+// buffers of 8 K steps each (32 E8M0 bytes per tile row: A rows, then B
+// rows), 160 KB in all.  For K % 1024 == 0 (whole scale blocks).
+struct Big4 {
+  static constexpr int BM = 256, BN = 256, NWM = 2, NWN = 2, NW = 4, kThreads = 256;
+  static constexpr int WTM = 128, WTN = 128, FRM = 8, FRN = 8;
+  static constexpr int kHalf = BM * 128;              // A codes of a stage; B codes follow
+  static constexpr int kStage = 2 * kHalf;
+  static constexpr int kScaleSteps = 8;
+  static constexpr int kScaleRow = 4 * kScaleSteps;   // bytes per tile row and scale block
+  static constexpr int kScaleBuf = (BM + BN) * kScaleRow;
+  static constexpr int kOffScale = 2 * kStage;
+  static constexpr int kLds = kOffScale + 2 * kScaleBuf;
+  static constexpr int kKAlign = 128 * kScaleSteps;   // K must be a multiple of this
+};
+static_assert(Big4::kLds == 160 * 1024, "the 4-wave tile takes all of a CU's LDS");
+
 constexpr int kGroupM = 4;      // row-tile band of the raster order
 constexpr int kMaxGroups = 1024;
 
@@ -500,6 +520,223 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
   }
 }
 
+// ---- The 4-wave big tile ----------------------------------------------------
+//
+// With one wave per SIMD a wave's MFMA stream is all its SIMD has, so every
+// memory operation sits between two MFMAs and the MFMA pipe keeps issuing.
+// K step kt (its codes in stage kt % 2, landed and visible):
+//  * column group j = 0..7 issues the 8 MFMAs acc[i][j] += B_i x A_j;
+//  * B fragments 0..2 and A fragment 0 were read during the previous step,
+//    B 3..7 are read in group 0 three MFMAs ahead of their use, A j+1 in
+//    group j;
+//  * the wave's 16 copies of step kt + 1 (8 slices of A, 8 of B) go between
+//    the MFMAs of groups 0..2, into the other stage, whose reads every wave
+//    finished before the previous step's barrier;
+//  * before group 7 the wave waits for its copies and meets the others at a
+//    barrier: step kt + 1's stage is complete and every read of stage kt is
+//    done (group 7 reads none of it);
+//  * group 7 reads step kt + 1's first fragments.
+// One m0 write serves four copies: a copy's immediate offset moves both its
+// global and its LDS address (the soffset takes the global part back).
+// Scales travel in blocks of 8 K steps (32 bytes per tile row, one 32-row
+// slice per copy instruction, 2 lanes per row).  A copy of 16-byte pieces of
+// 64 different rows costs several times a copy of 8 whole lines; measured on
+// MI355X (8192^3): 4-step blocks 2,700 clocks per K step, 8-step blocks
+// 2,640, no scale copies at all 2,470.  Block b + 1 is copied during steps
+// 8b .. 8b + 3 (one slice per wave and step) into the buffer block b - 1 used.
+// The MFMAs are inline asm on AGPR accumulators ("+a"): with the builtin the
+// compiler's register allocation rotated the 256 accumulators through copies
+// and spilled.  The asm keeps the MFMAs out of the compiler's hazard checks,
+// so the loop itself orders the accumulators' other accesses behind wait
+// states: the zeroing before the first MFMA and the reads after the last.
+
+template <int FA, int FB>
+__device__ __forceinline__ void mfma_acc(v4f& acc, const v8i& bv, int bs, const v8i& av, int as) {
+  if constexpr (FA == TE_E4M3 && FB == TE_E4M3)
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                 : "+a"(acc) : "v"(bv), "v"(av), "v"(bs), "v"(as));
+  else if constexpr (FA == TE_E4M3)  // B operand (the instruction's first) E5M2
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:1"
+                 : "+a"(acc) : "v"(bv), "v"(av), "v"(bs), "v"(as));
+  else if constexpr (FB == TE_E4M3)  // A operand E5M2
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] blgp:1"
+                 : "+a"(acc) : "v"(bv), "v"(av), "v"(bs), "v"(as));
+  else
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:1 blgp:1"
+                 : "+a"(acc) : "v"(bv), "v"(av), "v"(bs), "v"(as));
+}
+
+// m0 <- an LDS address, for the direct-to-LDS copies that follow
+__device__ __forceinline__ void set_m0(uint32_t lds_addr) { asm volatile("s_mov_b32 m0, %0" ::"s"(lds_addr) : "memory"); }
+
+// buffer_load_dwordx4 ... lds with an immediate offset, which moves the LDS
+// address too (lane l lands at m0 + IMM + 16 l)
+template <int IMM>
+__device__ __forceinline__ void lds_dma16_imm(const i32x4& rsrc, int voff, int soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds" ::"v"(voff), "s"(rsrc), "s"(soff), "i"(IMM)
+               : "memory");
+}
+
+#define TEMX_SCHED_BARRIER() __builtin_amdgcn_sched_barrier(0)
+
+template <int FA, int FB, int SM>
+__device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const Operand& A, const Operand& B,
+                                          int64_t K64, int wave, int lane) {
+  static_assert(SM == SM_MX || SM == SM_PT, "E8M0 block scales or none");
+  using LY = Big4;
+  constexpr int kNcg = 3;                            // column groups that carry the copies
+  constexpr int kScaleSlot = (4 * 8 * kNcg) / 16;    // the slot of data copy 4, which sets m0 again
+  const int K = (int)K64, KS = K / 32;
+  const int kt_n = K / BK;  // a multiple of 8, > 0
+  const int wm = wave >> 1, wn = wave & 1;
+  // zeros into the AGPRs here, ahead of the copies below, and wait states after them: the compiler
+  // cannot see the MFMAs read them (a VALU write read as an MFMA's accumulator input needs a gap)
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      asm volatile("" : "+a"(acc[i][j]));
+    }
+  asm volatile("s_nop 7" ::: "memory");
+  const uint32_t l0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+
+  // copies: wave w fills slices 8w .. 8w+7 of A and of B (slice q = rows 8q .. 8q+7, 1 KB); copy t
+  // takes slice 8w + t: lane l lands at row 8q + l/8, physical chunk l%8, which holds logical chunk
+  // (l%8) ^ swz(row) = (l%8) ^ (l/16) ^ 4 (t & 1)
+  const int chunk_e = (lane & 7) ^ (lane >> 4);
+  int vo_e = (64 * wave + (lane >> 3)) * K + chunk_e * 16;
+  int vo_o = (64 * wave + (lane >> 3)) * K + (chunk_e ^ 4) * 16;
+  int vo_s = (lane >> 1) * KS + 16 * (lane & 1);  // scale slice: lane l takes row l/2, bytes 16 (l%2) ..
+  // fragment reads: lane 16 g + r reads logical chunks g and g + 4 of row r of each fragment
+  const int g = lane >> 4, r = lane & 15;
+  const int lane_off = r * BK + ((g ^ swz(r)) << 4);
+  int ra_off = wm * 128 * BK + lane_off;                                  // + 2 KB j
+  int rb_off = LY::kHalf + wn * 128 * BK + lane_off;                      // + 2 KB i
+  int sa_off = (wm * 128 + r) * LY::kScaleRow + g;                        // + 512 j + 4 (kt % 8)
+  int sb_off = LY::BM * LY::kScaleRow + (wn * 128 + r) * LY::kScaleRow + g;  // + 512 i
+  asm volatile("" : "+v"(vo_e), "+v"(vo_o), "+v"(vo_s), "+v"(ra_off), "+v"(rb_off), "+v"(sa_off), "+v"(sb_off));
+
+  auto copy = [&](int c, int kbase, uint32_t l_stage) __attribute__((always_inline)) {
+    const int t = c & 7;
+    const bool isb = c >= 8;
+    if ((t & 3) == 0)
+      set_m0((uint32_t)__builtin_amdgcn_readfirstlane((int)(l_stage + (isb ? LY::kHalf : 0) + (8 * wave + t) * 1024)));
+    const int so = __builtin_amdgcn_readfirstlane(8 * t * K - (t & 3) * 1024) + kbase;
+    const int vo = (t & 1) ? vo_o : vo_e;
+    const i32x4& rs = isb ? B.data : A.data;
+    switch (t & 3) {
+      case 0: lds_dma16_imm<0>(rs, vo, so); break;
+      case 1: lds_dma16_imm<1024>(rs, vo, so); break;
+      case 2: lds_dma16_imm<2048>(rs, vo, so); break;
+      default: lds_dma16_imm<3072>(rs, vo, so); break;
+    }
+  };
+  // scale slice s = wave + 4k of block blk: slices 0..7 are A rows 32 s .., 8..15 B rows
+  auto copy_scales = [&](int blk, uint32_t l_sbuf, int k) __attribute__((always_inline)) {
+    const int s = wave + 4 * k;
+    blk = __builtin_amdgcn_readfirstlane(blk);
+    asm volatile("" : "+s"(blk));
+    set_m0((uint32_t)__builtin_amdgcn_readfirstlane((int)(l_sbuf + s * 1024)));
+    const int so = __builtin_amdgcn_readfirstlane(32 * (s & 7) * KS) + 32 * blk;
+    if (k < 2) lds_dma16_imm<0>(A.scale, vo_s, so);
+    else lds_dma16_imm<0>(B.scale, vo_s, so);
+  };
+  auto rd = [&](const uint8_t* stg, const uint8_t* sbuf, int off, int soff, int f, int sub)
+                __attribute__((always_inline)) {
+    Frag fr;
+    const uint4 lo = *reinterpret_cast<const uint4*>(stg + off + f * 16 * BK);
+    const uint4 hi = *reinterpret_cast<const uint4*>(stg + (off ^ 64) + f * 16 * BK);
+    fr.v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    fr.s = SM == SM_PT ? 127 : (int)sbuf[soff + f * 16 * LY::kScaleRow + 4 * sub];
+    return fr;
+  };
+
+  int m0_saved;
+  asm volatile("s_mov_b32 %0, m0" : "=s"(m0_saved));
+  // prologue: step 0's stage and scale block 0
+#pragma unroll
+  for (int c = 0; c < 16; ++c) copy(c, 0, l0);
+  if constexpr (SM == SM_MX) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) copy_scales(0, l0 + LY::kOffScale, k);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  Frag Af0, Bf[3];  // the step's first fragments, read during the previous step
+  Af0 = rd(lds, lds + LY::kOffScale, ra_off, sa_off, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) Bf[i] = rd(lds, lds + LY::kOffScale, rb_off, sb_off, i, 0);
+
+  auto step = [&](int kt, auto s8c, auto more_c) __attribute__((always_inline)) {
+    constexpr int S8 = decltype(s8c)::value;  // kt % 8
+    constexpr bool MORE = decltype(more_c)::value;
+    const uint8_t* cur = lds + (S8 & 1) * LY::kStage;
+    const uint8_t* nxt = lds + ((S8 & 1) ^ 1) * LY::kStage;
+    const uint32_t l_nxt = l0 + ((S8 & 1) ^ 1) * LY::kStage;
+    const uint8_t* sbuf = lds + LY::kOffScale + ((kt >> 3) & 1) * LY::kScaleBuf;
+    const uint8_t* sbuf_n = lds + LY::kOffScale + (((kt + 1) >> 3) & 1) * LY::kScaleBuf;
+    // opaque, so that the copies' offsets are a few hoisted constants plus this
+    int kbase_n = __builtin_amdgcn_readfirstlane((kt + 1) * BK);
+    asm volatile("" : "+s"(kbase_n));
+    Frag Bv[8], Av[2];
+    Bv[0] = Bf[0];
+    Bv[1] = Bf[1];
+    Bv[2] = Bf[2];
+    Av[0] = Af0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j == 7) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        TEMX_SCHED_BARRIER();
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int slot = 8 * j + i;
+        mfma_acc<FA, FB>(acc[i][j], Bv[i].v, Bv[i].s, Av[j & 1].v, Av[j & 1].s);
+        if (j == 0 && i + 3 < 8) Bv[i + 3] = rd(cur, sbuf, rb_off, sb_off, i + 3, S8);
+        if (j < 7 && i == 4) Av[(j + 1) & 1] = rd(cur, sbuf, ra_off, sa_off, j + 1, S8);
+        if (SM == SM_MX && S8 < 4 && slot == kScaleSlot)
+          copy_scales((kt >> 3) + 1, l0 + LY::kOffScale + ((((kt >> 3) + 1) & 1) * LY::kScaleBuf), S8);
+        if (MORE) {
+#pragma unroll
+          for (int c = 0; c < 16; ++c)
+            if ((c * 8 * kNcg) / 16 == slot) copy(c, kbase_n, l_nxt);
+        }
+        if (MORE && j == 7) {
+          if (i == 0) Af0 = rd(nxt, sbuf_n, ra_off, sa_off, 0, (S8 + 1) & 7);
+          if (i >= 1 && i <= 3) Bf[i - 1] = rd(nxt, sbuf_n, rb_off, sb_off, i - 1, (S8 + 1) & 7);
+        }
+        TEMX_SCHED_BARRIER();
+      }
+    }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  auto eight = [&](int k0, auto last) __attribute__((always_inline)) {
+    step(k0, std::integral_constant<int, 0>{}, T{});
+    step(k0 + 1, std::integral_constant<int, 1>{}, T{});
+    step(k0 + 2, std::integral_constant<int, 2>{}, T{});
+    step(k0 + 3, std::integral_constant<int, 3>{}, T{});
+    step(k0 + 4, std::integral_constant<int, 4>{}, T{});
+    step(k0 + 5, std::integral_constant<int, 5>{}, T{});
+    step(k0 + 6, std::integral_constant<int, 6>{}, T{});
+    step(k0 + 7, std::integral_constant<int, 7>{}, last);
+  };
+  int kt = 0;
+  for (; kt < kt_n - 8; kt += 8) eight(kt, T{});
+  eight(kt, F{});
+  // the last MFMAs' results: wait states before anything reads them (an MFMA result read by another
+  // instruction needs at most 19 on gfx950), and the copies' m0 back.  The empty asm statements tie
+  // every accumulator to a point after the wait states, so the compiler cannot read one earlier.
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_mov_b32 m0, %0" ::"s"(m0_saved) : "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
 // Epilogue from registers.  acc[i][j][e] is D[m][n] with
 // m = m0 + WTM wm + 16 j + (lane & 15), n = n0 + WTN wn + 16 i + 4 (lane >> 4) + e.
 // A store instruction writes 32 bytes of each of 16 rows; the row fragments
@@ -507,10 +744,19 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
 // stores and meet in L2 before it writes the line back (measured: 4096 x
 // 4096 x 1024 with GELU aux 42.2 -> 37.8 us, against the column-fragment
 // order, whose scattered partial lines doubled the bytes written).
-template <class LY, int EPI, int OUT>
+// a * b rounded on its own: never contracted into an FMA with a later add
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
+// SCALE: each result is first multiplied by alpha (its own rounding, no FMA
+// with the bias add), fragment by fragment: the per-tensor mode of the
+// 4-wave tile, whose 256 accumulators cannot all pass through VGPRs at once.
+template <class LY, int EPI, int OUT, bool SCALE = false>
 __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], void* d, uint16_t* aux,
                                          const uint16_t* bias, int64_t m0, int64_t m_end, int64_t n0, int64_t N,
-                                         int wave, int lane, float beta = 1.0f) {
+                                         int wave, int lane, float beta = 1.0f, float alpha = 1.0f) {
   const int wm = wave / LY::NWN, wn = wave % LY::NWN;
   const int g = lane >> 4, r = lane & 15;
   // bias of the lane's columns, all fragments
@@ -539,6 +785,12 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], voi
       const int64_t n = n0 + wn * LY::WTN + 16 * i + 4 * g;
       if (n >= N) continue;
       float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
+      if constexpr (SCALE) {
+        v0 = mul_rn(v0, alpha);
+        v1 = mul_rn(v1, alpha);
+        v2 = mul_rn(v2, alpha);
+        v3 = mul_rn(v3, alpha);
+      }
       if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
         v0 += bv[i][0];
         v1 += bv[i][1];
@@ -609,10 +861,10 @@ constexpr bool staged_epilogue(int epi, int out) {
          (epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX);
 }
 
-template <class LY, int EPI, int OUT>
+template <class LY, int EPI, int OUT, bool SCALE = false>
 __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8_t* lds, void* d,
                                              uint16_t* aux, const uint16_t* bias, int64_t m0, int64_t m_end,
-                                             int64_t n0, int64_t N, int wave, int lane) {
+                                             int64_t n0, int64_t N, int wave, int lane, float alpha = 1.0f) {
   static_assert(OUT == TE_BF16 || OUT == TE_FP16, "2-byte outputs");
   static_assert(EPI == TE_EPI_NONE || EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX, "forward epilogues");
   constexpr int RB = LY::WTN * 2, CH = RB / 16, kRegion = LY::WTM * RB;
@@ -633,10 +885,17 @@ __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8
         const float b2 = bf16_bits_to_float(bb.y & 0xFFFFu), b3 = bf16_bits_to_float(bb.y >> 16);
 #pragma unroll
         for (int j = 0; j < LY::FRM; ++j) {
-          acc[i][j][0] += b0;
-          acc[i][j][1] += b1;
-          acc[i][j][2] += b2;
-          acc[i][j][3] += b3;
+          if constexpr (SCALE) {
+            acc[i][j][0] = mul_rn(acc[i][j][0], alpha) + b0;
+            acc[i][j][1] = mul_rn(acc[i][j][1], alpha) + b1;
+            acc[i][j][2] = mul_rn(acc[i][j][2], alpha) + b2;
+            acc[i][j][3] = mul_rn(acc[i][j][3], alpha) + b3;
+          } else {
+            acc[i][j][0] += b0;
+            acc[i][j][1] += b1;
+            acc[i][j][2] += b2;
+            acc[i][j][3] += b3;
+          }
         }
       }
     }
@@ -653,6 +912,12 @@ __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8
 #pragma unroll
       for (int i = 0; i < LY::FRN; ++i) {
         float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
+        if constexpr (SCALE && EPI == TE_EPI_NONE) {  // with a bias the products went in above
+          v0 = mul_rn(v0, alpha);
+          v1 = mul_rn(v1, alpha);
+          v2 = mul_rn(v2, alpha);
+          v3 = mul_rn(v3, alpha);
+        }
         uint2 w;
         if (EPI == TE_EPI_BIAS_GELU_AUX && !to_aux) {
           v0 = gelu_tanh(v0);
@@ -773,35 +1038,36 @@ struct GemmParams {
   float beta = 1.0f;        // accumulate epilogue: D = fl32(beta D + acc)
 };
 
-// Dense: one workgroup per tile, operands scaled as SM says (SM_PT: the
-// accumulators are multiplied by alpha = a_scale_inv * b_scale_inv before the
-// epilogue).
-template <class LY, int FA, int FB, int EPI, int OUT, int SM = SM_MX>
-__global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
-  constexpr int BM = LY::BM, BN = LY::BN;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ntm = (int)((p.M + BM - 1) / BM), ntn = (int)((p.N + BN - 1) / BN);
+// Workgroup b's tile: workgroups are dealt round-robin to the 8 XCDs, so
+// each XCD is given a contiguous run of tiles, rastered in bands of kGroupM
+// row-tiles.
+__device__ __forceinline__ void raster_tile(int bid, int ntm, int ntn, int& tm, int& tn) {
   const int ntiles = ntm * ntn;
-  // XCD-aware remap: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous run of tiles.
-  const int bid = blockIdx.x;
   const int per = ntiles / 8;
   const int t = bid < 8 * per ? (bid % 8) * per + bid / 8 : bid;
-  // raster in bands of kGroupM row-tiles
   const int band = t / (kGroupM * ntn);
   const int first_tm = band * kGroupM;
   const int band_rows = min(ntm - first_tm, kGroupM);
   const int in_band = t % (kGroupM * ntn);
-  const int tm = first_tm + in_band % band_rows;
-  const int tn = in_band / band_rows;
-  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-  const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, BM);
-  const Operand B = b_2d(SM) ? make_operand_2d(p.b, p.b_scale, n0, p.N - n0, p.K, BN)
-                                 : make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, BN);
-  v4f acc[LY::FRN][LY::FRM];
-  mainloop<LY, FA, FB, SM>(lds, acc, A, B, p.K, wave, lane);
+  tm = first_tm + in_band % band_rows;
+  tn = in_band / band_rows;
+}
+
+// A dense tile's accumulators to D (and aux / MXFP8 scales), per the epilogue
+// and scaling mode.
+template <class LY, int EPI, int OUT, int SM>
+__device__ __forceinline__ void finish_tile(v4f (&acc)[LY::FRN][LY::FRM], uint8_t* lds, const GemmParams& p,
+                                            int64_t m0, int64_t n0, int wave, int lane) {
+  if constexpr (SM == SM_PT && LY::FRM * LY::FRN > 32) {
+    // alpha goes in fragment by fragment inside the epilogue (per-tensor mode: bf16 or fp32 D)
+    static_assert(OUT == TE_BF16 || OUT == TE_FP32, "per-tensor outputs");
+    const float alpha = *p.alpha_a * *p.alpha_b;
+    if constexpr (staged_epilogue(EPI, OUT))
+      epilogue_lds<LY, EPI, OUT, true>(acc, lds, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane, alpha);
+    else
+      epilogue<LY, EPI, OUT, true>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane, p.beta, alpha);
+    return;
+  }
   if constexpr (SM == SM_PT) {
     // these products are rounded on their own: with contraction off here the
     // epilogue's bias add stays a second rounding instead of becoming an FMA
@@ -819,6 +1085,44 @@ __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
     epilogue_lds<LY, EPI, OUT>(acc, lds, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane);
   else
     epilogue<LY, EPI, OUT>(acc, p.d, p.aux, p.bias, m0, p.M, n0, p.N, wave, lane, p.beta);
+}
+
+// Dense: one workgroup per tile, operands scaled as SM says (SM_PT: the
+// accumulators are multiplied by alpha = a_scale_inv * b_scale_inv before the
+// epilogue).
+template <class LY, int FA, int FB, int EPI, int OUT, int SM = SM_MX>
+__global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
+  constexpr int BM = LY::BM, BN = LY::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int tm, tn;
+  raster_tile(blockIdx.x, (int)((p.M + BM - 1) / BM), (int)((p.N + BN - 1) / BN), tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, BM);
+  const Operand B = b_2d(SM) ? make_operand_2d(p.b, p.b_scale, n0, p.N - n0, p.K, BN)
+                                 : make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, BN);
+  v4f acc[LY::FRN][LY::FRM];
+  mainloop<LY, FA, FB, SM>(lds, acc, A, B, p.K, wave, lane);
+  finish_tile<LY, EPI, OUT, SM>(acc, lds, p, m0, n0, wave, lane);
+}
+
+// Dense on the 4-wave big tile (MXFP8 or per-tensor operands, K % 1024 == 0):
+// one wave per SIMD, so the whole register file is the wave's.
+template <int FA, int FB, int EPI, int OUT, int SM = SM_MX>
+__global__ __launch_bounds__(Big4::kThreads, 1) void mx_gemm4_kernel(GemmParams p) {
+  using LY = Big4;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int tm, tn;
+  raster_tile(blockIdx.x, (int)((p.M + LY::BM - 1) / LY::BM), (int)((p.N + LY::BN - 1) / LY::BN), tm, tn);
+  const int64_t m0 = (int64_t)tm * LY::BM, n0 = (int64_t)tn * LY::BN;
+  const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, LY::BM);
+  const Operand B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, LY::BN);
+  v4f acc[LY::FRN][LY::FRM];
+  mainloop4<FA, FB, SM>(lds, acc, A, B, p.K, wave, lane);
+  finish_tile<LY, EPI, OUT, SM>(acc, lds, p, m0, n0, wave, lane);
 }
 
 // Grouped: a persistent grid walks the flat list of (expert row-tile,

@@ -76,6 +76,28 @@ def test_big_tile_exact_integer_partial_scale_block(fa, fb):
     assert np.array_equal(host(d[rows]).astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
+@pytest.mark.parametrize("K", [1024, 3072])
+def test_four_wave_tile_exact_integer(fa, fb, K):
+    # the 4-wave big tile (K % 1024 == 0, 17 x 17 tiles of 256) with a 48-row
+    # and an 80-column tail; K = 1024 is one 8-step scale block, 3072 three.
+    # Exact-integer operands: every fp32 output is exact, so sampled rows
+    # (every tile boundary, every wave-row boundary, the last row) must match
+    # the oracle bit for bit in every column.
+    M, N = 4096 + 48, 4096 + 80
+    rng = np.random.default_rng(K + 7)
+    qa, qb = exact_codes(rng, (M, K), fa), exact_codes(rng, (N, K), fb)
+    sa = rng.integers(124, 131, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(124, 131, size=(N, K // 32)).astype(np.uint8)
+    d, _ = te().mxfp8_gemm(dev(qa), dev(sa), fa, dev(qb), dev(sb), fb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, M - 1} | {128 * t + o for t in range(M // 128) for o in (0, 15, 16, 127)}
+                           | set(rng.choice(M, 16, replace=False).tolist())))
+    rows = rows[rows < M]
+    ref, _, _ = oracle.mx_gemm(qa[rows], sa[rows], oracle.format_by_name(fa), qb, sb, oracle.format_by_name(fb))
+    assert np.array_equal(host(d[rows]).astype(np.float64), ref)
+
+
 def test_gemm_k_zero_gives_epilogue_of_zero():
     M, N = 64, 48
     bias = workloads.normal_bf16(6, 1, (N,), 1.0)
@@ -204,11 +226,13 @@ def test_ragged_shapes_and_epilogues(epi, M, N, K):
 
 
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
-def test_big_tile_ragged_edges(epi):
-    # enough 256 x 256 tiles (17 x 17) that the big-tile kernel runs, with a
+@pytest.mark.parametrize("K", [256, 1024])
+def test_big_tile_ragged_edges(epi, K):
+    # enough 256 x 256 tiles (17 x 17) that a big-tile kernel runs, with a
     # 48-row and an 80-column tail; sampled rows / columns include every tile
-    # boundary and the last row and column
-    M, N, K = 4096 + 48, 4096 + 80, 256
+    # boundary and the last row and column.  K = 256 runs the 8-wave tile,
+    # K = 1024 (whole 8-step scale blocks) the 4-wave one.
+    M, N = 4096 + 48, 4096 + 80
     spec = workloads.GemmSpec("big_ragged", M, N, K, "e4m3", "e4m3", epi,
                               workloads.TensorSpec(53, M, (M, K), 1.0, 0.01),
                               workloads.TensorSpec(54, N, (N, K), 0.05),
@@ -349,7 +373,7 @@ def backward_operands(M, N, K, seed):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
-                                   (272, 400, 2176)])
+                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 1024)])
 def test_dgelu_epilogue(M, N, K):
     qa, sa, qb, sb, oqa, osa, oqb, osb = backward_operands(M, N, K, 70 + K)
     pre = workloads.normal_bf16(72, M + N, (M, N), 2.0, 0.0)   # the forward's saved pre-activation
@@ -390,7 +414,7 @@ def test_dgelu_epilogue(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
-                                   (272, 400, 2176)])
+                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 1024)])
 def test_accumulate_epilogue(M, N, K):
     qa, sa, qb, sb, oqa, osa, oqb, osb = backward_operands(M, N, K, 80 + K)
     rng = np.random.default_rng(M + N + K)
@@ -461,7 +485,7 @@ def test_grouped_backward_epilogues_match_dense(epi):
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
 @pytest.mark.parametrize("M,N,K,out_fmt", [(16, 32, 128, "e4m3"), (272, 416, 256, "e4m3"), (1040, 800, 640, "e4m3"),
                                            (4096 + 48, 4096 + 32, 256, "e4m3"), (272, 416, 256, "e5m2"),
-                                           (272, 416, 2176, "e4m3")])
+                                           (272, 416, 2176, "e4m3"), (4096 + 48, 4096 + 32, 1024, "e4m3")])
 def test_mxfp8_output_equals_quantized_bf16_output(epi, M, N, K, out_fmt):
     # the codes must be exactly the rowwise quantization of the bf16 D that
     # te_mxfp8_gemm writes for the same inputs (itself checked against the
