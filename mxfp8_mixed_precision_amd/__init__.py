@@ -466,15 +466,24 @@ def fp8_cast_current_scaling(x, fmt="e4m3", stream=None):
     return q, a, s, si
 
 
+def gemm_workspace(M: int, N: int, K: int, device="cuda"):
+    """The workspace te_mxfp8_gemm / te_mxfp8_gemm_mxout use for an M x N x K GEMM (None if none)."""
+    n = te_mxfp8_gemm_workspace_size(M, N, K)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, epilogue="none", bias=None, out_dtype=torch.bfloat16,
-               aux=None, out=None, stream=None):
+               aux=None, out=None, stream=None, workspace="auto"):
     """-> (D, aux) for D = epilogue(A . B^T).  aux is written and returned for "bias_gelu_aux" and is
-    the saved pre-activation read by "dgelu"; "accumulate" adds into the given fp32 ``out``."""
+    the saved pre-activation read by "dgelu"; "accumulate" adds into the given fp32 ``out``.
+    workspace: "auto" allocates what the GEMM can use, or a tensor, or None for none."""
     M, N = a.shape[0], b.shape[0]
     d = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=a.device)
     if epilogue == "bias_gelu_aux":
         aux = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
-    te_mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, d, epilogue, bias, aux, None, stream)
+    if isinstance(workspace, str):
+        workspace = gemm_workspace(M, N, a.shape[1], a.device)
+    te_mxfp8_gemm(a, a_scale, a_fmt, b, b_scale, b_fmt, d, epilogue, bias, aux, workspace, stream)
     return d, (aux if epilogue == "bias_gelu_aux" else None)
 
 
@@ -486,7 +495,8 @@ def mxfp8_gemm_mxout(a, a_scale, a_fmt, b, b_scale, b_fmt, epilogue="none", bias
     d = torch.empty((M, N), dtype=torch.uint8, device=a.device)
     ds = torch.empty((M, N // 32), dtype=torch.uint8, device=a.device)
     aux = torch.empty((M, N), dtype=torch.bfloat16, device=a.device) if epilogue == "bias_gelu_aux" else None
-    te_mxfp8_gemm_mxout(a, a_scale, a_fmt, b, b_scale, b_fmt, d, ds, out_fmt, epilogue, bias, aux, None, stream)
+    te_mxfp8_gemm_mxout(a, a_scale, a_fmt, b, b_scale, b_fmt, d, ds, out_fmt, epilogue, bias, aux,
+                        gemm_workspace(M, N, a.shape[1], a.device), stream)
     return d, ds, aux
 
 

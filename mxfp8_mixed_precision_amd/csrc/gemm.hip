@@ -112,14 +112,40 @@ int device_cu_count() {
 
 using namespace temx;
 
-extern "C" size_t te_mxfp8_gemm_workspace_size(int64_t, int64_t, int64_t) { return 0; }
+namespace temx {
+namespace {
+
+// MXFP8 GEMM on the big tile: the 4-wave kernel when the workspace takes the
+// rearranged scales (and the scale arrays allow 16-byte reads), else the
+// 8-wave kernel on the scales as they are.
+te_status launch_big_mx(GemmParams p, te_dtype a_fmt, te_dtype b_fmt, te_epilogue epi, te_dtype out, dim3 grid,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const int64_t M = p.M, N = p.N, K = p.K;
+  if (four_wave_mx(M, N, K) && workspace != nullptr && workspace_bytes >= scale_blocks_bytes(M, N, K) &&
+      ((uintptr_t)workspace & 255u) == 0 && aligned16(p.a_scale) && aligned16(p.b_scale)) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    uint8_t* bs = ws + scale_blocks_b_offset(M, K);
+    if (launch_scale_blocks(p.a_scale, M, K, ws, stream) != TE_OK) return TE_ERR_HIP;
+    if (launch_scale_blocks(p.b_scale, N, K, bs, stream) != TE_OK) return TE_ERR_HIP;
+    p.a_scale = ws;
+    p.b_scale = bs;
+    return launch2<Big4, false>(p, a_fmt, b_fmt, epi, out, grid, stream);
+  }
+  return launch2<Big, false>(p, a_fmt, b_fmt, epi, out, grid, stream);
+}
+
+}  // namespace
+}  // namespace temx
+
+extern "C" size_t te_mxfp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || !dense_shape_ok(M, N, K)) return 0;
+  return four_wave_mx(M, N, K) ? scale_blocks_bytes(M, N, K) : 0;
+}
 
 extern "C" te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,
                                    const uint8_t* b_scale, te_dtype b_fmt, int64_t M, int64_t N, int64_t K, void* d,
                                    te_dtype d_dtype, te_epilogue epi, const uint16_t* bias, uint16_t* aux,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   TE_REQUIRE(M >= 0 && N >= 0 && K >= 0, TE_ERR_SHAPE);
   TE_REQUIRE(K % 128 == 0 && M % 16 == 0 && N % 16 == 0, TE_ERR_SHAPE);
   TE_REQUIRE(dense_shape_ok(M, N, K), TE_ERR_SHAPE);
@@ -132,8 +158,7 @@ extern "C" te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_
   const dim3 grid = tile_grid(t, M, N);
   if (t == Tile::SmallDeep) return launch2<SmallDeep, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   if (t == Tile::Small) return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
-  if (K % Big4::kKAlign == 0) return launch2<Big4, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
-  return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
+  return launch_big_mx(p, a_fmt, b_fmt, epi, d_dtype, grid, workspace, workspace_bytes, stream);
 }
 
 extern "C" te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt, const uint8_t* b,
@@ -141,8 +166,6 @@ extern "C" te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scal
                                          uint8_t* d, uint8_t* d_scale, te_dtype d_fmt, te_epilogue epi,
                                          const uint16_t* bias, uint16_t* aux, void* workspace, size_t workspace_bytes,
                                          hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   TE_REQUIRE(epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX, TE_ERR_VALUE);
   TE_REQUIRE(d_fmt == TE_E4M3 || d_fmt == TE_E5M2, TE_ERR_DTYPE);
   TE_REQUIRE(M >= 0 && N >= 0 && K >= 0, TE_ERR_SHAPE);
@@ -159,8 +182,7 @@ extern "C" te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scal
   const dim3 grid = tile_grid(t, M, N);
   if (t == Tile::SmallDeep) return launch2<SmallDeep, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
   if (t == Tile::Small) return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
-  if (K % Big4::kKAlign == 0) return launch2<Big4, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
-  return launch2<Big, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
+  return launch_big_mx(p, a_fmt, b_fmt, epi, d_fmt, grid, workspace, workspace_bytes, stream);
 }
 
 extern "C" te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_dtype a_fmt, const uint8_t* b,

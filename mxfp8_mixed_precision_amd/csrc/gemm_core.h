@@ -538,33 +538,48 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
 //  * group 7 reads step kt + 1's first fragments.
 // One m0 write serves four copies: a copy's immediate offset moves both its
 // global and its LDS address (the soffset takes the global part back).
-// Scales travel in blocks of 8 K steps (32 bytes per tile row, one 32-row
-// slice per copy instruction, 2 lanes per row).  A copy of 16-byte pieces of
-// 64 different rows costs several times a copy of 8 whole lines; measured on
-// MI355X (8192^3): 4-step blocks 2,700 clocks per K step, 8-step blocks
-// 2,640, no scale copies at all 2,470.  Block b + 1 is copied during steps
-// 8b .. 8b + 3 (one slice per wave and step) into the buffer block b - 1 used.
+// Scales: blocks of 8 K steps in the layout scale_blocks_kernel writes (a
+// tile row's 32 bytes of a block contiguous, rows consecutive, each row
+// [32-block][step]), so a scale copy reads 32 rows' bytes as 1 KB in a row,
+// and a lane reads its block's bytes for 4 steps with one dword read, the
+// MFMA selecting the step's byte.  Block b + 1 is copied during steps 8b ..
+// 8b + 3 (one 32-row slice per wave and step) into the buffer block b - 1
+// used.  Measured on MI355X (8192^3, clocks per K step): scales as
+// [rows, K/32] in 4-step blocks 2,700, in 8-step blocks 2,600 (a copy of
+// 16-byte pieces of 32 or 64 rows costs several times one of whole lines,
+// and each step took 16 byte reads); rearranged 2,350-2,390, where no scale
+// traffic at all gives 2,350.
 // The MFMAs are inline asm on AGPR accumulators ("+a"): with the builtin the
 // compiler's register allocation rotated the 256 accumulators through copies
 // and spilled.  The asm keeps the MFMAs out of the compiler's hazard checks,
 // so the loop itself orders the accumulators' other accesses behind wait
 // states: the zeroing before the first MFMA and the reads after the last.
 
-template <int FA, int FB>
+// acc += B fragment x A fragment with their E8M0 scales; SEL picks the scale
+// byte of the two scale registers (op_sel / op_sel_hi of the scale operands).
+#define TEMX_MFMA_ASM(MODS)                                                                          \
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 " MODS                     \
+               : "+a"(acc) : "v"(bv), "v"(av), "v"(bs), "v"(as))
+#define TEMX_MFMA_FMT(SELMODS)                                                                       \
+  if constexpr (FA == TE_E4M3 && FB == TE_E4M3) TEMX_MFMA_ASM(SELMODS);                             \
+  else if constexpr (FA == TE_E4M3) TEMX_MFMA_ASM(SELMODS " cbsz:1"); /* B (the first operand) E5M2 */ \
+  else if constexpr (FB == TE_E4M3) TEMX_MFMA_ASM(SELMODS " blgp:1"); /* A E5M2 */                   \
+  else TEMX_MFMA_ASM(SELMODS " cbsz:1 blgp:1");
+
+template <int FA, int FB, int SEL = 0>
 __device__ __forceinline__ void mfma_acc(v4f& acc, const v8i& bv, int bs, const v8i& av, int as) {
-  if constexpr (FA == TE_E4M3 && FB == TE_E4M3)
-    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
-                 : "+a"(acc) : "v"(bv), "v"(av), "v"(bs), "v"(as));
-  else if constexpr (FA == TE_E4M3)  // B operand (the instruction's first) E5M2
-    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:1"
-                 : "+a"(acc) : "v"(bv), "v"(av), "v"(bs), "v"(as));
-  else if constexpr (FB == TE_E4M3)  // A operand E5M2
-    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] blgp:1"
-                 : "+a"(acc) : "v"(bv), "v"(av), "v"(bs), "v"(as));
-  else
-    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:1 blgp:1"
-                 : "+a"(acc) : "v"(bv), "v"(av), "v"(bs), "v"(as));
+  if constexpr (SEL == 0) {
+    TEMX_MFMA_FMT("op_sel_hi:[0,0,0]")
+  } else if constexpr (SEL == 1) {
+    TEMX_MFMA_FMT("op_sel:[1,1,0] op_sel_hi:[0,0,0]")
+  } else if constexpr (SEL == 2) {
+    TEMX_MFMA_FMT("op_sel_hi:[1,1,0]")
+  } else {
+    TEMX_MFMA_FMT("op_sel:[1,1,0] op_sel_hi:[1,1,0]")
+  }
 }
+#undef TEMX_MFMA_FMT
+#undef TEMX_MFMA_ASM
 
 // m0 <- an LDS address, for the direct-to-LDS copies that follow
 __device__ __forceinline__ void set_m0(uint32_t lds_addr) { asm volatile("s_mov_b32 m0, %0" ::"s"(lds_addr) : "memory"); }
@@ -579,14 +594,16 @@ __device__ __forceinline__ void lds_dma16_imm(const i32x4& rsrc, int voff, int s
 
 #define TEMX_SCHED_BARRIER() __builtin_amdgcn_sched_barrier(0)
 
+// MXFP8 scales come in the layout of scale_blocks_kernel (a_blk / b_blk: the
+// byte offset of one scale block of A / B, rows x 32).
 template <int FA, int FB, int SM>
 __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const Operand& A, const Operand& B,
-                                          int64_t K64, int wave, int lane) {
+                                          int64_t K64, int wave, int lane, int a_blk = 0, int b_blk = 0) {
   static_assert(SM == SM_MX || SM == SM_PT, "E8M0 block scales or none");
   using LY = Big4;
   constexpr int kNcg = 3;                            // column groups that carry the copies
   constexpr int kScaleSlot = (4 * 8 * kNcg) / 16;    // the slot of data copy 4, which sets m0 again
-  const int K = (int)K64, KS = K / 32;
+  const int K = (int)K64;
   const int kt_n = K / BK;  // a multiple of 8, > 0
   const int wm = wave >> 1, wn = wave & 1;
   // zeros into the AGPRs here, ahead of the copies below, and wait states after them: the compiler
@@ -607,14 +624,16 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
   const int chunk_e = (lane & 7) ^ (lane >> 4);
   int vo_e = (64 * wave + (lane >> 3)) * K + chunk_e * 16;
   int vo_o = (64 * wave + (lane >> 3)) * K + (chunk_e ^ 4) * 16;
-  int vo_s = (lane >> 1) * KS + 16 * (lane & 1);  // scale slice: lane l takes row l/2, bytes 16 (l%2) ..
+  int vo_s = 16 * lane;  // a scale slice is 1 KB in a row (32 rows of 32 bytes)
   // fragment reads: lane 16 g + r reads logical chunks g and g + 4 of row r of each fragment
   const int g = lane >> 4, r = lane & 15;
   const int lane_off = r * BK + ((g ^ swz(r)) << 4);
   int ra_off = wm * 128 * BK + lane_off;                                  // + 2 KB j
   int rb_off = LY::kHalf + wn * 128 * BK + lane_off;                      // + 2 KB i
-  int sa_off = (wm * 128 + r) * LY::kScaleRow + g;                        // + 512 j + 4 (kt % 8)
-  int sb_off = LY::BM * LY::kScaleRow + (wn * 128 + r) * LY::kScaleRow + g;  // + 512 i
+  // a scale read: lane (g, r) takes the dword of block g of row r for 4 steps (a row's 32 bytes are
+  // [block][step]); the MFMA picks the step's byte
+  int sa_off = (wm * 128 + r) * LY::kScaleRow + 8 * g;                        // + 512 j + 4 (kt % 8 / 4)
+  int sb_off = LY::BM * LY::kScaleRow + (wn * 128 + r) * LY::kScaleRow + 8 * g;  // + 512 i
   asm volatile("" : "+v"(vo_e), "+v"(vo_o), "+v"(vo_s), "+v"(ra_off), "+v"(rb_off), "+v"(sa_off), "+v"(sb_off));
 
   auto copy = [&](int c, int kbase, uint32_t l_stage) __attribute__((always_inline)) {
@@ -638,17 +657,23 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
     blk = __builtin_amdgcn_readfirstlane(blk);
     asm volatile("" : "+s"(blk));
     set_m0((uint32_t)__builtin_amdgcn_readfirstlane((int)(l_sbuf + s * 1024)));
-    const int so = __builtin_amdgcn_readfirstlane(32 * (s & 7) * KS) + 32 * blk;
+    const int so = __builtin_amdgcn_readfirstlane(1024 * (s & 7)) + blk * (k < 2 ? a_blk : b_blk);
     if (k < 2) lds_dma16_imm<0>(A.scale, vo_s, so);
     else lds_dma16_imm<0>(B.scale, vo_s, so);
   };
-  auto rd = [&](const uint8_t* stg, const uint8_t* sbuf, int off, int soff, int f, int sub)
+  int held[16];  // each fragment's scale dword of the current 4 steps (A 0..7, B 8..15)
+  auto rd = [&](const uint8_t* stg, const uint8_t* sbuf, int off, int soff, int f, int sub, int h)
                 __attribute__((always_inline)) {
     Frag fr;
     const uint4 lo = *reinterpret_cast<const uint4*>(stg + off + f * 16 * BK);
     const uint4 hi = *reinterpret_cast<const uint4*>(stg + (off ^ 64) + f * 16 * BK);
     fr.v = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    fr.s = SM == SM_PT ? 127 : (int)sbuf[soff + f * 16 * LY::kScaleRow + 4 * sub];
+    if constexpr (SM == SM_PT) {
+      fr.s = 127;  // 2^0 in every byte the MFMA may pick
+    } else {
+      if ((sub & 3) == 0) held[h] = *reinterpret_cast<const int*>(sbuf + soff + f * 16 * LY::kScaleRow + sub);
+      fr.s = held[h];
+    }
     return fr;
   };
 
@@ -664,9 +689,9 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Frag Af0, Bf[3];  // the step's first fragments, read during the previous step
-  Af0 = rd(lds, lds + LY::kOffScale, ra_off, sa_off, 0, 0);
+  Af0 = rd(lds, lds + LY::kOffScale, ra_off, sa_off, 0, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) Bf[i] = rd(lds, lds + LY::kOffScale, rb_off, sb_off, i, 0);
+  for (int i = 0; i < 3; ++i) Bf[i] = rd(lds, lds + LY::kOffScale, rb_off, sb_off, i, 0, 8 + i);
 
   auto step = [&](int kt, auto s8c, auto more_c) __attribute__((always_inline)) {
     constexpr int S8 = decltype(s8c)::value;  // kt % 8
@@ -694,9 +719,9 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int slot = 8 * j + i;
-        mfma_acc<FA, FB>(acc[i][j], Bv[i].v, Bv[i].s, Av[j & 1].v, Av[j & 1].s);
-        if (j == 0 && i + 3 < 8) Bv[i + 3] = rd(cur, sbuf, rb_off, sb_off, i + 3, S8);
-        if (j < 7 && i == 4) Av[(j + 1) & 1] = rd(cur, sbuf, ra_off, sa_off, j + 1, S8);
+        mfma_acc<FA, FB, SM == SM_MX ? (S8 & 3) : 0>(acc[i][j], Bv[i].v, Bv[i].s, Av[j & 1].v, Av[j & 1].s);
+        if (j == 0 && i + 3 < 8) Bv[i + 3] = rd(cur, sbuf, rb_off, sb_off, i + 3, S8, 8 + i + 3);
+        if (j < 7 && i == 4) Av[(j + 1) & 1] = rd(cur, sbuf, ra_off, sa_off, j + 1, S8, j + 1);
         if (SM == SM_MX && S8 < 4 && slot == kScaleSlot)
           copy_scales((kt >> 3) + 1, l0 + LY::kOffScale + ((((kt >> 3) + 1) & 1) * LY::kScaleBuf), S8);
         if (MORE) {
@@ -705,8 +730,8 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
             if ((c * 8 * kNcg) / 16 == slot) copy(c, kbase_n, l_nxt);
         }
         if (MORE && j == 7) {
-          if (i == 0) Af0 = rd(nxt, sbuf_n, ra_off, sa_off, 0, (S8 + 1) & 7);
-          if (i >= 1 && i <= 3) Bf[i - 1] = rd(nxt, sbuf_n, rb_off, sb_off, i - 1, (S8 + 1) & 7);
+          if (i == 0) Af0 = rd(nxt, sbuf_n, ra_off, sa_off, 0, (S8 + 1) & 7, 0);
+          if (i >= 1 && i <= 3) Bf[i - 1] = rd(nxt, sbuf_n, rb_off, sb_off, i - 1, (S8 + 1) & 7, 8 + i - 1);
         }
         TEMX_SCHED_BARRIER();
       }
@@ -1107,21 +1132,63 @@ __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
   finish_tile<LY, EPI, OUT, SM>(acc, lds, p, m0, n0, wave, lane);
 }
 
-// Dense on the 4-wave big tile (MXFP8 or per-tensor operands, K % 1024 == 0):
-// one wave per SIMD, so the whole register file is the wave's.
+// The E8M0 scales of an operand [rows, K/32] rearranged for the 4-wave tile:
+// blocks of 8 K steps (32 scale bytes of a row), block-major, each row's 32
+// bytes ordered [32-block g][step s] (byte 8 g + s) instead of [s][g]:
+//   out[blk][row][8 g + s] = in[row][4 (8 blk + s) + g].
+// A tile's scale block is then one contiguous run per operand (its copies
+// read 8 whole lines per instruction instead of 32 partial ones), and a lane
+// reads the scales of 4 steps of its block with one dword read, the MFMA
+// picking the step's byte.  One thread per (row, block); K % 1024 == 0.
+__global__ __launch_bounds__(256) void scale_blocks_kernel(const uint8_t* __restrict__ in, int64_t rows, int64_t ks,
+                                                           uint8_t* __restrict__ out) {
+  const int64_t nblk = ks / 32;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * nblk) return;
+  const int64_t row = idx / nblk, blk = idx - row * nblk;
+  const uint4* src = reinterpret_cast<const uint4*>(in + row * ks + blk * 32);
+  const uint4 p0 = src[0], p1 = src[1];
+  const uint32_t d[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};  // d[s]: blocks 0..3 of step s
+  uint32_t o[8];
+#pragma unroll
+  for (int gb = 0; gb < 4; ++gb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) w |= ((d[4 * h + t] >> (8 * gb)) & 0xFFu) << (8 * t);
+      o[2 * gb + h] = w;
+    }
+  uint4* dst = reinterpret_cast<uint4*>(out + blk * rows * 32 + row * 32);
+  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// Dense on the 4-wave big tile (K % 1024 == 0): one wave per SIMD, so the
+// whole register file is the wave's.  MXFP8 operands come with their scales
+// in the layout of scale_blocks_kernel (p.a_scale / p.b_scale point at the
+// rearranged copies); per-tensor operands have none.
 template <int FA, int FB, int EPI, int OUT, int SM = SM_MX>
 __global__ __launch_bounds__(Big4::kThreads, 1) void mx_gemm4_kernel(GemmParams p) {
   using LY = Big4;
+  constexpr bool kBlk = SM == SM_MX;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int tm, tn;
   raster_tile(blockIdx.x, (int)((p.M + LY::BM - 1) / LY::BM), (int)((p.N + LY::BN - 1) / LY::BN), tm, tn);
   const int64_t m0 = (int64_t)tm * LY::BM, n0 = (int64_t)tn * LY::BN;
-  const Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, LY::BM);
-  const Operand B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, LY::BN);
+  Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, LY::BM);
+  Operand B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, LY::BN);
+  if constexpr (kBlk) {
+    // the tile's rows of every block: block blk at + blk * rows * 32 (the soffset), rows past the
+    // operand's end read the next block (never stored) or zeros past the array
+    const int64_t nblk = p.K / 1024;
+    A.scale = make_rsrc(p.a_scale + m0 * 32, (nblk * p.M - m0) * 32);
+    B.scale = make_rsrc(p.b_scale + n0 * 32, (nblk * p.N - n0) * 32);
+  }
   v4f acc[LY::FRN][LY::FRM];
-  mainloop4<FA, FB, SM>(lds, acc, A, B, p.K, wave, lane);
+  mainloop4<FA, FB, SM>(lds, acc, A, B, p.K, wave, lane, (int)(p.M * 32), (int)(p.N * 32));
   finish_tile<LY, EPI, OUT, SM>(acc, lds, p, m0, n0, wave, lane);
 }
 
@@ -1219,6 +1286,25 @@ inline dim3 tile_grid(Tile t, int64_t M, int64_t N) {
 // Shape limits of the dense GEMMs beyond the divisibility rules: tile copies
 // use 32-bit buffer offsets (up to 225 K bytes) and a tile's rows x K bytes
 // must fit a buffer resource, so K <= 2^23; M, N and the tile count fit int.
+// The 4-wave MXFP8 path: the tile choice is the big tile, K is whole 8-step
+// scale blocks, and each operand's rearranged scales fit 32-bit offsets.  Its
+// workspace holds the rearranged scales of A, then (256-byte aligned) of B.
+inline bool four_wave_mx(int64_t M, int64_t N, int64_t K) {
+  const int64_t lim = ((int64_t)1 << 31) - 4096;
+  return pick_tile(M, N, K) == Tile::Big && K % Big4::kKAlign == 0 && M * (K / 32) < lim && N * (K / 32) < lim;
+}
+inline size_t scale_blocks_b_offset(int64_t M, int64_t K) { return (size_t)((M * (K / 32) + 255) / 256 * 256); }
+inline size_t scale_blocks_bytes(int64_t M, int64_t N, int64_t K) {
+  return scale_blocks_b_offset(M, K) + (size_t)(N * (K / 32));
+}
+
+inline te_status launch_scale_blocks(const uint8_t* s, int64_t rows, int64_t K, uint8_t* out, hipStream_t stream) {
+  const int64_t threads = rows * (K / 1024);
+  hipLaunchKernelGGL(scale_blocks_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, s, rows,
+                     K / 32, out);
+  return launch_status();
+}
+
 inline bool dense_shape_ok(int64_t M, int64_t N, int64_t K) {
   return M <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 23) &&
          ((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 31);

@@ -98,6 +98,36 @@ def test_four_wave_tile_exact_integer(fa, fb, K):
     assert np.array_equal(host(d[rows]).astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
+def test_four_wave_tile_matches_eight_wave_tile(epi):
+    # the same GEMM with the workspace (the 4-wave kernel after its scales are rearranged into the
+    # workspace) and without (the 8-wave kernel on the scales as they are): the same D and aux, bit
+    # for bit, on real quantized data with a 48-row and an 80-column tail
+    M, N, K = 4096 + 48, 4096 + 80, 2048
+    a = workloads.normal_bf16(91, 0, (M, K), 1.0, 0.01)
+    b = workloads.normal_bf16(91, 1, (N, K), 0.05)
+    qa, sa, _, _ = te().mxfp8_quantize(dev(a), "e4m3", "row")
+    qb, sb, _, _ = te().mxfp8_quantize(dev(b), "e4m3", "row")
+    bias = None if epi == "none" else dev(workloads.normal_bf16(92, N, (N,), 0.5))
+    need = te().te_mxfp8_gemm_workspace_size(M, N, K)
+    assert need == (M * K // 32 + 255) // 256 * 256 + N * K // 32
+    d4, aux4 = te().mxfp8_gemm(qa, sa, "e4m3", qb, sb, "e4m3", epi, bias, workspace="auto")
+    d8, aux8 = te().mxfp8_gemm(qa, sa, "e4m3", qb, sb, "e4m3", epi, bias, workspace=None)
+    torch.cuda.synchronize()
+    assert torch.equal(d4, d8)
+    if epi == "bias_gelu_aux":
+        assert torch.equal(aux4, aux8)
+
+
+def test_gemm_workspace_size():
+    # only the 4-wave path takes a workspace: big-tile grids with K % 1024 == 0
+    ws = te().te_mxfp8_gemm_workspace_size
+    assert ws(8192, 8192, 8192) == 2 * 8192 * 256
+    assert ws(8192, 8192, 1152) == 0          # K not whole 8-step scale blocks
+    assert ws(4096, 1024, 4096) == 0          # a small-tile grid
+    assert ws(0, 8192, 8192) == 0 and ws(8192, 8192, 100) == 0
+
+
 def test_gemm_k_zero_gives_epilogue_of_zero():
     M, N = 64, 48
     bias = workloads.normal_bf16(6, 1, (N,), 1.0)
