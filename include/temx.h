@@ -256,8 +256,17 @@ te_status te_mxfp8_quantize_bgrad(const uint16_t* x, int64_t rows, int64_t cols,
  *   [HK-PR] checks; M and N need not be multiples of the tile size);
  *   K <= 2^23 (the tile copies use 32-bit offsets), M, N < 2^31 - 256.
  *   M == 0 or N == 0 enqueues nothing; K == 0 gives D = epi(0).
- *   workspace: none is needed (te_mxfp8_gemm_workspace_size returns 0);
- *   pass NULL / 0.
+ *   workspace: optional device scratch, owned by the caller and free for
+ *   reuse once the GEMM has run (stream order).  te_mxfp8_gemm_workspace_size
+ *   returns the bytes that enable the faster path for the shape on the
+ *   current device, 0 where there is none: grids the 256 x 256 tile serves
+ *   with K % 1024 == 0 take (M + N) K / 32 bytes (A's part rounded up to 256)
+ *   for a rearranged copy of both operands' E8M0 scales (blocks of 8 K steps,
+ *   a tile row's 32 bytes contiguous), written by the GEMM itself on the same
+ *   stream.  With a NULL workspace, a smaller one, one not 256-byte aligned,
+ *   or scale arrays not 16-byte aligned, the GEMM runs without it (same
+ *   results, bit for bit); a workspace is never an error.  Calls that share
+ *   one workspace must be ordered on one stream.
  */
 size_t te_mxfp8_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
 te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt,
@@ -276,8 +285,8 @@ te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt
  *   a_scale_inv, b_scale_inv   float [1] each, device (e.g. q_scale_inv_out
  *                    of te_fp8_cast_delayed_scaling or scale_inv_out of
  *                    te_fp8_cast_current_scaling)
- *   d, d_dtype, bias, aux, shapes, workspace: as te_mxfp8_gemm; epi is
- *   TE_EPI_NONE, TE_EPI_BIAS or TE_EPI_BIAS_GELU_AUX.
+ *   d, d_dtype, bias, aux, shapes: as te_mxfp8_gemm; epi is TE_EPI_NONE,
+ *   TE_EPI_BIAS or TE_EPI_BIAS_GELU_AUX; workspace: none is used (NULL / 0).
  */
 te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_dtype a_fmt,
                       const uint8_t* b, const float* b_scale_inv, te_dtype b_fmt,
@@ -297,7 +306,8 @@ te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_dtype a_fmt
  *   d        uint8 [M, N] codes, d_fmt TE_E4M3 or TE_E5M2
  *   d_scale  uint8 [M, N/32] E8M0 scales
  *   aux      as te_mxfp8_gemm (bf16 pre-activation, BIAS_GELU_AUX only)
- *   Shapes as te_mxfp8_gemm, and N % 32 == 0.
+ *   Shapes as te_mxfp8_gemm, and N % 32 == 0; workspace as te_mxfp8_gemm
+ *   (te_mxfp8_gemm_workspace_size gives its size).
  */
 te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scale, te_dtype a_fmt,
                               const uint8_t* b, const uint8_t* b_scale, te_dtype b_fmt,

@@ -42,7 +42,11 @@ def test_status_strings():
 
 
 def test_workspace_queries():
-    assert te.te_mxfp8_gemm_workspace_size(8192, 8192, 8192) == 0
+    # the rearranged E8M0 scales of the 4-wave path (big-tile grids, K % 1024 == 0); without a GPU
+    # the library takes a 256-CU device
+    assert te.te_mxfp8_gemm_workspace_size(8192, 8192, 8192) == 2 * 8192 * 8192 // 32
+    assert te.te_mxfp8_gemm_workspace_size(8192, 8192, 1152) == 0
+    assert te.te_mxfp8_gemm_workspace_size(-1, 8192, 8192) == 0
     assert te.te_amax_workspace_size(0) == 4
     assert te.te_amax_workspace_size(8192 * 8192) == 4 * 1024
     assert te.te_amax_workspace_size(4096) == 4
