@@ -258,9 +258,9 @@ def build_step(workload, torch, te, workloads):
         bias = upload(g.bias.make()) if g.bias is not None else None
         aux = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev) if g.epilogue == "bias_gelu_aux" else None
         # the GEMM's workspace (allocated here, outside the timed region): with it the 4-wave kernel
-        # runs, after two small kernels that rearrange the operands' scales into it
+        # runs, after a small kernel that rearranges the operands' scales into it
         ws = te.gemm_workspace(g.M, g.N, g.K, dev)
-        gemm_kernels = (["scale_blocks_kernel"] * 2 + ["mx_gemm4_kernel"]) if ws is not None else ["mx_gemm_kernel"]
+        gemm_kernels = ["scale_blocks_kernel", "mx_gemm4_kernel"] if ws is not None else ["mx_gemm_kernel"]
         if g.mx_out:
             outs = qbufs(g.M, g.N, "row")
             mx_outputs[g.name] = outs

@@ -125,8 +125,7 @@ te_status launch_big_mx(GemmParams p, te_dtype a_fmt, te_dtype b_fmt, te_epilogu
       ((uintptr_t)workspace & 255u) == 0 && aligned16(p.a_scale) && aligned16(p.b_scale)) {
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     uint8_t* bs = ws + scale_blocks_b_offset(M, K);
-    if (launch_scale_blocks(p.a_scale, M, K, ws, stream) != TE_OK) return TE_ERR_HIP;
-    if (launch_scale_blocks(p.b_scale, N, K, bs, stream) != TE_OK) return TE_ERR_HIP;
+    if (launch_scale_blocks(p.a_scale, M, ws, p.b_scale, N, bs, K, stream) != TE_OK) return TE_ERR_HIP;
     p.a_scale = ws;
     p.b_scale = bs;
     return launch2<Big4, false>(p, a_fmt, b_fmt, epi, out, grid, stream);

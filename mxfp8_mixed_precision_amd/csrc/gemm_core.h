@@ -124,21 +124,21 @@ using SmallDeep = Cfg<128, 128, 2, 2, 4, 4>;
 // The 4-wave big tile (mainloop4): 256 x 256, one wave per SIMD in 2 x 2,
 // each 128 x 128 (8 x 8 MFMA tiles, 256 fp32 accumulators held in AGPRs).
 // LDS: two 64-KB stages (A codes [256][128], then B codes), then two scale
-// buffers of 8 K steps each (32 E8M0 bytes per tile row: A rows, then B
-// rows), 160 KB in all.  For K % 1024 == 0 (whole scale blocks).
+// buffers of 4 K steps each (16 E8M0 bytes per tile row: A rows, then B
+// rows), 144 KB in all.  For K % 1024 == 0: the loop runs 8 steps a turn.
 struct Big4 {
   static constexpr int BM = 256, BN = 256, NWM = 2, NWN = 2, NW = 4, kThreads = 256;
   static constexpr int WTM = 128, WTN = 128, FRM = 8, FRN = 8;
   static constexpr int kHalf = BM * 128;              // A codes of a stage; B codes follow
   static constexpr int kStage = 2 * kHalf;
-  static constexpr int kScaleSteps = 8;
+  static constexpr int kScaleSteps = 4;
   static constexpr int kScaleRow = 4 * kScaleSteps;   // bytes per tile row and scale block
   static constexpr int kScaleBuf = (BM + BN) * kScaleRow;
   static constexpr int kOffScale = 2 * kStage;
   static constexpr int kLds = kOffScale + 2 * kScaleBuf;
-  static constexpr int kKAlign = 128 * kScaleSteps;   // K must be a multiple of this
+  static constexpr int kKAlign = 1024;                // K must be a multiple of this
 };
-static_assert(Big4::kLds == 160 * 1024, "the 4-wave tile takes all of a CU's LDS");
+static_assert(Big4::kLds == 144 * 1024, "the 4-wave tile's LDS");
 
 constexpr int kGroupM = 4;      // row-tile band of the raster order
 constexpr int kMaxGroups = 1024;
@@ -538,15 +538,15 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
 //  * group 7 reads step kt + 1's first fragments.
 // One m0 write serves four copies: a copy's immediate offset moves both its
 // global and its LDS address (the soffset takes the global part back).
-// Scales: blocks of 8 K steps in the layout scale_blocks_kernel writes (a
-// tile row's 32 bytes of a block contiguous, rows consecutive, each row
-// [32-block][step]), so a scale copy reads 32 rows' bytes as 1 KB in a row,
-// and a lane reads its block's bytes for 4 steps with one dword read, the
-// MFMA selecting the step's byte.  Block b + 1 is copied during steps 8b ..
-// 8b + 3 (one 32-row slice per wave and step) into the buffer block b - 1
-// used.  Measured on MI355X (8192^3, clocks per K step): scales as
+// Scales: blocks of 4 K steps in the layout scale_blocks_kernel writes (a
+// tile row's 16 bytes of a block contiguous, rows consecutive, each row
+// [32-block][step]), so a scale copy reads 64 rows' bytes as 1 KB in a row,
+// and a lane reads its block's bytes for the 4 steps with one dword read,
+// the MFMA selecting the step's byte.  Block b + 1 is copied during steps 4b
+// and 4b + 1 (one 64-row slice per wave and step) into the buffer block
+// b - 1 used.  Measured on MI355X (8192^3, clocks per K step): scales as
 // [rows, K/32] in 4-step blocks 2,700, in 8-step blocks 2,600 (a copy of
-// 16-byte pieces of 32 or 64 rows costs several times one of whole lines,
+// 16-byte pieces of 64 or 32 rows costs several times one of whole lines,
 // and each step took 16 byte reads); rearranged 2,350-2,390, where no scale
 // traffic at all gives 2,350.
 // The MFMAs are inline asm on AGPR accumulators ("+a"): with the builtin the
@@ -594,13 +594,26 @@ __device__ __forceinline__ void lds_dma16_imm(const i32x4& rsrc, int voff, int s
 
 #define TEMX_SCHED_BARRIER() __builtin_amdgcn_sched_barrier(0)
 
+// The lane index, computed afresh where this is called (opaque to the
+// compiler): after the 4-wave main loop the epilogue derives its per-lane
+// offsets from it instead of keeping the prologue's values live through the
+// loop, which has no VGPR to spare.
+__device__ __forceinline__ int lane_id_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // MXFP8 scales come in the layout of scale_blocks_kernel (a_blk / b_blk: the
 // byte offset of one scale block of A / B, rows x 32).
 template <int FA, int FB, int SM>
 __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const Operand& A, const Operand& B,
-                                          int64_t K64, int wave, int lane, int a_blk = 0, int b_blk = 0) {
+                                          int64_t K64, int wave, int a_blk = 0, int b_blk = 0) {
   static_assert(SM == SM_MX || SM == SM_PT, "E8M0 block scales or none");
   using LY = Big4;
+  // the per-lane offsets below start from a fresh lane index, so none of them is computed ahead of
+  // this function and kept live through it
+  const int lane = lane_id_fresh();
   constexpr int kNcg = 3;                            // column groups that carry the copies
   constexpr int kScaleSlot = (4 * 8 * kNcg) / 16;    // the slot of data copy 4, which sets m0 again
   const int K = (int)K64;
@@ -608,11 +621,14 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
   const int wm = wave >> 1, wn = wave & 1;
   // zeros into the AGPRs here, ahead of the copies below, and wait states after them: the compiler
   // cannot see the MFMAs read them (a VALU write read as an MFMA's accumulator input needs a gap)
+  // (the zero comes from an opaque move here, so the compiler keeps no copy of it live from elsewhere)
+  float zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      acc[i][j] = v4f{zero, zero, zero, zero};
       asm volatile("" : "+a"(acc[i][j]));
     }
   asm volatile("s_nop 7" ::: "memory");
@@ -624,16 +640,16 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
   const int chunk_e = (lane & 7) ^ (lane >> 4);
   int vo_e = (64 * wave + (lane >> 3)) * K + chunk_e * 16;
   int vo_o = (64 * wave + (lane >> 3)) * K + (chunk_e ^ 4) * 16;
-  int vo_s = 16 * lane;  // a scale slice is 1 KB in a row (32 rows of 32 bytes)
+  int vo_s = 16 * lane;  // a scale slice is 1 KB in a row (64 rows of 16 bytes)
   // fragment reads: lane 16 g + r reads logical chunks g and g + 4 of row r of each fragment
   const int g = lane >> 4, r = lane & 15;
   const int lane_off = r * BK + ((g ^ swz(r)) << 4);
   int ra_off = wm * 128 * BK + lane_off;                                  // + 2 KB j
   int rb_off = LY::kHalf + wn * 128 * BK + lane_off;                      // + 2 KB i
-  // a scale read: lane (g, r) takes the dword of block g of row r for 4 steps (a row's 32 bytes are
-  // [block][step]); the MFMA picks the step's byte
-  int sa_off = (wm * 128 + r) * LY::kScaleRow + 8 * g;                        // + 512 j + 4 (kt % 8 / 4)
-  int sb_off = LY::BM * LY::kScaleRow + (wn * 128 + r) * LY::kScaleRow + 8 * g;  // + 512 i
+  // a scale read: lane (g, r) takes the dword of block g of row r for the 4 steps (a row's 16 bytes
+  // are [block][step]); the MFMA picks the step's byte
+  int sa_off = (wm * 128 + r) * LY::kScaleRow + 4 * g;                        // + 256 j
+  int sb_off = LY::BM * LY::kScaleRow + (wn * 128 + r) * LY::kScaleRow + 4 * g;  // + 256 i
   asm volatile("" : "+v"(vo_e), "+v"(vo_o), "+v"(vo_s), "+v"(ra_off), "+v"(rb_off), "+v"(sa_off), "+v"(sb_off));
 
   auto copy = [&](int c, int kbase, uint32_t l_stage) __attribute__((always_inline)) {
@@ -651,14 +667,15 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
       default: lds_dma16_imm<3072>(rs, vo, so); break;
     }
   };
-  // scale slice s = wave + 4k of block blk: slices 0..7 are A rows 32 s .., 8..15 B rows
+  // scale slice s = wave + 4k of block blk (1 KB: 64 rows of 16 bytes): k = 0 A rows 64 w ..,
+  // k = 1 B rows 64 w ..
   auto copy_scales = [&](int blk, uint32_t l_sbuf, int k) __attribute__((always_inline)) {
     const int s = wave + 4 * k;
     blk = __builtin_amdgcn_readfirstlane(blk);
     asm volatile("" : "+s"(blk));
     set_m0((uint32_t)__builtin_amdgcn_readfirstlane((int)(l_sbuf + s * 1024)));
-    const int so = __builtin_amdgcn_readfirstlane(1024 * (s & 7)) + blk * (k < 2 ? a_blk : b_blk);
-    if (k < 2) lds_dma16_imm<0>(A.scale, vo_s, so);
+    const int so = __builtin_amdgcn_readfirstlane(1024 * wave) + blk * (k == 0 ? a_blk : b_blk);
+    if (k == 0) lds_dma16_imm<0>(A.scale, vo_s, so);
     else lds_dma16_imm<0>(B.scale, vo_s, so);
   };
   int held[16];  // each fragment's scale dword of the current 4 steps (A 0..7, B 8..15)
@@ -671,7 +688,7 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
     if constexpr (SM == SM_PT) {
       fr.s = 127;  // 2^0 in every byte the MFMA may pick
     } else {
-      if ((sub & 3) == 0) held[h] = *reinterpret_cast<const int*>(sbuf + soff + f * 16 * LY::kScaleRow + sub);
+      if ((sub & 3) == 0) held[h] = *reinterpret_cast<const int*>(sbuf + soff + f * 16 * LY::kScaleRow);
       fr.s = held[h];
     }
     return fr;
@@ -684,7 +701,7 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
   for (int c = 0; c < 16; ++c) copy(c, 0, l0);
   if constexpr (SM == SM_MX) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) copy_scales(0, l0 + LY::kOffScale, k);
+    for (int k = 0; k < 2; ++k) copy_scales(0, l0 + LY::kOffScale, k);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -699,8 +716,8 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
     const uint8_t* cur = lds + (S8 & 1) * LY::kStage;
     const uint8_t* nxt = lds + ((S8 & 1) ^ 1) * LY::kStage;
     const uint32_t l_nxt = l0 + ((S8 & 1) ^ 1) * LY::kStage;
-    const uint8_t* sbuf = lds + LY::kOffScale + ((kt >> 3) & 1) * LY::kScaleBuf;
-    const uint8_t* sbuf_n = lds + LY::kOffScale + (((kt + 1) >> 3) & 1) * LY::kScaleBuf;
+    const uint8_t* sbuf = lds + LY::kOffScale + ((kt >> 2) & 1) * LY::kScaleBuf;
+    const uint8_t* sbuf_n = lds + LY::kOffScale + (((kt + 1) >> 2) & 1) * LY::kScaleBuf;
     // opaque, so that the copies' offsets are a few hoisted constants plus this
     int kbase_n = __builtin_amdgcn_readfirstlane((kt + 1) * BK);
     asm volatile("" : "+s"(kbase_n));
@@ -722,8 +739,8 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
         mfma_acc<FA, FB, SM == SM_MX ? (S8 & 3) : 0>(acc[i][j], Bv[i].v, Bv[i].s, Av[j & 1].v, Av[j & 1].s);
         if (j == 0 && i + 3 < 8) Bv[i + 3] = rd(cur, sbuf, rb_off, sb_off, i + 3, S8, 8 + i + 3);
         if (j < 7 && i == 4) Av[(j + 1) & 1] = rd(cur, sbuf, ra_off, sa_off, j + 1, S8, j + 1);
-        if (SM == SM_MX && S8 < 4 && slot == kScaleSlot)
-          copy_scales((kt >> 3) + 1, l0 + LY::kOffScale + ((((kt >> 3) + 1) & 1) * LY::kScaleBuf), S8);
+        if (SM == SM_MX && (S8 & 3) < 2 && slot == kScaleSlot)
+          copy_scales((kt >> 2) + 1, l0 + LY::kOffScale + ((((kt >> 2) + 1) & 1) * LY::kScaleBuf), S8 & 3);
         if (MORE) {
 #pragma unroll
           for (int c = 0; c < 16; ++c)
@@ -779,25 +796,24 @@ __device__ __forceinline__ float mul_rn(float a, float b) {
 // with the bias add), fragment by fragment: the per-tensor mode of the
 // 4-wave tile, whose 256 accumulators cannot all pass through VGPRs at once.
 template <class LY, int EPI, int OUT, bool SCALE = false>
-__device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], void* d, uint16_t* aux,
+__device__ __forceinline__ void epilogue(v4f (&acc)[LY::FRN][LY::FRM], void* d, uint16_t* aux,
                                          const uint16_t* bias, int64_t m0, int64_t m_end, int64_t n0, int64_t N,
                                          int wave, int lane, float beta = 1.0f, float alpha = 1.0f) {
   const int wm = wave / LY::NWN, wn = wave % LY::NWN;
   const int g = lane >> 4, r = lane & 15;
-  // bias of the lane's columns, all fragments
+  // bias of the lane's columns, all fragments (columns past N, never stored, read column 0's)
   float bv[LY::FRN][4];
 #pragma unroll
   for (int i = 0; i < LY::FRN; ++i) {
     const int64_t n = n0 + wn * LY::WTN + 16 * i + 4 * g;
-    bv[i][0] = bv[i][1] = bv[i][2] = bv[i][3] = 0.f;
     if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
-      if (n < N) {
-        const uint2 bb = *reinterpret_cast<const uint2*>(bias + n);
-        bv[i][0] = bf16_bits_to_float(bb.x & 0xFFFFu);
-        bv[i][1] = bf16_bits_to_float(bb.x >> 16);
-        bv[i][2] = bf16_bits_to_float(bb.y & 0xFFFFu);
-        bv[i][3] = bf16_bits_to_float(bb.y >> 16);
-      }
+      const uint2 bb = *reinterpret_cast<const uint2*>(bias + (n < N ? n : 0));
+      bv[i][0] = bf16_bits_to_float(bb.x & 0xFFFFu);
+      bv[i][1] = bf16_bits_to_float(bb.x >> 16);
+      bv[i][2] = bf16_bits_to_float(bb.y & 0xFFFFu);
+      bv[i][3] = bf16_bits_to_float(bb.y >> 16);
+    } else {
+      bv[i][0] = bv[i][1] = bv[i][2] = bv[i][3] = 0.f;
     }
   }
   // row fragments outermost: a row's pieces of the wave's columns leave in consecutive stores
@@ -809,6 +825,9 @@ __device__ __forceinline__ void epilogue(const v4f (&acc)[LY::FRN][LY::FRM], voi
     for (int i = 0; i < LY::FRN; ++i) {
       const int64_t n = n0 + wn * LY::WTN + 16 * i + 4 * g;
       if (n >= N) continue;
+      // 4-wave tile: the fragment's AGPRs are read here and not hoisted above the row / column checks
+      // (256 accumulators do not all fit in VGPRs at once)
+      if constexpr (LY::FRN * LY::FRM > 32) asm volatile("" : "+a"(acc[i][j]));
       float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
       if constexpr (SCALE) {
         v0 = mul_rn(v0, alpha);
@@ -898,9 +917,27 @@ __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8
   const int g = lane >> 4, r = lane & 15;
   uint8_t* region = lds + wave * kRegion;
   const int64_t mb = m0 + wm * LY::WTM, nb = n0 + wn * LY::WTN;
-  // the bias is added in place (the accumulators are not needed afterwards): fewer live registers than
-  // keeping the bias beside them through both passes
-  if constexpr (EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX) {
+  // With up to 32 fragments the bias is added in place (the accumulators are not needed afterwards):
+  // fewer live registers than keeping the bias beside them through both passes.  The 4-wave tile's
+  // 256 accumulators live in AGPRs, where an in-place add would pull them all into VGPRs: there each
+  // pass adds the bias (held, 4 values per column fragment) fragment by fragment.
+  constexpr bool kHasBias = EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX;
+  constexpr bool kInPlace = LY::FRN * LY::FRM <= 32;
+  float bv[kInPlace ? 1 : LY::FRN][4];
+  if constexpr (kHasBias && !kInPlace) {
+#pragma unroll
+    for (int i = 0; i < LY::FRN; ++i) {
+      // columns past N (never stored) read column 0's bias: no zero defaults, whose registers the
+      // compiler may set up ahead of the main loop and keep live through it
+      const int64_t n = nb + 16 * i + 4 * g;
+      const uint2 bb = *reinterpret_cast<const uint2*>(bias + (n < N ? n : 0));
+      bv[i][0] = bf16_bits_to_float(bb.x & 0xFFFFu);
+      bv[i][1] = bf16_bits_to_float(bb.x >> 16);
+      bv[i][2] = bf16_bits_to_float(bb.y & 0xFFFFu);
+      bv[i][3] = bf16_bits_to_float(bb.y >> 16);
+    }
+  }
+  if constexpr (kHasBias && kInPlace) {
 #pragma unroll
     for (int i = 0; i < LY::FRN; ++i) {
       const int64_t n = nb + 16 * i + 4 * g;
@@ -936,12 +973,20 @@ __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8
     for (int j = 0; j < LY::FRM; ++j) {
 #pragma unroll
       for (int i = 0; i < LY::FRN; ++i) {
+        // 4-wave tile: the fragment's AGPRs are read here, one fragment at a time through VGPRs
+        if constexpr (!kInPlace) asm volatile("" : "+a"(acc[i][j]));
         float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
-        if constexpr (SCALE && EPI == TE_EPI_NONE) {  // with a bias the products went in above
+        if constexpr (SCALE && !(kHasBias && kInPlace)) {  // in place with the bias, alpha went in above
           v0 = mul_rn(v0, alpha);
           v1 = mul_rn(v1, alpha);
           v2 = mul_rn(v2, alpha);
           v3 = mul_rn(v3, alpha);
+        }
+        if constexpr (kHasBias && !kInPlace) {
+          v0 += bv[i][0];
+          v1 += bv[i][1];
+          v2 += bv[i][2];
+          v3 += bv[i][3];
         }
         uint2 w;
         if (EPI == TE_EPI_BIAS_GELU_AUX && !to_aux) {
@@ -961,6 +1006,16 @@ __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8
     asm volatile("" ::: "memory");
     store_region<LY>(region, to_aux ? aux : static_cast<uint16_t*>(d), mb, m_end, nb, N, lane);
     asm volatile("" ::: "memory");
+    if constexpr (!kInPlace && kPasses == 2) {
+      // the second pass reads the AGPRs again: without this the compiler keeps the first pass's
+      // 256 VGPR copies live between the passes
+      if (pass == 0) {
+#pragma unroll
+        for (int i = 0; i < LY::FRN; ++i)
+#pragma unroll
+          for (int j = 0; j < LY::FRM; ++j) asm volatile("" : "+a"(acc[i][j]));
+      }
+    }
   }
 }
 
@@ -1133,35 +1188,42 @@ __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
 }
 
 // The E8M0 scales of an operand [rows, K/32] rearranged for the 4-wave tile:
-// blocks of 8 K steps (32 scale bytes of a row), block-major, each row's 32
-// bytes ordered [32-block g][step s] (byte 8 g + s) instead of [s][g]:
-//   out[blk][row][8 g + s] = in[row][4 (8 blk + s) + g].
+// blocks of 4 K steps (16 scale bytes of a row), block-major, each row's 16
+// bytes ordered [32-block g][step s] (byte 4 g + s) instead of [s][g]:
+//   out[blk][row][4 g + s] = in[row][4 (4 blk + s) + g].
 // A tile's scale block is then one contiguous run per operand (its copies
-// read 8 whole lines per instruction instead of 32 partial ones), and a lane
-// reads the scales of 4 steps of its block with one dword read, the MFMA
-// picking the step's byte.  One thread per (row, block); K % 1024 == 0.
-__global__ __launch_bounds__(256) void scale_blocks_kernel(const uint8_t* __restrict__ in, int64_t rows, int64_t ks,
-                                                           uint8_t* __restrict__ out) {
-  const int64_t nblk = ks / 32;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= rows * nblk) return;
+// read 8 whole lines per instruction instead of 64 partial ones), and a lane
+// reads the scales of the block's 4 steps with one dword read, the MFMA
+// picking the step's byte.  One launch for both operands: threads
+// [0, rows_a * nblk) take A's (row, block) pairs, the rest B's.
+__global__ __launch_bounds__(256) void scale_blocks_kernel(const uint8_t* __restrict__ a_in, int64_t rows_a,
+                                                           uint8_t* __restrict__ a_out,
+                                                           const uint8_t* __restrict__ b_in, int64_t rows_b,
+                                                           uint8_t* __restrict__ b_out, int64_t ks) {
+  const int64_t nblk = ks / 16;
+  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const uint8_t* in = a_in;
+  uint8_t* out = a_out;
+  int64_t rows = rows_a;
+  if (idx >= rows_a * nblk) {
+    idx -= rows_a * nblk;
+    in = b_in;
+    out = b_out;
+    rows = rows_b;
+    if (idx >= rows_b * nblk) return;
+  }
   const int64_t row = idx / nblk, blk = idx - row * nblk;
-  const uint4* src = reinterpret_cast<const uint4*>(in + row * ks + blk * 32);
-  const uint4 p0 = src[0], p1 = src[1];
-  const uint32_t d[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};  // d[s]: blocks 0..3 of step s
-  uint32_t o[8];
+  const uint4 v = *reinterpret_cast<const uint4*>(in + row * ks + blk * 16);
+  const uint32_t d[4] = {v.x, v.y, v.z, v.w};  // d[s]: blocks 0..3 of step s
+  uint32_t o[4];
 #pragma unroll
-  for (int gb = 0; gb < 4; ++gb)
+  for (int gb = 0; gb < 4; ++gb) {
+    uint32_t w = 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) w |= ((d[4 * h + t] >> (8 * gb)) & 0xFFu) << (8 * t);
-      o[2 * gb + h] = w;
-    }
-  uint4* dst = reinterpret_cast<uint4*>(out + blk * rows * 32 + row * 32);
-  dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-  dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    for (int t = 0; t < 4; ++t) w |= ((d[t] >> (8 * gb)) & 0xFFu) << (8 * t);
+    o[gb] = w;
+  }
+  *reinterpret_cast<uint4*>(out + blk * rows * 16 + row * 16) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // Dense on the 4-wave big tile (K % 1024 == 0): one wave per SIMD, so the
@@ -1183,13 +1245,13 @@ __global__ __launch_bounds__(Big4::kThreads, 1) void mx_gemm4_kernel(GemmParams 
   if constexpr (kBlk) {
     // the tile's rows of every block: block blk at + blk * rows * 32 (the soffset), rows past the
     // operand's end read the next block (never stored) or zeros past the array
-    const int64_t nblk = p.K / 1024;
-    A.scale = make_rsrc(p.a_scale + m0 * 32, (nblk * p.M - m0) * 32);
-    B.scale = make_rsrc(p.b_scale + n0 * 32, (nblk * p.N - n0) * 32);
+    const int64_t nblk = p.K / 512;
+    A.scale = make_rsrc(p.a_scale + m0 * 16, (nblk * p.M - m0) * 16);
+    B.scale = make_rsrc(p.b_scale + n0 * 16, (nblk * p.N - n0) * 16);
   }
   v4f acc[LY::FRN][LY::FRM];
-  mainloop4<FA, FB, SM>(lds, acc, A, B, p.K, wave, lane, (int)(p.M * 32), (int)(p.N * 32));
-  finish_tile<LY, EPI, OUT, SM>(acc, lds, p, m0, n0, wave, lane);
+  mainloop4<FA, FB, SM>(lds, acc, A, B, p.K, wave, (int)(p.M * 16), (int)(p.N * 16));
+  finish_tile<LY, EPI, OUT, SM>(acc, lds, p, m0, n0, wave, lane_id_fresh());
 }
 
 // Grouped: a persistent grid walks the flat list of (expert row-tile,
@@ -1283,11 +1345,9 @@ inline dim3 tile_grid(Tile t, int64_t M, int64_t N) {
                         : dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128)));
 }
 
-// Shape limits of the dense GEMMs beyond the divisibility rules: tile copies
-// use 32-bit buffer offsets (up to 225 K bytes) and a tile's rows x K bytes
-// must fit a buffer resource, so K <= 2^23; M, N and the tile count fit int.
-// The 4-wave MXFP8 path: the tile choice is the big tile, K is whole 8-step
-// scale blocks, and each operand's rearranged scales fit 32-bit offsets.  Its
+// The 4-wave MXFP8 path: the tile choice is the big tile, K % 1024 == 0 (the
+// loop's 8-step turns), and each operand's rearranged scales fit 32-bit
+// offsets.  Its
 // workspace holds the rearranged scales of A, then (256-byte aligned) of B.
 inline bool four_wave_mx(int64_t M, int64_t N, int64_t K) {
   const int64_t lim = ((int64_t)1 << 31) - 4096;
@@ -1298,13 +1358,17 @@ inline size_t scale_blocks_bytes(int64_t M, int64_t N, int64_t K) {
   return scale_blocks_b_offset(M, K) + (size_t)(N * (K / 32));
 }
 
-inline te_status launch_scale_blocks(const uint8_t* s, int64_t rows, int64_t K, uint8_t* out, hipStream_t stream) {
-  const int64_t threads = rows * (K / 1024);
-  hipLaunchKernelGGL(scale_blocks_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, s, rows,
-                     K / 32, out);
+inline te_status launch_scale_blocks(const uint8_t* a_scale, int64_t M, uint8_t* a_out, const uint8_t* b_scale,
+                                     int64_t N, uint8_t* b_out, int64_t K, hipStream_t stream) {
+  const int64_t threads = (M + N) * (K / 512);
+  hipLaunchKernelGGL(scale_blocks_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a_scale, M,
+                     a_out, b_scale, N, b_out, K / 32);
   return launch_status();
 }
 
+// Shape limits of the dense GEMMs beyond the divisibility rules: tile copies
+// use 32-bit buffer offsets (up to 225 K bytes) and a tile's rows x K bytes
+// must fit a buffer resource, so K <= 2^23; M, N and the tile count fit int.
 inline bool dense_shape_ok(int64_t M, int64_t N, int64_t K) {
   return M <= ((int64_t)1 << 31) - 256 && N <= ((int64_t)1 << 31) - 256 && K <= ((int64_t)1 << 23) &&
          ((M + 127) / 128) * ((N + 127) / 128) < ((int64_t)1 << 31);
