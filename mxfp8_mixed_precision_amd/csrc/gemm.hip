@@ -5,11 +5,18 @@
 namespace temx {
 namespace {
 
+// The persistent 4-wave kernel's grid: one workgroup per CU (a multiple of 8, the XCD count, so each
+// workgroup stays on the XCD its tiles are rastered for), or one per tile if there are fewer.
+inline dim3 persistent_grid(dim3 tiles) {
+  const unsigned cap = (unsigned)(device_cu_count() / 8 * 8);
+  return dim3(cap >= 8 && tiles.x > cap ? cap : tiles.x);
+}
+
 template <class C, bool GROUPED, int FA, int FB, int EPI, int OUT>
 te_status launch5(const GemmParams& p, dim3 grid, hipStream_t stream) {
   if constexpr (std::is_same<C, Big4>::value) {
     static_assert(!GROUPED, "the 4-wave tile serves dense GEMMs");
-    hipLaunchKernelGGL((mx_gemm4_kernel<FA, FB, EPI, OUT>), grid, dim3(C::kThreads), 0, stream, p);
+    hipLaunchKernelGGL((mx_gemm4_kernel<FA, FB, EPI, OUT>), persistent_grid(grid), dim3(C::kThreads), 0, stream, p);
   } else if constexpr (GROUPED) {
     hipLaunchKernelGGL((mx_grouped_gemm_kernel<C, FA, FB, EPI, OUT>), grid, dim3(C::kThreads), 0, stream, p);
   } else {
@@ -28,9 +35,11 @@ template <class C, int FA, int FB, int EPI>
 te_status launch_pt4(const GemmParams& p, te_dtype out, dim3 grid, hipStream_t stream) {
   if constexpr (std::is_same<C, Big4>::value) {
     if (out == TE_BF16)
-      hipLaunchKernelGGL((mx_gemm4_kernel<FA, FB, EPI, TE_BF16, SM_PT>), grid, dim3(C::kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mx_gemm4_kernel<FA, FB, EPI, TE_BF16, SM_PT>), persistent_grid(grid), dim3(C::kThreads), 0,
+                         stream, p);
     else
-      hipLaunchKernelGGL((mx_gemm4_kernel<FA, FB, EPI, TE_FP32, SM_PT>), grid, dim3(C::kThreads), 0, stream, p);
+      hipLaunchKernelGGL((mx_gemm4_kernel<FA, FB, EPI, TE_FP32, SM_PT>), persistent_grid(grid), dim3(C::kThreads), 0,
+                         stream, p);
   } else {
     if (out == TE_BF16)
       hipLaunchKernelGGL((mx_gemm_kernel<C, FA, FB, EPI, TE_BF16, SM_PT>), grid, dim3(C::kThreads), 0, stream, p);

@@ -585,11 +585,20 @@ __device__ __forceinline__ void mfma_acc(v4f& acc, const v8i& bv, int bs, const 
 __device__ __forceinline__ void set_m0(uint32_t lds_addr) { asm volatile("s_mov_b32 m0, %0" ::"s"(lds_addr) : "memory"); }
 
 // buffer_load_dwordx4 ... lds with an immediate offset, which moves the LDS
-// address too (lane l lands at m0 + IMM + 16 l)
-template <int IMM>
+// address too (lane l lands at m0 + IMM + 16 l).  A VALU write of an SGPR
+// (v_readlane, v_readfirstlane) that a vector memory instruction reads needs 5
+// wait states, which the compiler cannot insert ahead of an asm statement:
+// WAIT puts them in, for code where the compiler may reload the resource or
+// offset SGPRs from VGPR lanes right before (measured: without it, copies
+// after such reloads read rows at stale offsets).
+template <int IMM, bool WAIT = false>
 __device__ __forceinline__ void lds_dma16_imm(const i32x4& rsrc, int voff, int soff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds" ::"v"(voff), "s"(rsrc), "s"(soff), "i"(IMM)
-               : "memory");
+  if constexpr (WAIT)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds" ::"v"(voff), "s"(rsrc), "s"(soff),
+                 "i"(IMM) : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds" ::"v"(voff), "s"(rsrc), "s"(soff), "i"(IMM)
+                 : "memory");
 }
 
 #define TEMX_SCHED_BARRIER() __builtin_amdgcn_sched_barrier(0)
@@ -604,8 +613,82 @@ __device__ __forceinline__ int lane_id_fresh() {
   return l;
 }
 
+// The 4-wave tile's direct-to-LDS copies.  Wave w fills slices 8w .. 8w+7
+// of A and of B (slice q = rows 8q .. 8q+7, 1 KB); copy t takes slice 8w + t:
+// lane l lands at row 8q + l/8, physical chunk l%8, which holds logical chunk
+// (l%8) ^ swz(row) = (l%8) ^ (l/16) ^ 4 (t & 1).  vo_e / vo_o: the lane's
+// global offsets for even / odd t; vo_s: its offset in a 1-KB scale slice
+// (64 rows of 16 bytes).
+struct Copy4 {
+  int vo_e, vo_o, vo_s;
+};
+__device__ __forceinline__ Copy4 copy4_offsets(int K, int wave, int lane) {
+  const int chunk_e = (lane & 7) ^ (lane >> 4);
+  Copy4 co;
+  co.vo_e = (64 * wave + (lane >> 3)) * K + chunk_e * 16;
+  co.vo_o = (64 * wave + (lane >> 3)) * K + (chunk_e ^ 4) * 16;
+  co.vo_s = 16 * lane;
+  return co;
+}
+// data copy c (0..15: A slices, then B) of the K step at byte kbase into the stage at l_stage; copies
+// 0, 4, 8 and 12 set m0, the next three add their immediate offset to it (WAIT: see lds_dma16_imm)
+template <bool WAIT = false>
+__device__ __forceinline__ void copy4_data(const Operand& A, const Operand& B, const Copy4& co, int c, int K,
+                                           int kbase, uint32_t l_stage, int wave) {
+  const int t = c & 7;
+  const bool isb = c >= 8;
+  if ((t & 3) == 0)
+    set_m0((uint32_t)__builtin_amdgcn_readfirstlane((int)(l_stage + (isb ? Big4::kHalf : 0) + (8 * wave + t) * 1024)));
+  const int so = __builtin_amdgcn_readfirstlane(8 * t * K - (t & 3) * 1024) + kbase;
+  const int vo = (t & 1) ? co.vo_o : co.vo_e;
+  const i32x4& rs = isb ? B.data : A.data;
+  switch (t & 3) {
+    case 0: lds_dma16_imm<0, WAIT>(rs, vo, so); break;
+    case 1: lds_dma16_imm<1024, WAIT>(rs, vo, so); break;
+    case 2: lds_dma16_imm<2048, WAIT>(rs, vo, so); break;
+    default: lds_dma16_imm<3072, WAIT>(rs, vo, so); break;
+  }
+}
+// scale slice s = wave + 4k of block blk (1 KB: 64 rows of 16 bytes) into the scale buffer at l_sbuf:
+// k = 0 A rows 64 w .., k = 1 B rows 64 w ..  (a_blk / b_blk: the byte offset of one block)
+template <bool WAIT = false>
+__device__ __forceinline__ void copy4_scales(const Operand& A, const Operand& B, const Copy4& co, int blk,
+                                             uint32_t l_sbuf, int k, int wave, int a_blk, int b_blk) {
+  const int s = wave + 4 * k;
+  blk = __builtin_amdgcn_readfirstlane(blk);
+  asm volatile("" : "+s"(blk));
+  set_m0((uint32_t)__builtin_amdgcn_readfirstlane((int)(l_sbuf + s * 1024)));
+  const int so = __builtin_amdgcn_readfirstlane(1024 * wave) + blk * (k == 0 ? a_blk : b_blk);
+  if (k == 0) lds_dma16_imm<0, WAIT>(A.scale, co.vo_s, so);
+  else lds_dma16_imm<0, WAIT>(B.scale, co.vo_s, so);
+}
+
+// A tile's K step 0 into stage 0, and (MXFP8) its scale block 0 into scale
+// buffer 0; mainloop4 waits for these copies.  The persistent kernel issues
+// them for its next tile as soon as the current tile's main loop is done: the
+// last step reads stage 1 and scale buffer 1 only (K / 128 is a multiple of
+// 8), and every wave is past the step before it.  Its copies take the wait
+// states of lds_dma16_imm: between tiles the compiler reloads their offsets.
+template <int SM>
+__device__ __forceinline__ void prologue4(uint8_t* lds, const Operand& A, const Operand& B, int64_t K64, int wave,
+                                          int a_blk, int b_blk) {
+  const int K = (int)K64;
+  const Copy4 co = copy4_offsets(K, wave, lane_id_fresh());
+  const uint32_t l0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  int m0_saved;
+  asm volatile("s_mov_b32 %0, m0" : "=s"(m0_saved));
+#pragma unroll
+  for (int c = 0; c < 16; ++c) copy4_data<true>(A, B, co, c, K, 0, l0, wave);
+  if constexpr (SM == SM_MX) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) copy4_scales<true>(A, B, co, 0, l0 + Big4::kOffScale, k, wave, a_blk, b_blk);
+  }
+  asm volatile("s_mov_b32 m0, %0" ::"s"(m0_saved) : "memory");
+}
+
 // MXFP8 scales come in the layout of scale_blocks_kernel (a_blk / b_blk: the
-// byte offset of one scale block of A / B, rows x 32).
+// byte offset of one scale block of A / B, rows x 32).  Step 0's copies were
+// issued by prologue4.
 template <int FA, int FB, int SM>
 __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const Operand& A, const Operand& B,
                                           int64_t K64, int wave, int a_blk = 0, int b_blk = 0) {
@@ -619,8 +702,8 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
   const int K = (int)K64;
   const int kt_n = K / BK;  // a multiple of 8, > 0
   const int wm = wave >> 1, wn = wave & 1;
-  // zeros into the AGPRs here, ahead of the copies below, and wait states after them: the compiler
-  // cannot see the MFMAs read them (a VALU write read as an MFMA's accumulator input needs a gap)
+  // zeros into the AGPRs, and wait states after them: the compiler cannot see the MFMAs read them (a
+  // VALU write read as an MFMA's accumulator input needs a gap)
   // (the zero comes from an opaque move here, so the compiler keeps no copy of it live from elsewhere)
   float zero;
   asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
@@ -634,13 +717,7 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
   asm volatile("s_nop 7" ::: "memory");
   const uint32_t l0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
 
-  // copies: wave w fills slices 8w .. 8w+7 of A and of B (slice q = rows 8q .. 8q+7, 1 KB); copy t
-  // takes slice 8w + t: lane l lands at row 8q + l/8, physical chunk l%8, which holds logical chunk
-  // (l%8) ^ swz(row) = (l%8) ^ (l/16) ^ 4 (t & 1)
-  const int chunk_e = (lane & 7) ^ (lane >> 4);
-  int vo_e = (64 * wave + (lane >> 3)) * K + chunk_e * 16;
-  int vo_o = (64 * wave + (lane >> 3)) * K + (chunk_e ^ 4) * 16;
-  int vo_s = 16 * lane;  // a scale slice is 1 KB in a row (64 rows of 16 bytes)
+  Copy4 co = copy4_offsets(K, wave, lane);
   // fragment reads: lane 16 g + r reads logical chunks g and g + 4 of row r of each fragment
   const int g = lane >> 4, r = lane & 15;
   const int lane_off = r * BK + ((g ^ swz(r)) << 4);
@@ -650,33 +727,14 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
   // are [block][step]); the MFMA picks the step's byte
   int sa_off = (wm * 128 + r) * LY::kScaleRow + 4 * g;                        // + 256 j
   int sb_off = LY::BM * LY::kScaleRow + (wn * 128 + r) * LY::kScaleRow + 4 * g;  // + 256 i
-  asm volatile("" : "+v"(vo_e), "+v"(vo_o), "+v"(vo_s), "+v"(ra_off), "+v"(rb_off), "+v"(sa_off), "+v"(sb_off));
+  asm volatile("" : "+v"(co.vo_e), "+v"(co.vo_o), "+v"(co.vo_s), "+v"(ra_off), "+v"(rb_off), "+v"(sa_off),
+               "+v"(sb_off));
 
   auto copy = [&](int c, int kbase, uint32_t l_stage) __attribute__((always_inline)) {
-    const int t = c & 7;
-    const bool isb = c >= 8;
-    if ((t & 3) == 0)
-      set_m0((uint32_t)__builtin_amdgcn_readfirstlane((int)(l_stage + (isb ? LY::kHalf : 0) + (8 * wave + t) * 1024)));
-    const int so = __builtin_amdgcn_readfirstlane(8 * t * K - (t & 3) * 1024) + kbase;
-    const int vo = (t & 1) ? vo_o : vo_e;
-    const i32x4& rs = isb ? B.data : A.data;
-    switch (t & 3) {
-      case 0: lds_dma16_imm<0>(rs, vo, so); break;
-      case 1: lds_dma16_imm<1024>(rs, vo, so); break;
-      case 2: lds_dma16_imm<2048>(rs, vo, so); break;
-      default: lds_dma16_imm<3072>(rs, vo, so); break;
-    }
+    copy4_data(A, B, co, c, K, kbase, l_stage, wave);
   };
-  // scale slice s = wave + 4k of block blk (1 KB: 64 rows of 16 bytes): k = 0 A rows 64 w ..,
-  // k = 1 B rows 64 w ..
   auto copy_scales = [&](int blk, uint32_t l_sbuf, int k) __attribute__((always_inline)) {
-    const int s = wave + 4 * k;
-    blk = __builtin_amdgcn_readfirstlane(blk);
-    asm volatile("" : "+s"(blk));
-    set_m0((uint32_t)__builtin_amdgcn_readfirstlane((int)(l_sbuf + s * 1024)));
-    const int so = __builtin_amdgcn_readfirstlane(1024 * wave) + blk * (k == 0 ? a_blk : b_blk);
-    if (k == 0) lds_dma16_imm<0>(A.scale, vo_s, so);
-    else lds_dma16_imm<0>(B.scale, vo_s, so);
+    copy4_scales(A, B, co, blk, l_sbuf, k, wave, a_blk, b_blk);
   };
   int held[16];  // each fragment's scale dword of the current 4 steps (A 0..7, B 8..15)
   auto rd = [&](const uint8_t* stg, const uint8_t* sbuf, int off, int soff, int f, int sub, int h)
@@ -696,13 +754,8 @@ __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const 
 
   int m0_saved;
   asm volatile("s_mov_b32 %0, m0" : "=s"(m0_saved));
-  // prologue: step 0's stage and scale block 0
-#pragma unroll
-  for (int c = 0; c < 16; ++c) copy(c, 0, l0);
-  if constexpr (SM == SM_MX) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) copy_scales(0, l0 + LY::kOffScale, k);
-  }
+  // step 0's stage and scale block 0 (prologue4) have landed, and every wave is done with the LDS
+  // (a previous tile's epilogue stages its output in stage 1)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   Frag Af0, Bf[3];  // the step's first fragments, read during the previous step
@@ -879,20 +932,21 @@ __device__ __forceinline__ void epilogue(v4f (&acc)[LY::FRN][LY::FRM], void* d, 
 // through LDS.  Stored straight from the MFMA layout, a wave store writes 32
 // bytes into each of 16 rows: 16 partial lines per instruction, which left
 // the store path the slowest part of a decoder-sized GEMM.  Here each wave
-// first writes its WTM x WTN block of 2-byte results to a region of LDS of its
-// own (row q at q * 2 WTN bytes, 16-byte chunk c at chunk c ^ (q % CH), CH
-// chunks per row: the 8-byte writes and the 16-byte reads are both free of
-// bank conflicts), then reads it back row-major, 16 bytes per lane, and
+// writes blocks of up to 64 rows x WTN of 2-byte results to a region of LDS
+// of its own (row q at q * 2 WTN bytes, 16-byte chunk c at chunk c ^ (q % CH),
+// CH chunks per row: the 8-byte writes and the 16-byte reads are both free of
+// bank conflicts), then reads each back row-major, 16 bytes per lane, and
 // stores 2 WTN contiguous bytes of each of 64 / CH rows per instruction.
 // The LDS is free once every wave has finished the last step's reads (the
-// barrier below); with the GELU aux the region is used twice, aux first
-// (LDS accesses of one wave complete in issue order).
-template <class LY>
+// barrier below); the region is reused by the next block (and with the GELU
+// aux, aux first, then D), since LDS accesses of one wave complete in issue
+// order.  The regions of all waves take staged_bytes<LY>() from lds.
+template <class LY, int ROWS>
 __device__ __forceinline__ void store_region(const uint8_t* region, uint16_t* out, int64_t mb, int64_t m_end,
                                              int64_t nb, int64_t N, int lane) {
   constexpr int RB = LY::WTN * 2, CH = RB / 16;
 #pragma unroll
-  for (int t = 0; t < LY::WTM * CH / 64; ++t) {
+  for (int t = 0; t < ROWS * CH / 64; ++t) {
     const int q = (64 * t + lane) / CH, c = (64 * t + lane) % CH;
     const uint4 v = *reinterpret_cast<const uint4*>(region + q * RB + ((c ^ (q & (CH - 1))) << 4));
     const int64_t m = mb + q, n = nb + 8 * c;  // N % 16 == 0: a chunk of 8 columns is all in or all out
@@ -904,6 +958,10 @@ constexpr bool staged_epilogue(int epi, int out) {
   return (out == TE_BF16 || out == TE_FP16) &&
          (epi == TE_EPI_NONE || epi == TE_EPI_BIAS || epi == TE_EPI_BIAS_GELU_AUX);
 }
+template <class LY>
+constexpr int staged_row_frags() { return LY::FRM < 4 ? LY::FRM : 4; }  // row fragments per staged block
+template <class LY>
+constexpr int staged_bytes() { return LY::NW * 16 * staged_row_frags<LY>() * LY::WTN * 2; }
 
 template <class LY, int EPI, int OUT, bool SCALE = false>
 __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8_t* lds, void* d,
@@ -911,8 +969,9 @@ __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8
                                              int64_t n0, int64_t N, int wave, int lane, float alpha = 1.0f) {
   static_assert(OUT == TE_BF16 || OUT == TE_FP16, "2-byte outputs");
   static_assert(EPI == TE_EPI_NONE || EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX, "forward epilogues");
-  constexpr int RB = LY::WTN * 2, CH = RB / 16, kRegion = LY::WTM * RB;
-  static_assert((CH & (CH - 1)) == 0 && CH <= 16 && LY::NW * kRegion <= LY::kLds, "staging layout");
+  constexpr int FRH = staged_row_frags<LY>(), RB = LY::WTN * 2, CH = RB / 16, kRegion = 16 * FRH * RB;
+  static_assert((CH & (CH - 1)) == 0 && CH <= 16 && LY::FRM % FRH == 0 && staged_bytes<LY>() <= LY::kLds,
+                "staging layout");
   const int wm = wave / LY::NWN, wn = wave % LY::NWN;
   const int g = lane >> 4, r = lane & 15;
   uint8_t* region = lds + wave * kRegion;
@@ -970,42 +1029,47 @@ __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8
   for (int pass = 0; pass < kPasses; ++pass) {
     const bool to_aux = kPasses == 2 && pass == 0;
 #pragma unroll
-    for (int j = 0; j < LY::FRM; ++j) {
+    for (int h = 0; h < LY::FRM / FRH; ++h) {
 #pragma unroll
-      for (int i = 0; i < LY::FRN; ++i) {
-        // 4-wave tile: the fragment's AGPRs are read here, one fragment at a time through VGPRs
-        if constexpr (!kInPlace) asm volatile("" : "+a"(acc[i][j]));
-        float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
-        if constexpr (SCALE && !(kHasBias && kInPlace)) {  // in place with the bias, alpha went in above
-          v0 = mul_rn(v0, alpha);
-          v1 = mul_rn(v1, alpha);
-          v2 = mul_rn(v2, alpha);
-          v3 = mul_rn(v3, alpha);
+      for (int jj = 0; jj < FRH; ++jj) {
+        const int j = FRH * h + jj;
+#pragma unroll
+        for (int i = 0; i < LY::FRN; ++i) {
+          // 4-wave tile: the fragment's AGPRs are read here, one fragment at a time through VGPRs
+          if constexpr (!kInPlace) asm volatile("" : "+a"(acc[i][j]));
+          float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
+          if constexpr (SCALE && !(kHasBias && kInPlace)) {  // in place with the bias, alpha went in above
+            v0 = mul_rn(v0, alpha);
+            v1 = mul_rn(v1, alpha);
+            v2 = mul_rn(v2, alpha);
+            v3 = mul_rn(v3, alpha);
+          }
+          if constexpr (kHasBias && !kInPlace) {
+            v0 += bv[i][0];
+            v1 += bv[i][1];
+            v2 += bv[i][2];
+            v3 += bv[i][3];
+          }
+          uint2 w;
+          if (EPI == TE_EPI_BIAS_GELU_AUX && !to_aux) {
+            v0 = gelu_tanh(v0);
+            v1 = gelu_tanh(v1);
+            v2 = gelu_tanh(v2);
+            v3 = gelu_tanh(v3);
+          }
+          if (OUT == TE_FP16 && !to_aux)
+            w = make_uint2(pack_f16x2(v0, v1), pack_f16x2(v2, v3));
+          else
+            w = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+          const int q = 16 * jj + r, chunk = 2 * i + (g >> 1);
+          *reinterpret_cast<uint2*>(region + wr_off + 16 * jj * RB + ((chunk ^ (q & (CH - 1))) << 4)) = w;
         }
-        if constexpr (kHasBias && !kInPlace) {
-          v0 += bv[i][0];
-          v1 += bv[i][1];
-          v2 += bv[i][2];
-          v3 += bv[i][3];
-        }
-        uint2 w;
-        if (EPI == TE_EPI_BIAS_GELU_AUX && !to_aux) {
-          v0 = gelu_tanh(v0);
-          v1 = gelu_tanh(v1);
-          v2 = gelu_tanh(v2);
-          v3 = gelu_tanh(v3);
-        }
-        if (OUT == TE_FP16 && !to_aux)
-          w = make_uint2(pack_f16x2(v0, v1), pack_f16x2(v2, v3));
-        else
-          w = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-        const int q = 16 * j + r, chunk = 2 * i + (g >> 1);
-        *reinterpret_cast<uint2*>(region + wr_off + 16 * j * RB + ((chunk ^ (q & (CH - 1))) << 4)) = w;
       }
+      asm volatile("" ::: "memory");
+      store_region<LY, 16 * FRH>(region, to_aux ? aux : static_cast<uint16_t*>(d), mb + 16 * FRH * h, m_end, nb, N,
+                                 lane);
+      asm volatile("" ::: "memory");
     }
-    asm volatile("" ::: "memory");
-    store_region<LY>(region, to_aux ? aux : static_cast<uint16_t*>(d), mb, m_end, nb, N, lane);
-    asm volatile("" ::: "memory");
     if constexpr (!kInPlace && kPasses == 2) {
       // the second pass reads the AGPRs again: without this the compiler keeps the first pass's
       // 256 VGPR copies live between the passes
@@ -1229,29 +1293,59 @@ __global__ __launch_bounds__(256) void scale_blocks_kernel(const uint8_t* __rest
 // Dense on the 4-wave big tile (K % 1024 == 0): one wave per SIMD, so the
 // whole register file is the wave's.  MXFP8 operands come with their scales
 // in the layout of scale_blocks_kernel (p.a_scale / p.b_scale point at the
-// rearranged copies); per-tensor operands have none.
+// rearranged copies); per-tensor operands have none.  Persistent: workgroup
+// w takes the tiles of workgroups w, w + G, w + 2G, ... (G = gridDim.x, a
+// multiple of 8 when it is below the tile count), so the XCD-aware tile order
+// is unchanged.  Once a tile's main loop is done, the next tile's first
+// copies are issued before its epilogue, whose staging then uses stage 1 only:
+// the next tile's first stage lands while this one's results are stored.
 template <int FA, int FB, int EPI, int OUT, int SM = SM_MX>
 __global__ __launch_bounds__(Big4::kThreads, 1) void mx_gemm4_kernel(GemmParams p) {
   using LY = Big4;
-  constexpr bool kBlk = SM == SM_MX;
+  static_assert(staged_bytes<LY>() <= LY::kStage, "the staged epilogue fits in stage 1");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int tm, tn;
-  raster_tile(blockIdx.x, (int)((p.M + LY::BM - 1) / LY::BM), (int)((p.N + LY::BN - 1) / LY::BN), tm, tn);
-  const int64_t m0 = (int64_t)tm * LY::BM, n0 = (int64_t)tn * LY::BN;
-  Operand A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, LY::BM);
-  Operand B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, LY::BN);
-  if constexpr (kBlk) {
-    // the tile's rows of every block: block blk at + blk * rows * 32 (the soffset), rows past the
-    // operand's end read the next block (never stored) or zeros past the array
-    const int64_t nblk = p.K / 512;
-    A.scale = make_rsrc(p.a_scale + m0 * 16, (nblk * p.M - m0) * 16);
-    B.scale = make_rsrc(p.b_scale + n0 * 16, (nblk * p.N - n0) * 16);
+  const int ntm = (int)((p.M + LY::BM - 1) / LY::BM), ntn = (int)((p.N + LY::BN - 1) / LY::BN);
+  const int ntiles = ntm * ntn;
+  const int a_blk = (int)(p.M * 16), b_blk = (int)(p.N * 16);
+  auto tile = [&](int v, int64_t& m0, int64_t& n0, Operand& A, Operand& B) __attribute__((always_inline)) {
+    int tm, tn;
+    raster_tile(v, ntm, ntn, tm, tn);
+    m0 = (int64_t)tm * LY::BM;
+    n0 = (int64_t)tn * LY::BN;
+    A = make_operand(p.a, p.a_scale, m0, p.M - m0, p.K, LY::BM);
+    B = make_operand(p.b, p.b_scale, n0, p.N - n0, p.K, LY::BN);
+    if constexpr (SM == SM_MX) {
+      // the tile's rows of every block: block blk at + blk * rows * 16 (the soffset), rows past the
+      // operand's end read the next block (never stored) or zeros past the array
+      const int64_t nblk = p.K / 512;
+      A.scale = make_rsrc(p.a_scale + m0 * 16, (nblk * p.M - m0) * 16);
+      B.scale = make_rsrc(p.b_scale + n0 * 16, (nblk * p.N - n0) * 16);
+    }
+  };
+  int v = blockIdx.x;
+  int64_t m0, n0;
+  Operand A, B;
+  tile(v, m0, n0, A, B);
+  prologue4<SM>(lds, A, B, p.K, wave, a_blk, b_blk);
+  for (;;) {
+    v4f acc[LY::FRN][LY::FRM];
+    mainloop4<FA, FB, SM>(lds, acc, A, B, p.K, wave, a_blk, b_blk);
+    const int vn = v + (int)gridDim.x;
+    int64_t m0n = 0, n0n = 0;
+    Operand An = A, Bn = B;
+    if (vn < ntiles) {
+      tile(vn, m0n, n0n, An, Bn);
+      prologue4<SM>(lds, An, Bn, p.K, wave, a_blk, b_blk);
+    }
+    finish_tile<LY, EPI, OUT, SM>(acc, lds + LY::kStage, p, m0, n0, wave, lane_id_fresh());
+    if (vn >= ntiles) break;
+    v = vn;
+    m0 = m0n;
+    n0 = n0n;
+    A = An;
+    B = Bn;
   }
-  v4f acc[LY::FRN][LY::FRM];
-  mainloop4<FA, FB, SM>(lds, acc, A, B, p.K, wave, (int)(p.M * 16), (int)(p.N * 16));
-  finish_tile<LY, EPI, OUT, SM>(acc, lds, p, m0, n0, wave, lane_id_fresh());
 }
 
 // Grouped: a persistent grid walks the flat list of (expert row-tile,
