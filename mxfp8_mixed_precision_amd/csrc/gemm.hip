@@ -217,7 +217,7 @@ extern "C" te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_
   const dim3 grid = tile_grid(t, M, N);
   if (t == Tile::SmallDeep) return launch_pt<SmallDeep>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   if (t == Tile::Small) return launch_pt<Small>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
-  if (K % Big4::kKAlign == 0) return launch_pt<Big4>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
+  if (four_wave(M, N, K)) return launch_pt<Big4>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   return launch_pt<Big>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
 }
 

@@ -1439,13 +1439,26 @@ inline dim3 tile_grid(Tile t, int64_t M, int64_t N) {
                         : dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128)));
 }
 
-// The 4-wave MXFP8 path: the tile choice is the big tile, K % 1024 == 0 (the
-// loop's 8-step turns), and each operand's rearranged scales fit 32-bit
-// offsets.  Its
-// workspace holds the rearranged scales of A, then (256-byte aligned) of B.
+// The 4-wave tile instead of the 8-wave big tile: K % 1024 == 0 (the loop's
+// 8-step turns) and enough K steps per CU that its faster main loop outweighs
+// its single-wave prologue and epilogue: K >= 2048 and at least 32 steps per
+// CU over the whole grid.  Measured on MI355X (4-wave against 8-wave, us, the
+// MXFP8 path with its scale rearrangement): 4096 x 3072 x 1024 26.7 / 24.0,
+// 4096 x 4096 x 1024 with GELU aux 37.2 / 30.2, 4096 x 4096 x 2048 38.2 /
+// 36.6, 8192 x 8192 x 1024 82.0 / 81.8; 4096 x 4096 x 4096 59.8 / 61.9,
+// 8192 x 8192 x 2048 120.5 / 132.3, 14336 x 4096 x 4096 199.5 / 224.3,
+// 4096 x 4096 x 14336 170.9 / 193.5, 8192^3 386.7 / 437.9.
+inline bool four_wave(int64_t M, int64_t N, int64_t K) {
+  if (pick_tile(M, N, K) != Tile::Big || K % Big4::kKAlign != 0 || K < 2048) return false;
+  const int64_t cus = device_cu_count(), tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  return (K / BK) * ((tiles + cus - 1) / cus) >= 32;
+}
+// The 4-wave MXFP8 path: the above, and each operand's rearranged scales fit
+// 32-bit offsets.  Its workspace holds the rearranged scales of A, then
+// (256-byte aligned) of B.
 inline bool four_wave_mx(int64_t M, int64_t N, int64_t K) {
   const int64_t lim = ((int64_t)1 << 31) - 4096;
-  return pick_tile(M, N, K) == Tile::Big && K % Big4::kKAlign == 0 && M * (K / 32) < lim && N * (K / 32) < lim;
+  return four_wave(M, N, K) && M * (K / 32) < lim && N * (K / 32) < lim;
 }
 inline size_t scale_blocks_b_offset(int64_t M, int64_t K) { return (size_t)((M * (K / 32) + 255) / 256 * 256); }
 inline size_t scale_blocks_bytes(int64_t M, int64_t N, int64_t K) {

@@ -80,7 +80,6 @@ STATED_MISS_CEILING: dict = {
     "per_tensor:272x400x256:bias": 115,  # 102 of 108800
     "per_tensor:272x400x256:bias_gelu_aux": 28,  # 23 of 108800
     "per_tensor:272x400x256:none": 125,  # 111 of 108800
-    "per_tensor:4144x4176x1024:none": 3,  # 1 of 2304
     "per_tensor:4144x4176x256:bias": 5,  # 2 of 2304
     "per_tensor:4144x4176x256:bias_gelu_aux": 4,  # 1 of 2304
     "per_tensor:4144x4176x256:none": 5,  # 2 of 2304

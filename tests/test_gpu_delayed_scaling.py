@@ -64,7 +64,7 @@ def per_tensor_operands(M, N, K, seed):
 
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
-                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 1024)])
+                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 2048)])
 def test_per_tensor_gemm(epi, M, N, K):
     qa, ia, qb, ib = per_tensor_operands(M, N, K, 96 + K)
     bias_bits = None if epi == "none" else workloads.normal_bf16(97, N, (N,), 0.5)
@@ -101,9 +101,9 @@ def test_per_tensor_gemm(epi, M, N, K):
     assert_stated_misses(f"per_tensor:{M}x{N}x{K}:{epi}", int((~stated).sum()), stated.size)
 
 
-@pytest.mark.parametrize("M,N,K", [(272, 304, 512), (4096 + 48, 4096 + 80, 1024)])
+@pytest.mark.parametrize("M,N,K", [(272, 304, 512), (4096 + 48, 4096 + 80, 2048)])
 def test_per_tensor_gemm_fp32_output(M, N, K):
-    # (4144, 4176, 1024) runs the 4-wave big tile, which applies alpha inside its epilogue
+    # (4144, 4176, 2048) runs the 4-wave big tile, which applies alpha inside its epilogue
     qa, ia, qb, ib = per_tensor_operands(M, N, K, 98)
     d, _ = te().fp8_gemm(qa, ia, "e4m3", qb, ib, "e4m3", out_dtype=torch.float32)
     torch.cuda.synchronize()

@@ -77,14 +77,16 @@ def test_big_tile_exact_integer_partial_scale_block(fa, fb):
 
 
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
-@pytest.mark.parametrize("K", [1024, 3072])
+@pytest.mark.parametrize("K", [2048, 3072])
 def test_four_wave_tile_exact_integer(fa, fb, K):
-    # the 4-wave big tile (K % 1024 == 0, 17 x 17 tiles of 256) with a 48-row
-    # and an 80-column tail; K = 1024 is one 8-step scale block, 3072 three.
+    # the 4-wave big tile (K % 1024 == 0, 17 x 17 tiles of 256, two per CU: 32
+    # or more K steps per CU) with a 48-row and an 80-column tail; K = 2048 is
+    # four 4-step scale blocks, 3072 six.
     # Exact-integer operands: every fp32 output is exact, so sampled rows
     # (every tile boundary, every wave-row boundary, the last row) must match
     # the oracle bit for bit in every column.
     M, N = 4096 + 48, 4096 + 80
+    assert te().te_mxfp8_gemm_workspace_size(M, N, K) > 0  # the 4-wave path serves this shape
     rng = np.random.default_rng(K + 7)
     qa, qb = exact_codes(rng, (M, K), fa), exact_codes(rng, (N, K), fb)
     sa = rng.integers(124, 131, size=(M, K // 32)).astype(np.uint8)
@@ -120,10 +122,15 @@ def test_four_wave_tile_matches_eight_wave_tile(epi):
 
 
 def test_gemm_workspace_size():
-    # only the 4-wave path takes a workspace: big-tile grids with K % 1024 == 0
+    # only the 4-wave path takes a workspace: big-tile grids with K % 1024 == 0, K >= 2048 and 32 or
+    # more K steps per CU
     ws = te().te_mxfp8_gemm_workspace_size
     assert ws(8192, 8192, 8192) == 2 * 8192 * 256
-    assert ws(8192, 8192, 1152) == 0          # K not whole 8-step scale blocks
+    assert ws(8192, 8192, 2048) == 2 * 8192 * 64
+    assert ws(4096, 4096, 4096) == 2 * 4096 * 128
+    assert ws(8192, 8192, 1152) == 0          # K not whole 8-step turns
+    assert ws(8192, 8192, 1024) == 0          # K below 2048
+    assert ws(4096, 4096, 2048) == 0          # 16 K steps per CU
     assert ws(4096, 1024, 4096) == 0          # a small-tile grid
     assert ws(0, 8192, 8192) == 0 and ws(8192, 8192, 100) == 0
 
@@ -256,12 +263,12 @@ def test_ragged_shapes_and_epilogues(epi, M, N, K):
 
 
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
-@pytest.mark.parametrize("K", [256, 1024])
+@pytest.mark.parametrize("K", [256, 2048])
 def test_big_tile_ragged_edges(epi, K):
     # enough 256 x 256 tiles (17 x 17) that a big-tile kernel runs, with a
     # 48-row and an 80-column tail; sampled rows / columns include every tile
     # boundary and the last row and column.  K = 256 runs the 8-wave tile,
-    # K = 1024 (whole 8-step scale blocks) the 4-wave one.
+    # K = 2048 (whole 8-step turns, 32 K steps per CU) the 4-wave one.
     M, N = 4096 + 48, 4096 + 80
     spec = workloads.GemmSpec("big_ragged", M, N, K, "e4m3", "e4m3", epi,
                               workloads.TensorSpec(53, M, (M, K), 1.0, 0.01),
@@ -403,7 +410,7 @@ def backward_operands(M, N, K, seed):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
-                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 1024)])
+                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 2048)])
 def test_dgelu_epilogue(M, N, K):
     qa, sa, qb, sb, oqa, osa, oqb, osb = backward_operands(M, N, K, 70 + K)
     pre = workloads.normal_bf16(72, M + N, (M, N), 2.0, 0.0)   # the forward's saved pre-activation
@@ -444,7 +451,7 @@ def test_dgelu_epilogue(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
-                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 1024)])
+                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 2048)])
 def test_accumulate_epilogue(M, N, K):
     qa, sa, qb, sb, oqa, osa, oqb, osb = backward_operands(M, N, K, 80 + K)
     rng = np.random.default_rng(M + N + K)
@@ -515,7 +522,7 @@ def test_grouped_backward_epilogues_match_dense(epi):
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
 @pytest.mark.parametrize("M,N,K,out_fmt", [(16, 32, 128, "e4m3"), (272, 416, 256, "e4m3"), (1040, 800, 640, "e4m3"),
                                            (4096 + 48, 4096 + 32, 256, "e4m3"), (272, 416, 256, "e5m2"),
-                                           (272, 416, 2176, "e4m3"), (4096 + 48, 4096 + 32, 1024, "e4m3")])
+                                           (272, 416, 2176, "e4m3"), (4096 + 48, 4096 + 32, 2048, "e4m3")])
 def test_mxfp8_output_equals_quantized_bf16_output(epi, M, N, K, out_fmt):
     # the codes must be exactly the rowwise quantization of the bf16 D that
     # te_mxfp8_gemm writes for the same inputs (itself checked against the
