@@ -24,7 +24,9 @@
 // * 256 x 256 workgroup tile, 8 waves in 4 x 2 (two per SIMD), 64 x 128 per
 //   wave (4 x 8 MFMA tiles = 128 fp32 accumulators per lane), K step 128;
 //   a 128 x 128 tile (4 waves of 64 x 64) for grids the big tile cannot fill,
-//   with 2 or 4 LDS stages (see Cfg).
+//   with 2 or 4 LDS stages (see Cfg); and for long-K grids the 4-wave
+//   256 x 256 tile (Big4, mainloop4: one wave per SIMD, 128 x 128 per wave,
+//   256 accumulators in AGPRs), persistent over its tiles.
 // * A, B and their scale tiles are copied global -> LDS with direct-to-LDS
 //   buffer loads (buffer_load_dwordx4 / _dword ... lds) into a ring of
 //   stages, issued by one wave per SIMD.
@@ -33,7 +35,8 @@
 //   bands of 4 row-tiles) and its L2 sees the reuse.
 // * Ragged M / N tails: each tile's copies go through buffer resources that
 //   cover only its valid rows, so rows past the end read as zeros; stores are
-//   masked.  The workspace is 0 bytes.
+//   masked.  Only the 4-wave MXFP8 path takes a workspace: (M + N) K / 32
+//   bytes, the operands' scales rearranged by scale_blocks_kernel.
 #pragma once
 
 #include "temx_device.h"
