@@ -42,11 +42,16 @@ def test_status_strings():
 
 
 def test_workspace_queries():
-    # the rearranged E8M0 scales of the 4-wave path (big-tile grids, K % 1024 == 0); without a GPU
-    # the library takes a 256-CU device
+    # the rearranged E8M0 scales of the 4-wave path (big-tile grids, K % 1024 == 0, K >= 2048 and 32
+    # or more K steps per CU); without a GPU the library takes a 256-CU device
     assert te.te_mxfp8_gemm_workspace_size(8192, 8192, 8192) == 2 * 8192 * 8192 // 32
     assert te.te_mxfp8_gemm_workspace_size(8192, 8192, 1152) == 0
     assert te.te_mxfp8_gemm_workspace_size(-1, 8192, 8192) == 0
+    assert te.te_mxfp8_gemm_workspace_size(8192, 8192, 2048) == 2 * 8192 * 2048 // 32
+    assert te.te_mxfp8_gemm_workspace_size(4096, 4096, 4096) == 2 * 4096 * 4096 // 32
+    assert te.te_mxfp8_gemm_workspace_size(8192, 8192, 1024) == 0
+    assert te.te_mxfp8_gemm_workspace_size(4096, 4096, 2048) == 0
+    assert te.te_mxfp8_gemm_workspace_size(4096 + 48, 4096 + 80, 2048) == (4144 * 64 + 255) // 256 * 256 + 4176 * 64
     assert te.te_amax_workspace_size(0) == 4
     assert te.te_amax_workspace_size(8192 * 8192) == 4 * 1024
     assert te.te_amax_workspace_size(4096) == 4
