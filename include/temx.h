@@ -259,8 +259,9 @@ te_status te_mxfp8_quantize_bgrad(const uint16_t* x, int64_t rows, int64_t cols,
  *   workspace: optional device scratch, owned by the caller and free for
  *   reuse once the GEMM has run (stream order).  te_mxfp8_gemm_workspace_size
  *   returns the bytes that enable the faster path for the shape on the
- *   current device, 0 where there is none: grids the 256 x 256 tile serves
- *   with K % 1024 == 0 take (M + N) K / 32 bytes (A's part rounded up to 256)
+ *   current device, 0 where there is none: grids the 4-wave 256 x 256 tile
+ *   serves (K % 1024 == 0, K >= 2048 and 32 or more K steps per CU) take
+ *   (M + N) K / 32 bytes (A's part rounded up to 256)
  *   for a rearranged copy of both operands' E8M0 scales (blocks of 4 K steps,
  *   a tile row's 16 bytes contiguous), written by the GEMM itself on the same
  *   stream.  With a NULL workspace, a smaller one, one not 256-byte aligned,

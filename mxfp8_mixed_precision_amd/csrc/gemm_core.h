@@ -690,7 +690,7 @@ __device__ __forceinline__ void prologue4(uint8_t* lds, const Operand& A, const 
 }
 
 // MXFP8 scales come in the layout of scale_blocks_kernel (a_blk / b_blk: the
-// byte offset of one scale block of A / B, rows x 32).  Step 0's copies were
+// byte offset of one scale block of A / B, rows x 16).  Step 0's copies were
 // issued by prologue4.
 template <int FA, int FB, int SM>
 __device__ __forceinline__ void mainloop4(uint8_t* lds, v4f (&acc)[8][8], const Operand& A, const Operand& B,
