@@ -101,11 +101,12 @@ def test_four_wave_tile_exact_integer(fa, fb, K):
 
 
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
-def test_four_wave_tile_matches_eight_wave_tile(epi):
+@pytest.mark.parametrize("M,N,K", [(4096 + 48, 4096 + 80, 2048), (8192, 8192 + 80, 2048)])
+def test_four_wave_tile_matches_eight_wave_tile(epi, M, N, K):
     # the same GEMM with the workspace (the 4-wave kernel after its scales are rearranged into the
     # workspace) and without (the 8-wave kernel on the scales as they are): the same D and aux, bit
-    # for bit, on real quantized data with a 48-row and an 80-column tail
-    M, N, K = 4096 + 48, 4096 + 80, 2048
+    # for bit, on real quantized data with ragged tails; the persistent 4-wave grid runs 2 tiles per
+    # workgroup on the first shape and 4 or 5 on the second (1056 tiles on 256 workgroups)
     a = workloads.normal_bf16(91, 0, (M, K), 1.0, 0.01)
     b = workloads.normal_bf16(91, 1, (N, K), 0.05)
     qa, sa, _, _ = te().mxfp8_quantize(dev(a), "e4m3", "row")
