@@ -49,10 +49,10 @@ def test_delayed_scaling_sequence(fmt, algo, margin, L, n):
         assert np.array_equal(host(q), oq), f"step {step}: codes"
 
 
-def per_tensor_operands(M, N, K, seed):
+def per_tensor_operands(M, N, K, seed, fa="e4m3", fb="e4m3"):
     """Delayed-scaling casts (one step each, from scale 1 after a warm-up step) of an activation and a weight."""
     out = []
-    for t, (rows, sigma, fmt) in enumerate([(M, 1.0, "e4m3"), (N, 0.05, "e4m3")]):
+    for t, (rows, sigma, fmt) in enumerate([(M, 1.0, fa), (N, 0.05, fb)]):
         st = te().DelayedScaling(fmt, 16, "max", 0)
         warm = workloads.normal_bf16(seed, 10 + t, (rows, K), sigma, 0.01)
         st.step(dev(warm))   # the warm-up step gives a data-derived scale
@@ -99,6 +99,27 @@ def test_per_tensor_gemm(epi, M, N, K):
     ok, stated = gemm_check(bf16_to_f64(got_bits), ref, s, b, K, h_pairs, through_gelu=epi == "bias_gelu_aux")
     assert ok.all(), f"{(~ok).sum()} of {ok.size} outside the bound"
     assert_stated_misses(f"per_tensor:{M}x{N}x{K}:{epi}", int((~stated).sum()), stated.size)
+
+
+@pytest.mark.parametrize("fa,fb", [("e5m2", "e4m3"), ("e4m3", "e5m2")])
+@pytest.mark.parametrize("M,N,K", [(1040, 784, 640), (4096 + 48, 4096 + 80, 256), (4096 + 48, 4096 + 80, 2048)])
+def test_per_tensor_gemm_e5m2_operand(fa, fb, M, N, K):
+    # HYBRID per-tensor operands (an E5M2 gradient times E4M3, either side) on the small, 8-wave and
+    # 4-wave tiles: D bit-exact against the MFMA model with unit block scales and the fp32 alpha
+    qa, ia, qb, ib = per_tensor_operands(M, N, K, 131 + K, fa, fb)
+    bias_bits = workloads.normal_bf16(132, N, (N,), 0.5)
+    d, _ = te().fp8_gemm(qa, ia, fa, qb, ib, fb, "bias", dev(bias_bits))
+    torch.cuda.synchronize()
+    big = M > 2048
+    rows = np.unique(np.r_[0, M - 1, np.linspace(0, M - 1, 48).astype(int)]) if big else np.arange(M)
+    cols = np.unique(np.r_[0, N - 1, np.linspace(0, N - 1, 48).astype(int)]) if big else np.arange(N)
+    hqa, hqb = host(qa)[rows], host(qb)[cols]
+    ones_a = np.full((len(rows), K // 32), 127, np.uint8)
+    ones_b = np.full((len(cols), K // 32), 127, np.uint8)
+    acc = mfma_model.hw_gemm_fp32(hqa, ones_a, oracle.format_by_name(fa), hqb, ones_b, oracle.format_by_name(fb))
+    alpha = np.float32(host(ia)[0] * host(ib)[0])
+    want_d, _ = model_outputs((acc * alpha).astype(np.float32), bias_bits[cols], "bias")
+    assert np.array_equal(host(d)[rows][:, cols], want_d), "D differs from the MFMA model"
 
 
 @pytest.mark.parametrize("M,N,K", [(272, 304, 512), (4096 + 48, 4096 + 80, 2048)])
