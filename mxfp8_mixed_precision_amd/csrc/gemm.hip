@@ -162,10 +162,11 @@ extern "C" te_status te_mxfp8_gemm(const uint8_t* a, const uint8_t* a_scale, te_
   if (M == 0 || N == 0) return TE_OK;
   TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   GemmParams p{a, a_scale, b, b_scale, d, bias, aux, M, N, K, nullptr, 0};
-  const Tile t = pick_tile(M, N, K);
+  const Tile t = pick_tile_dense(M, N, K);
   const dim3 grid = tile_grid(t, M, N);
   if (t == Tile::SmallDeep) return launch2<SmallDeep, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   if (t == Tile::Small) return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
+  if (t == Tile::Big192) return launch2<Big192, false>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   return launch_big_mx(p, a_fmt, b_fmt, epi, d_dtype, grid, workspace, workspace_bytes, stream);
 }
 
@@ -186,10 +187,11 @@ extern "C" te_status te_mxfp8_gemm_mxout(const uint8_t* a, const uint8_t* a_scal
   TE_REQUIRE(d_scale != nullptr, TE_ERR_NULL);
   TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   GemmParams p{a, a_scale, b, b_scale, d, bias, aux, M, N, K, nullptr, 0, d_scale};
-  const Tile t = pick_tile(M, N, K);
+  const Tile t = pick_tile_dense(M, N, K);
   const dim3 grid = tile_grid(t, M, N);
   if (t == Tile::SmallDeep) return launch2<SmallDeep, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
   if (t == Tile::Small) return launch2<Small, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
+  if (t == Tile::Big192) return launch2<Big192, false>(p, a_fmt, b_fmt, epi, d_fmt, grid, stream);
   return launch_big_mx(p, a_fmt, b_fmt, epi, d_fmt, grid, workspace, workspace_bytes, stream);
 }
 
@@ -213,10 +215,11 @@ extern "C" te_status te_fp8_gemm(const uint8_t* a, const float* a_scale_inv, te_
   TE_REQUIRE(device_is_gfx950(), TE_ERR_ARCH);
   // the block-scale descriptors are never read in per-tensor mode; they point at the data
   GemmParams p{a, a, b, b, d, bias, aux, M, N, K, nullptr, 0, nullptr, a_scale_inv, b_scale_inv};
-  const Tile t = pick_tile(M, N, K);
+  const Tile t = pick_tile_dense(M, N, K);
   const dim3 grid = tile_grid(t, M, N);
   if (t == Tile::SmallDeep) return launch_pt<SmallDeep>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   if (t == Tile::Small) return launch_pt<Small>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
+  if (t == Tile::Big192) return launch_pt<Big192>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   if (four_wave(M, N, K)) return launch_pt<Big4>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
   return launch_pt<Big>(p, a_fmt, b_fmt, epi, d_dtype, grid, stream);
 }

@@ -112,15 +112,20 @@ struct Cfg {
   static constexpr int kScaleBuf = (BM + BN) * 16;
   static constexpr int kOffScaleBuf = NSTAGE * kStage;
   static constexpr int kLds = NSTAGE * kStage + (SB == 1 ? 0 : 2 * kScaleBuf);
-  static_assert(SB == 1 || (SB == 4 && NSTAGE == 2 && BM == BN && 2 * (BM / 64) == 2 * NCOPY), "scale blocks");
-  // scale slices (64 rows of one operand) per copier wave: every copier issues
-  // the same number of copies per stage
+  static_assert(SB == 1 || (SB == 4 && NSTAGE == 2 && BM % 64 == 0 && BN % 64 == 0 && (BM + BN) / 64 <= 2 * NCOPY),
+                "scale blocks: at most two 64-row slices per copier wave");
+  // SB = 1: scale slices (64 rows of one operand) per copier wave; every
+  // copier issues the same number of copies per stage
   static constexpr int kScaleSlicesPerCopier = 2 * (BM / 64) / NCOPY;
-  static_assert(2 * (BM / 64) % NCOPY == 0, "scale slices split evenly over the copier waves");
-  static_assert(BM == BN, "one row clamp and one copy scheme serve both operands");
-  static_assert(NCOPY % 2 == 0 && (BM / 8) % NCOPY == 0 && (BM / 64) <= NCOPY, "copy slices per copier wave");
+  static_assert(SB == 4 || (BM == BN && 2 * (BM / 64) % NCOPY == 0), "per-step scale slices split evenly");
+  static_assert(NCOPY % 2 == 0 && (BM / 8) % NCOPY == 0 && (BN / 8) % NCOPY == 0 && (BM / 64) <= NCOPY,
+                "copy slices per copier wave");
 };
 using Big = Cfg<256, 256, 4, 2, 4, 2, 4>;
+// 256 x 192 (8 waves of 64 x 96): for grids whose 256 x 256 tiles leave CUs
+// idle and whose 256 x 192 tiles fill them without a second round (the
+// decoder's QKV, 4096 x 3072: 192 tiles of 256 x 256, 256 of 256 x 192).
+using Big192 = Cfg<256, 192, 4, 2, 4, 2, 4>;
 using Small = Cfg<128, 128, 2, 2, 4>;
 using SmallDeep = Cfg<128, 128, 2, 2, 4, 4>;
 
@@ -250,12 +255,13 @@ __device__ __forceinline__ CopyOffsets copy_offsets(int64_t K, int c, int lane) 
 template <class C, int SM = SM_MX>
 __device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, const Operand& B,
                                            const CopyOffsets& off, int64_t K, int kt, int c) {
+  constexpr int kA = C::BM / 8 / C::NCOPY, kB = C::BN / 8 / C::NCOPY;  // slices per copier
 #pragma unroll
-  for (int i = 0; i < C::BM / 8 / C::NCOPY; ++i) {
+  for (int i = 0; i < (kA > kB ? kA : kB); ++i) {
     const int q = c + C::NCOPY * i;
     const int so = (int)(8 * C::NCOPY * i * K) + kt * BK;
-    lds_dma16(A.data, stage + q * 1024, off.data, so);
-    lds_dma16(B.data, stage + C::kOffBData + q * 1024, off.data, so);
+    if (i < kA) lds_dma16(A.data, stage + q * 1024, off.data, so);
+    if (i < kB) lds_dma16(B.data, stage + C::kOffBData + q * 1024, off.data, so);
   }
   if constexpr (SM != SM_PT && C::SB == 1) {
 #pragma unroll
@@ -282,12 +288,14 @@ __device__ __forceinline__ void load_stage(uint32_t stage, const Operand& A, con
 template <class C, int SM>
 __device__ __forceinline__ void load_scale_block(uint32_t sbuf, const Operand& A, const Operand& B,
                                                  const CopyOffsets& off, int64_t K, int blk, int c) {
+  constexpr int kSa = C::BM / 64, kSb = C::BN / 64;  // slices of A, then of B
 #pragma unroll
-  for (int i = 0; i < 2 * (C::BM / 64) / C::NCOPY; ++i) {
+  for (int i = 0; i < (kSa + kSb + C::NCOPY - 1) / C::NCOPY; ++i) {
     const int q = c + C::NCOPY * i;
-    const int s64 = q % (C::BM / 64);
+    if (q >= kSa + kSb) break;
+    const int s64 = q < kSa ? q : q - kSa;
     const int soff = (int)(64 * s64 * (K / 32)) + 16 * blk;
-    if (q < C::BM / 64) {
+    if (q < kSa) {
       lds_dma16(A.scale, sbuf + s64 * 1024, off.scale, soff);
     } else if constexpr (b_2d(SM)) {
       lds_dma16(B.scale, sbuf + C::BM * 16 + s64 * 1024, 0, (int)((s64 >> 1) * (K / 32)) + 16 * blk);
@@ -326,7 +334,7 @@ __device__ __forceinline__ ReadOffsets read_offsets(int wm, int wn, int lane) { 
   o.a_data2 = o.a_data ^ 64;
   o.b_data = LY::kOffBData + wn * LY::WTN * BK + lane_off;
   o.b_data2 = o.b_data ^ 64;
-  if constexpr (LY::SB == 4 && SM != SM_MX) {  // blockwise scales in 4-step blocks: 16 bytes per row
+  if constexpr (LY::SB == 4 && block_scales(SM)) {  // blockwise scales in 4-step blocks: 16 bytes per row
     static_assert(128 % LY::WTN == 0, "a wave's columns stay inside one 128-row block of B");
     o.a_scale = (wm * LY::WTM + r) * 16;
     o.b_scale = LY::BM * 16 + (wn * LY::WTN + ((SM == SM_FS1) ? 4 * g : (SM == SM_BE1) ? r : 0)) * 16;
@@ -493,7 +501,7 @@ __device__ __forceinline__ void mainloop(uint8_t* lds, v4f (&acc)[LY::FRN][LY::F
   constexpr int S = LY::NSTAGE;
   static_assert(S >= 2 && S <= 4, "the waits below cover up to two later stages in flight");
   // copies per copier wave and stage (the same for every copier)
-  constexpr int kPerStage = 2 * (LY::BM / 8 / LY::NCOPY) + (SM == SM_PT || LY::SB == 4 ? 0 : LY::kScaleSlicesPerCopier);
+  constexpr int kPerStage = (LY::BM + LY::BN) / 8 / LY::NCOPY + (SM == SM_PT || LY::SB == 4 ? 0 : LY::kScaleSlicesPerCopier);
   constexpr bool kBlk = LY::SB == 4 && SM != SM_PT;
   if (copier) {
 #pragma unroll
@@ -944,14 +952,24 @@ __device__ __forceinline__ void epilogue(v4f (&acc)[LY::FRN][LY::FRM], void* d, 
 // barrier below); the region is reused by the next block (and with the GELU
 // aux, aux first, then D), since LDS accesses of one wave complete in issue
 // order.  The regions of all waves take staged_bytes<LY>() from lds.
+// A staged row's bytes: 2 WTN, rounded up to a power of two (96-column waves
+// use 12 of 16 chunks), so the chunk swizzle stays an XOR.
+template <class LY>
+constexpr int staged_row_bytes() {
+  int rb = 16;
+  while (rb < 2 * LY::WTN) rb *= 2;
+  return rb;
+}
+
 template <class LY, int ROWS>
 __device__ __forceinline__ void store_region(const uint8_t* region, uint16_t* out, int64_t mb, int64_t m_end,
                                              int64_t nb, int64_t N, int lane) {
-  constexpr int RB = LY::WTN * 2, CH = RB / 16;
+  constexpr int RB = staged_row_bytes<LY>(), CHP = RB / 16, CH = LY::WTN * 2 / 16;
+  static_assert(ROWS * CH % 64 == 0, "whole store instructions");
 #pragma unroll
   for (int t = 0; t < ROWS * CH / 64; ++t) {
     const int q = (64 * t + lane) / CH, c = (64 * t + lane) % CH;
-    const uint4 v = *reinterpret_cast<const uint4*>(region + q * RB + ((c ^ (q & (CH - 1))) << 4));
+    const uint4 v = *reinterpret_cast<const uint4*>(region + q * RB + ((c ^ (q & (CHP - 1))) << 4));
     const int64_t m = mb + q, n = nb + 8 * c;  // N % 16 == 0: a chunk of 8 columns is all in or all out
     if (m < m_end && n < N) *reinterpret_cast<uint4*>(out + m * N + n) = v;
   }
@@ -964,7 +982,11 @@ constexpr bool staged_epilogue(int epi, int out) {
 template <class LY>
 constexpr int staged_row_frags() { return LY::FRM < 4 ? LY::FRM : 4; }  // row fragments per staged block
 template <class LY>
-constexpr int staged_bytes() { return LY::NW * 16 * staged_row_frags<LY>() * LY::WTN * 2; }
+constexpr int staged_bytes() { return LY::NW * 16 * staged_row_frags<LY>() * staged_row_bytes<LY>(); }
+// LDS of a dense 8- or 4-wave kernel: its stages and scale buffers, or the
+// staged epilogue's regions if those are larger (256 x 192: 128 KB against 126)
+template <class LY>
+constexpr int lds_bytes() { return LY::kLds > staged_bytes<LY>() ? LY::kLds : staged_bytes<LY>(); }
 
 template <class LY, int EPI, int OUT, bool SCALE = false>
 __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8_t* lds, void* d,
@@ -972,9 +994,8 @@ __device__ __forceinline__ void epilogue_lds(v4f (&acc)[LY::FRN][LY::FRM], uint8
                                              int64_t n0, int64_t N, int wave, int lane, float alpha = 1.0f) {
   static_assert(OUT == TE_BF16 || OUT == TE_FP16, "2-byte outputs");
   static_assert(EPI == TE_EPI_NONE || EPI == TE_EPI_BIAS || EPI == TE_EPI_BIAS_GELU_AUX, "forward epilogues");
-  constexpr int FRH = staged_row_frags<LY>(), RB = LY::WTN * 2, CH = RB / 16, kRegion = 16 * FRH * RB;
-  static_assert((CH & (CH - 1)) == 0 && CH <= 16 && LY::FRM % FRH == 0 && staged_bytes<LY>() <= LY::kLds,
-                "staging layout");
+  constexpr int FRH = staged_row_frags<LY>(), RB = staged_row_bytes<LY>(), CH = RB / 16, kRegion = 16 * FRH * RB;
+  static_assert(CH <= 16 && LY::FRM % FRH == 0 && staged_bytes<LY>() <= lds_bytes<LY>(), "staging layout");
   const int wm = wave / LY::NWN, wn = wave % LY::NWN;
   const int g = lane >> 4, r = lane & 15;
   uint8_t* region = lds + wave * kRegion;
@@ -1240,7 +1261,7 @@ __device__ __forceinline__ void finish_tile(v4f (&acc)[LY::FRN][LY::FRM], uint8_
 template <class LY, int FA, int FB, int EPI, int OUT, int SM = SM_MX>
 __global__ __launch_bounds__(LY::kThreads) void mx_gemm_kernel(GemmParams p) {
   constexpr int BM = LY::BM, BN = LY::BN;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LY::kLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[lds_bytes<LY>()];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int tm, tn;
@@ -1429,7 +1450,7 @@ inline bool use_small_tile(int64_t big_tiles) {
 // Tile configuration of a dense GEMM: SmallDeep for grids of at most one
 // small tile per CU with K >= 2048 (16 or more K steps; 4096 x 1024 x 4096:
 // 26.7 us against 31.5 for Small), else as above.
-enum class Tile { Big, Small, SmallDeep };
+enum class Tile { Big, Small, SmallDeep, Big192 };
 
 inline Tile pick_tile(int64_t M, int64_t N, int64_t K) {
   const int64_t small_tiles = ((M + 127) / 128) * ((N + 127) / 128);
@@ -1438,8 +1459,9 @@ inline Tile pick_tile(int64_t M, int64_t N, int64_t K) {
 }
 
 inline dim3 tile_grid(Tile t, int64_t M, int64_t N) {
-  return t == Tile::Big ? dim3((unsigned)(((M + 255) / 256) * ((N + 255) / 256)))
-                        : dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128)));
+  if (t == Tile::Big) return dim3((unsigned)(((M + 255) / 256) * ((N + 255) / 256)));
+  if (t == Tile::Big192) return dim3((unsigned)(((M + 255) / 256) * ((N + 191) / 192)));
+  return dim3((unsigned)(((M + 127) / 128) * ((N + 127) / 128)));
 }
 
 // The 4-wave tile instead of the 8-wave big tile: K % 1024 == 0 (the loop's
@@ -1462,6 +1484,16 @@ inline bool four_wave(int64_t M, int64_t N, int64_t K) {
 inline bool four_wave_mx(int64_t M, int64_t N, int64_t K) {
   const int64_t lim = ((int64_t)1 << 31) - 4096;
   return four_wave(M, N, K) && M * (K / 32) < lim && N * (K / 32) < lim;
+}
+// Tile of a dense MXFP8 or per-tensor GEMM (the blockwise GEMMs keep
+// pick_tile: their FP32-scale modes take 128-column wave tiles): the
+// 256 x 192 tile where the big-tile grid is one partial round, the 256 x 192
+// grid fits in one and the 4-wave tile does not apply.
+inline Tile pick_tile_dense(int64_t M, int64_t N, int64_t K) {
+  const Tile t = pick_tile(M, N, K);
+  if (t != Tile::Big || four_wave(M, N, K)) return t;
+  const int64_t cus = device_cu_count(), rows = (M + 255) / 256;
+  return rows * ((N + 255) / 256) < cus && rows * ((N + 191) / 192) <= cus ? Tile::Big192 : Tile::Big;
 }
 inline size_t scale_blocks_b_offset(int64_t M, int64_t K) { return (size_t)((M * (K / 32) + 255) / 256 * 256); }
 inline size_t scale_blocks_bytes(int64_t M, int64_t N, int64_t K) {

@@ -55,6 +55,7 @@ STATED_MISS_CEILING: dict = {
     "big_ragged:4144x4176x256:bias_gelu_aux:D": 5,  # 2 of 5550
     "big_ragged:4144x4176x256:bias_gelu_aux:aux": 10,  # 7 of 5550
     "big_ragged:4144x4176x256:none:D": 5,  # 2 of 5550
+    "big192:4048x2992x1024:none:D": 4,  # 1 of 4745
     "block_beta:e8m0": 8,  # 5 of 335872
     "block_beta:fp32": 8,  # 5 of 335872
     "block_epilogue:e8m0:bias": 10,  # 7 of 211200
@@ -80,6 +81,7 @@ STATED_MISS_CEILING: dict = {
     "per_tensor:272x400x256:bias": 115,  # 102 of 108800
     "per_tensor:272x400x256:bias_gelu_aux": 28,  # 23 of 108800
     "per_tensor:272x400x256:none": 125,  # 111 of 108800
+    "per_tensor:4048x2992x1024:bias": 5,  # 2 of 2304
     "per_tensor:4144x4176x256:bias": 5,  # 2 of 2304
     "per_tensor:4144x4176x256:bias_gelu_aux": 4,  # 1 of 2304
     "per_tensor:4144x4176x256:none": 5,  # 2 of 2304

@@ -64,7 +64,7 @@ def per_tensor_operands(M, N, K, seed, fa="e4m3", fb="e4m3"):
 
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
-                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 2048)])
+                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 2048), (4096 - 48, 3072 - 80, 1024)])
 def test_per_tensor_gemm(epi, M, N, K):
     qa, ia, qb, ib = per_tensor_operands(M, N, K, 96 + K)
     bias_bits = None if epi == "none" else workloads.normal_bf16(97, N, (N,), 0.5)

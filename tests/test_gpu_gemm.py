@@ -57,6 +57,25 @@ def test_gemm_exact_integer_bitexact(fa, fb, M, N, K):
 
 
 @pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
+def test_big192_tile_exact_integer(fa, fb):
+    # the 256 x 192 tile (16 x 12 tiles of 256 x 256 leave 64 CUs idle, 16 x 16 of 256 x 192 fill
+    # them), with a 48-row and an 80-column tail; exact-integer operands, so sampled rows (every
+    # tile boundary, every wave-row boundary, the last row) match the oracle bit for bit
+    M, N, K = 4096 - 48, 3072 - 80, 1024
+    rng = np.random.default_rng(19201)
+    qa, qb = exact_codes(rng, (M, K), fa), exact_codes(rng, (N, K), fb)
+    sa = rng.integers(124, 131, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(124, 131, size=(N, K // 32)).astype(np.uint8)
+    d, _ = te().mxfp8_gemm(dev(qa), dev(sa), fa, dev(qb), dev(sb), fb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, M - 1} | {64 * t + o for t in range(M // 64) for o in (0, 15, 63)}
+                           | set(rng.choice(M, 16, replace=False).tolist())))
+    rows = rows[rows < M]
+    ref, _, _ = oracle.mx_gemm(qa[rows], sa[rows], oracle.format_by_name(fa), qb, sb, oracle.format_by_name(fb))
+    assert np.array_equal(host(d[rows]).astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
 def test_big_tile_exact_integer_partial_scale_block(fa, fb):
     # enough 256 x 256 tiles (24 x 25) for the big tile, whose scales travel in
     # blocks of 4 K steps: K = 1152 is 9 steps, so the last block holds one
@@ -278,6 +297,18 @@ def test_big_tile_ragged_edges(epi, K):
     check_gemm_spec(spec, full=False)
 
 
+@pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
+def test_big192_tile_epilogues(epi):
+    # the 256 x 192 tile with a 48-row and an 80-column tail (16 x 16 tiles): D and aux against the
+    # oracle and the MFMA model on sampled rows and columns
+    M, N, K = 4096 - 48, 3072 - 80, 1024
+    spec = workloads.GemmSpec("big192", M, N, K, "e4m3", "e4m3", epi,
+                              workloads.TensorSpec(56, M, (M, K), 1.0, 0.01),
+                              workloads.TensorSpec(57, N, (N, K), 0.05),
+                              bias=None if epi == "none" else workloads.TensorSpec(58, N, (N,), 0.5))
+    check_gemm_spec(spec, full=False)
+
+
 def test_fp32_output_and_canaries():
     M, N, K = 272, 304, 512
     a = workloads.normal_bf16(60, 0, (M, K), 1.0)
@@ -411,7 +442,8 @@ def backward_operands(M, N, K, seed):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
-                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 2048)])
+                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 2048),
+                                   (4096 - 48, 3072 - 80, 1024)])
 def test_dgelu_epilogue(M, N, K):
     qa, sa, qb, sb, oqa, osa, oqb, osb = backward_operands(M, N, K, 70 + K)
     pre = workloads.normal_bf16(72, M + N, (M, N), 2.0, 0.0)   # the forward's saved pre-activation
@@ -452,7 +484,8 @@ def test_dgelu_epilogue(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 16, 128), (272, 400, 256), (1040, 784, 640), (4096 + 48, 4096 + 80, 256),
-                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 2048)])
+                                   (272, 400, 2176), (4096 + 48, 4096 + 80, 2048),
+                                   (4096 - 48, 3072 - 80, 1024)])
 def test_accumulate_epilogue(M, N, K):
     qa, sa, qb, sb, oqa, osa, oqb, osb = backward_operands(M, N, K, 80 + K)
     rng = np.random.default_rng(M + N + K)
@@ -523,7 +556,8 @@ def test_grouped_backward_epilogues_match_dense(epi):
 @pytest.mark.parametrize("epi", ["none", "bias", "bias_gelu_aux"])
 @pytest.mark.parametrize("M,N,K,out_fmt", [(16, 32, 128, "e4m3"), (272, 416, 256, "e4m3"), (1040, 800, 640, "e4m3"),
                                            (4096 + 48, 4096 + 32, 256, "e4m3"), (272, 416, 256, "e5m2"),
-                                           (272, 416, 2176, "e4m3"), (4096 + 48, 4096 + 32, 2048, "e4m3")])
+                                           (272, 416, 2176, "e4m3"), (4096 + 48, 4096 + 32, 2048, "e4m3"),
+                                           (4096 - 48, 3072 - 64, 1024, "e4m3")])
 def test_mxfp8_output_equals_quantized_bf16_output(epi, M, N, K, out_fmt):
     # the codes must be exactly the rowwise quantization of the bf16 D that
     # te_mxfp8_gemm writes for the same inputs (itself checked against the
