@@ -23,10 +23,12 @@
 //   epilogue stores 8 bytes (bf16) per lane straight from registers.
 // * 256 x 256 workgroup tile, 8 waves in 4 x 2 (two per SIMD), 64 x 128 per
 //   wave (4 x 8 MFMA tiles = 128 fp32 accumulators per lane), K step 128;
-//   a 128 x 128 tile (4 waves of 64 x 64) for grids the big tile cannot fill,
-//   with 2 or 4 LDS stages (see Cfg); and for long-K grids the 4-wave
-//   256 x 256 tile (Big4, mainloop4: one wave per SIMD, 128 x 128 per wave,
-//   256 accumulators in AGPRs), persistent over its tiles.
+//   a 256 x 192 tile (8 waves of 64 x 96) where that fills the CUs the
+//   256 x 256 grid leaves idle; a 128 x 128 tile (4 waves of 64 x 64) for
+//   grids the big tile cannot fill, with 2 or 4 LDS stages (see Cfg); and for
+//   long-K grids the 4-wave 256 x 256 tile (Big4, mainloop4: one wave per
+//   SIMD, 128 x 128 per wave, 256 accumulators in AGPRs), persistent over its
+//   tiles.
 // * A, B and their scale tiles are copied global -> LDS with direct-to-LDS
 //   buffer loads (buffer_load_dwordx4 / _dword ... lds) into a ring of
 //   stages, issued by one wave per SIMD.
