@@ -56,13 +56,15 @@ def test_gemm_exact_integer_bitexact(fa, fb, M, N, K):
     assert np.array_equal(host(d).astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("fa,fb", [("e4m3", "e4m3"), ("e5m2", "e4m3"), ("e4m3", "e5m2")])
-def test_big192_tile_exact_integer(fa, fb):
+@pytest.mark.parametrize("fa,fb,K", [("e4m3", "e4m3", 1024), ("e5m2", "e4m3", 1024), ("e4m3", "e5m2", 1024),
+                                     ("e4m3", "e4m3", 128), ("e4m3", "e4m3", 384)])
+def test_big192_tile_exact_integer(fa, fb, K):
     # the 256 x 192 tile (16 x 12 tiles of 256 x 256 leave 64 CUs idle, 16 x 16 of 256 x 192 fill
     # them), with a 48-row and an 80-column tail; exact-integer operands, so sampled rows (every
-    # tile boundary, every wave-row boundary, the last row) match the oracle bit for bit
-    M, N, K = 4096 - 48, 3072 - 80, 1024
-    rng = np.random.default_rng(19201)
+    # tile boundary, every wave-row boundary, the last row) match the oracle bit for bit.  K = 128
+    # and 384: one and three K steps, a partial 4-step scale block
+    M, N = 4096 - 48, 3072 - 80
+    rng = np.random.default_rng(19201 + K)
     qa, qb = exact_codes(rng, (M, K), fa), exact_codes(rng, (N, K), fb)
     sa = rng.integers(124, 131, size=(M, K // 32)).astype(np.uint8)
     sb = rng.integers(124, 131, size=(N, K // 32)).astype(np.uint8)
